@@ -1,0 +1,457 @@
+// C ABI of the MoE library: validation, workspace layout, kernel sequencing.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "moe.h"
+#include "moe_kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+moe_status fail(moe_status code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+moe_status ok() {
+  g_err[0] = '\0';
+  return MOE_OK;
+}
+moe_status hip_fail(hipError_t e, const char* what) {
+  return fail(MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+uint64_t blob_size(int H, int I, int G) { return 3ull * I * H / 2 + 12ull * I * H / G; }
+
+moe_status check_desc(const moe_layer_desc* d) {
+  if (!d) return fail(MOE_EINVAL, "desc is NULL");
+  const int H = d->hidden, E = d->n_experts, K = d->top_k, I = d->inter, Is = d->shared_inter, G = d->group_size;
+  if (H < 64 || H > moe::kMaxH || H % 64) return fail(MOE_ESHAPE, "hidden=%d must be a multiple of 64 in [64, %d]", H, moe::kMaxH);
+  if (E < 1 || E > moe::kMaxExperts) return fail(MOE_ESHAPE, "n_experts=%d must be in [1, %d]", E, moe::kMaxExperts);
+  if (K < 1 || K > E || K > moe::kMaxTopK) return fail(MOE_ESHAPE, "top_k=%d must be in [1, min(E, %d)]", K, moe::kMaxTopK);
+  if (I < 64 || I > moe::kMaxInter || I % 64) return fail(MOE_ESHAPE, "inter=%d must be a multiple of 64 in [64, %d]", I, moe::kMaxInter);
+  if (Is != 0 && (Is < 64 || Is > moe::kMaxInter || Is % 64))
+    return fail(MOE_ESHAPE, "shared_inter=%d must be 0 or a multiple of 64 in [64, %d]", Is, moe::kMaxInter);
+  if (G != 32 && G != 64 && G != 128) return fail(MOE_ESHAPE, "group_size=%d must be 32, 64 or 128", G);
+  if (H % G || I % G || (Is && Is % G)) return fail(MOE_ESHAPE, "group_size=%d must divide hidden, inter and shared_inter", G);
+  if (d->act_dtype != MOE_F16 && d->act_dtype != MOE_BF16) return fail(MOE_EINVAL, "act_dtype=%d is not MOE_F16/MOE_BF16", d->act_dtype);
+  if (d->path < MOE_PATH_AUTO || d->path > MOE_PATH_GROUPED) return fail(MOE_EINVAL, "path=%d is not a MOE_PATH_*", d->path);
+  return MOE_OK;
+}
+
+moe_status check_weights(const moe_layer_desc* d, const moe_layer_weights* w) {
+  if (!w) return fail(MOE_EINVAL, "weights is NULL");
+  if (!w->router_w || !aligned(w->router_w, 16)) return fail(MOE_EINVAL, "router_w must be a 16-byte aligned device pointer");
+  if (!w->experts || !aligned(w->experts, 256)) return fail(MOE_EINVAL, "experts must be a 256-byte aligned device pointer");
+  if (!w->expert_offset) {
+    if (w->expert_stride % 256 || w->expert_stride < blob_size(d->hidden, d->inter, d->group_size))
+      return fail(MOE_EINVAL, "expert_stride=%llu must be a multiple of 256 and >= %llu",
+                  (unsigned long long)w->expert_stride,
+                  (unsigned long long)blob_size(d->hidden, d->inter, d->group_size));
+  }
+  if (d->shared_inter > 0 && (!w->shared || !aligned(w->shared, 256)))
+    return fail(MOE_EINVAL, "shared blob must be a 256-byte aligned device pointer when shared_inter > 0");
+  return MOE_OK;
+}
+
+size_t al(size_t v) { return (v + 255) & ~size_t(255); }
+
+struct Ws {
+  size_t logits, idx, w, gamma, off, perm, inv, active, nact, h, yrow, total;
+};
+
+Ws layout(const moe_layer_desc* d, int T) {
+  const size_t E = d->n_experts, K = d->top_k, H = d->hidden;
+  const size_t hstride = d->inter > d->shared_inter ? d->inter : d->shared_inter;
+  const size_t rows = T * K + (d->shared_inter ? T : 0);
+  Ws s{};
+  size_t o = 0;
+  s.logits = o; o += al(T * (E + 1) * 4);
+  s.idx = o; o += al(T * K * 4);
+  s.w = o; o += al(T * K * 4);
+  s.gamma = o; o += al(T * 4);
+  s.off = o; o += al((E + 1) * 4);
+  s.perm = o; o += al(T * K * 4);
+  s.inv = o; o += al(T * K * 4);
+  s.active = o; o += al((E + 1) * 4);
+  s.nact = o; o += al(16);
+  s.h = o; o += al(rows * hstride * 4);
+  s.yrow = o; o += al(rows * H * 4);
+  s.total = o;
+  return s;
+}
+
+template <class T>
+T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
+
+moe_status check_ws(const moe_layer_desc* d, int T, void* ws, size_t ws_bytes, Ws& L) {
+  L = layout(d, T);
+  if (!ws || !aligned(ws, 256)) return fail(MOE_EINVAL, "workspace must be a 256-byte aligned device pointer");
+  if (ws_bytes < L.total) return fail(MOE_EWORKSPACE, "workspace of %zu bytes < required %zu", ws_bytes, L.total);
+  return MOE_OK;
+}
+
+bool use_grouped(const moe_layer_desc* d, int T) {
+  if (d->path == MOE_PATH_GEMV) return false;
+  if (d->path == MOE_PATH_GROUPED) return true;
+  return static_cast<long long>(T) * d->top_k > MOE_GEMV_MAX_ROWS;
+}
+
+moe_status do_route(const moe_layer_desc* d, const moe_layer_weights* w, const void* x, int T, int32_t* idx,
+                    float* tw, float* gamma, float* logits, hipStream_t s) {
+  hipError_t e = moe::launch_router_logits(d->act_dtype, static_cast<const uint16_t*>(x), w->router_w,
+                                           w->router_bias, logits, T, d->hidden, d->n_experts, s);
+  if (e != hipSuccess) return hip_fail(e, "router kernel launch");
+  e = moe::launch_topk(logits, T, d->n_experts, d->top_k, idx, tw, gamma, s);
+  if (e != hipSuccess) return hip_fail(e, "top-k kernel launch");
+  return MOE_OK;
+}
+
+moe_status do_ffn(const moe_layer_desc* d, const moe_layer_weights* w, const void* x, int T, const int32_t* idx,
+                  const float* tw, const float* gamma, float* y, float* r, void* x_next, void* ws, const Ws& L,
+                  hipStream_t s) {
+  moe::FfnArgs a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.topk_idx = idx;
+  a.experts = w->experts;
+  a.stride = w->expert_stride;
+  a.offsets = w->expert_offset;
+  a.shared = w->shared;
+  a.h = at<float>(ws, L.h);
+  a.yrow = at<float>(ws, L.yrow);
+  a.T = T;
+  a.H = d->hidden;
+  a.K = d->top_k;
+  a.I = d->inter;
+  a.Is = d->shared_inter;
+  a.G = d->group_size;
+  a.E = d->n_experts;
+  a.hstride = d->inter > d->shared_inter ? d->inter : d->shared_inter;
+  const int32_t* inv = nullptr;
+  hipError_t e;
+  if (use_grouped(d, T)) {
+    a.perm = at<int32_t>(ws, L.perm);
+    a.expert_off = at<int32_t>(ws, L.off);
+    a.active = at<int32_t>(ws, L.active);
+    a.n_active = at<int32_t>(ws, L.nact);
+    e = moe::launch_permute(idx, T * d->top_k, d->n_experts, at<int32_t>(ws, L.off), at<int32_t>(ws, L.perm),
+                            at<int32_t>(ws, L.inv), at<int32_t>(ws, L.active), at<int32_t>(ws, L.nact), s);
+    if (e != hipSuccess) return hip_fail(e, "permute kernel launch");
+    e = moe::launch_gateup_grouped(d->act_dtype, a, s);
+    if (e != hipSuccess) return hip_fail(e, "grouped gate/up kernel launch");
+    e = moe::launch_down_grouped(a, s);
+    if (e != hipSuccess) return hip_fail(e, "grouped down kernel launch");
+    inv = at<int32_t>(ws, L.inv);
+  } else {
+    e = moe::launch_gateup_gemv(d->act_dtype, a, s);
+    if (e != hipSuccess) return hip_fail(e, "gate/up GEMV kernel launch");
+    e = moe::launch_down_gemv(a, s);
+    if (e != hipSuccess) return hip_fail(e, "down GEMV kernel launch");
+  }
+  e = moe::launch_combine(d->act_dtype, a.yrow, inv, tw, gamma, T, d->top_k, d->hidden, d->shared_inter > 0, y, r,
+                          static_cast<uint16_t*>(x_next), s);
+  if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
+  return MOE_OK;
+}
+
+}  // namespace
+
+namespace moe {
+moe_status set_error(moe_status code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+}  // namespace moe
+
+struct moe_graph {
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+};
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_err; }
+
+const char* moe_version(void) { return "int4_routed_expert_router_amd 0.1 (gfx950)"; }
+
+uint64_t moe_blob_bytes(int32_t hidden, int32_t inter, int32_t group_size) {
+  if (hidden <= 0 || inter <= 0 || hidden % 64 || inter % 64) return 0;
+  if ((group_size != 32 && group_size != 64 && group_size != 128) || hidden % group_size || inter % group_size)
+    return 0;
+  return blob_size(hidden, inter, group_size);
+}
+
+moe_status moe_pack_expert(int32_t H, int32_t I, int32_t G, const uint8_t* gate_q, const uint16_t* gate_s,
+                           const uint16_t* gate_b, const uint8_t* up_q, const uint16_t* up_s, const uint16_t* up_b,
+                           const uint8_t* down_q, const uint16_t* down_s, const uint16_t* down_b,
+                           uint8_t* blob_out) {
+  if (moe_blob_bytes(H, I, G) == 0) return fail(MOE_ESHAPE, "bad blob shape H=%d I=%d G=%d", H, I, G);
+  if (!gate_q || !gate_s || !gate_b || !up_q || !up_s || !up_b || !down_q || !down_s || !down_b || !blob_out)
+    return fail(MOE_EINVAL, "NULL pointer");
+  const size_t nq = static_cast<size_t>(I) * H;
+  for (size_t i = 0; i < nq; ++i)
+    if ((gate_q[i] | up_q[i] | down_q[i]) > 15) return fail(MOE_EINVAL, "q value above 15 at element %zu", i);
+  memset(blob_out, 0, blob_size(H, I, G));
+  // nibble sections: for pair-tile p, chunk c, lane l = 16 kb + n, word wd:
+  // tile (wd >> 1), half ks = (wd & 1), value j -> column 64c + 32ks + 8kb + j
+  auto pack_section = [&](uint8_t* sec, int n_pairs, int in_dim, const uint8_t* qa, int row_a0_stride,
+                          const uint8_t* qb, bool gu) {
+    const int nc = in_dim / 64;
+    for (int p = 0; p < n_pairs; ++p)
+      for (int c = 0; c < nc; ++c)
+        for (int l = 0; l < 64; ++l) {
+          const int n = l % 16, kb = l / 16;
+          for (int wd = 0; wd < 4; ++wd) {
+            const int tile = wd >> 1, ks = wd & 1;
+            int row;
+            const uint8_t* q;
+            if (gu) {
+              row = 16 * p + n;
+              q = tile ? qb : qa;
+            } else {
+              row = 32 * p + 16 * tile + n;
+              q = qa;
+            }
+            uint32_t word = 0;
+            for (int j = 0; j < 8; ++j) {
+              const int col = 64 * c + 32 * ks + 8 * kb + j;
+              const uint32_t v = q[static_cast<size_t>(row) * in_dim + col];
+              word |= v << (4 * ((j >> 1) + 4 * (j & 1)));
+            }
+            uint8_t* dst = sec + (static_cast<size_t>(p) * nc + c) * 1024 + 16 * l + 4 * wd;
+            memcpy(dst, &word, 4);
+          }
+        }
+    (void)row_a0_stride;
+  };
+  pack_section(blob_out, I / 16, H, gate_q, 0, up_q, true);
+  pack_section(blob_out + static_cast<size_t>(I) * H, H / 32, I, down_q, 0, nullptr, false);
+  auto pack_scales = [&](uint8_t* sec, int n_pairs, int in_dim, const uint16_t* sa, const uint16_t* ba,
+                         const uint16_t* sb_, const uint16_t* bb, bool gu) {
+    const int ng = in_dim / G;
+    for (int p = 0; p < n_pairs; ++p)
+      for (int g = 0; g < ng; ++g)
+        for (int n = 0; n < 16; ++n) {
+          uint16_t v[4];
+          if (gu) {
+            const size_t r = static_cast<size_t>(16 * p + n) * ng + g;
+            v[0] = sa[r];
+            v[1] = ba[r];
+            v[2] = sb_[r];
+            v[3] = bb[r];
+          } else {
+            const size_t ra = static_cast<size_t>(32 * p + n) * ng + g;
+            const size_t rb = static_cast<size_t>(32 * p + 16 + n) * ng + g;
+            v[0] = sa[ra];
+            v[1] = ba[ra];
+            v[2] = sa[rb];
+            v[3] = ba[rb];
+          }
+          memcpy(sec + ((static_cast<size_t>(p) * ng + g) * 16 + n) * 8, v, 8);
+        }
+  };
+  const size_t gu_s = 3ull * I * H / 2, d_s = gu_s + 8ull * I * H / G;
+  pack_scales(blob_out + gu_s, I / 16, H, gate_s, gate_b, up_s, up_b, true);
+  pack_scales(blob_out + d_s, H / 32, I, down_s, down_b, nullptr, nullptr, false);
+  return ok();
+}
+
+moe_status moe_workspace_bytes(const moe_layer_desc* d, int32_t n_tokens, size_t* bytes) {
+  moe_status st = check_desc(d);
+  if (st) return st;
+  if (n_tokens < 0) return fail(MOE_ESHAPE, "n_tokens=%d < 0", n_tokens);
+  if (!bytes) return fail(MOE_EINVAL, "bytes is NULL");
+  *bytes = layout(d, n_tokens).total;
+  return ok();
+}
+
+moe_status moe_route(const moe_layer_desc* d, const moe_layer_weights* w, const void* x, int32_t T,
+                     int32_t* topk_idx, float* topk_w, float* shared_gate, float* logits_or_null, void* ws,
+                     size_t ws_bytes, moe_stream stream) {
+  moe_status st = check_desc(d);
+  if (st) return st;
+  if ((st = check_weights(d, w))) return st;
+  if (T < 0) return fail(MOE_ESHAPE, "n_tokens=%d < 0", T);
+  if (T == 0) return ok();
+  if (!x || !aligned(x, 16)) return fail(MOE_EINVAL, "x must be a 16-byte aligned device pointer");
+  if (!topk_idx || !topk_w) return fail(MOE_EINVAL, "topk_idx and topk_w are required");
+  Ws L;
+  if ((st = check_ws(d, T, ws, ws_bytes, L))) return st;
+  float* logits = logits_or_null ? logits_or_null : at<float>(ws, L.logits);
+  float* gamma = shared_gate ? shared_gate : at<float>(ws, L.gamma);
+  st = do_route(d, w, x, T, topk_idx, topk_w, gamma, logits, reinterpret_cast<hipStream_t>(stream));
+  return st ? st : ok();
+}
+
+moe_status moe_permute(const moe_layer_desc* d, const int32_t* topk_idx, int32_t T, int32_t* expert_off,
+                       int32_t* perm, int32_t* inv_or_null, void* ws, size_t ws_bytes, moe_stream stream) {
+  moe_status st = check_desc(d);
+  if (st) return st;
+  if (T < 0) return fail(MOE_ESHAPE, "n_tokens=%d < 0", T);
+  if (T == 0) return ok();
+  if (!topk_idx || !expert_off || !perm) return fail(MOE_EINVAL, "topk_idx, expert_off and perm are required");
+  Ws L;
+  if ((st = check_ws(d, T, ws, ws_bytes, L))) return st;
+  hipError_t e = moe::launch_permute(topk_idx, T * d->top_k, d->n_experts, expert_off, perm, inv_or_null,
+                                     at<int32_t>(ws, L.active), at<int32_t>(ws, L.nact),
+                                     reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "permute kernel launch");
+  return ok();
+}
+
+moe_status moe_expert_ffn(const moe_layer_desc* d, const moe_layer_weights* w, const void* x, int32_t T,
+                          const int32_t* topk_idx, const float* topk_w, const float* shared_gate, float* y,
+                          void* ws, size_t ws_bytes, moe_stream stream) {
+  moe_status st = check_desc(d);
+  if (st) return st;
+  if ((st = check_weights(d, w))) return st;
+  if (T < 0) return fail(MOE_ESHAPE, "n_tokens=%d < 0", T);
+  if (T == 0) return ok();
+  if (!x || !aligned(x, 16)) return fail(MOE_EINVAL, "x must be a 16-byte aligned device pointer");
+  if (!topk_idx || !topk_w || !y) return fail(MOE_EINVAL, "topk_idx, topk_w and y are required");
+  if (d->shared_inter > 0 && !shared_gate) return fail(MOE_EINVAL, "shared_gate is required when shared_inter > 0");
+  Ws L;
+  if ((st = check_ws(d, T, ws, ws_bytes, L))) return st;
+  st = do_ffn(d, w, x, T, topk_idx, topk_w, shared_gate, y, nullptr, nullptr, ws, L,
+              reinterpret_cast<hipStream_t>(stream));
+  return st ? st : ok();
+}
+
+moe_status moe_layer_forward(const moe_layer_desc* d, const moe_layer_weights* w, const void* x, int32_t T,
+                             float* y, int32_t* idx_out, float* w_out, float* gamma_out, void* ws,
+                             size_t ws_bytes, moe_stream stream) {
+  moe_status st = check_desc(d);
+  if (st) return st;
+  if ((st = check_weights(d, w))) return st;
+  if (T < 0) return fail(MOE_ESHAPE, "n_tokens=%d < 0", T);
+  if (T == 0) return ok();
+  if (!x || !aligned(x, 16)) return fail(MOE_EINVAL, "x must be a 16-byte aligned device pointer");
+  if (!y) return fail(MOE_EINVAL, "y is required");
+  Ws L;
+  if ((st = check_ws(d, T, ws, ws_bytes, L))) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int32_t* idx = idx_out ? idx_out : at<int32_t>(ws, L.idx);
+  float* tw = w_out ? w_out : at<float>(ws, L.w);
+  float* gamma = gamma_out ? gamma_out : at<float>(ws, L.gamma);
+  if ((st = do_route(d, w, x, T, idx, tw, gamma, at<float>(ws, L.logits), s))) return st;
+  if ((st = do_ffn(d, w, x, T, idx, tw, gamma, y, nullptr, nullptr, ws, L, s))) return st;
+  return ok();
+}
+
+moe_status moe_stack_epilogue(const moe_layer_desc* d, int32_t T, const float* y, float* r, void* x_next,
+                              moe_stream stream) {
+  moe_status st = check_desc(d);
+  if (st) return st;
+  if (T < 0) return fail(MOE_ESHAPE, "n_tokens=%d < 0", T);
+  if (T == 0) return ok();
+  if (!y || !r || !x_next) return fail(MOE_EINVAL, "y, r and x_next are required");
+  hipError_t e = moe::launch_epilogue(d->act_dtype, y, r, static_cast<uint16_t*>(x_next), T, d->hidden,
+                                      reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "epilogue kernel launch");
+  return ok();
+}
+
+static moe_status stack_enqueue(const moe_layer_desc* d, const moe_layer_weights* layers, int32_t L_, const void* x0,
+                                int32_t T, float* r, void* x_buf, void* x_all, float* y_all, int32_t* idx_all,
+                                float* w_all, float* gamma_all, void* ws, size_t ws_bytes, hipStream_t s) {
+  moe_status st = check_desc(d);
+  if (st) return st;
+  if (L_ < 0 || (L_ > 0 && !layers)) return fail(MOE_EINVAL, "bad layer array");
+  if (T < 0) return fail(MOE_ESHAPE, "n_tokens=%d < 0", T);
+  if (T == 0 || L_ == 0) return ok();
+  if (!x0 || !aligned(x0, 16) || !r || !x_buf || !aligned(x_buf, 16))
+    return fail(MOE_EINVAL, "x0, r and x_buf are required (16-byte aligned)");
+  for (int l = 0; l < L_; ++l)
+    if ((st = check_weights(d, &layers[l]))) return fail(st, "layer %d: %s", l, moe_last_error());
+  Ws L;
+  if ((st = check_ws(d, T, ws, ws_bytes, L))) return st;
+  const size_t TH = static_cast<size_t>(T) * d->hidden, TK = static_cast<size_t>(T) * d->top_k;
+  for (int l = 0; l < L_; ++l) {
+    const void* xl = (l == 0) ? x0 : x_buf;
+    if (x_all) {
+      hipError_t e = hipMemcpyAsync(static_cast<uint16_t*>(x_all) + l * TH, xl, TH * 2, hipMemcpyDeviceToDevice, s);
+      if (e != hipSuccess) return hip_fail(e, "x capture copy");
+    }
+    int32_t* idx = idx_all ? idx_all + l * TK : at<int32_t>(ws, L.idx);
+    float* tw = w_all ? w_all + l * TK : at<float>(ws, L.w);
+    float* gamma = gamma_all ? gamma_all + static_cast<size_t>(l) * T : at<float>(ws, L.gamma);
+    float* y = y_all ? y_all + l * TH : nullptr;
+    if ((st = do_route(d, &layers[l], xl, T, idx, tw, gamma, at<float>(ws, L.logits), s))) return st;
+    if ((st = do_ffn(d, &layers[l], xl, T, idx, tw, gamma, y, r, x_buf, ws, L, s))) return st;
+  }
+  return MOE_OK;
+}
+
+moe_status moe_stack_forward(const moe_layer_desc* d, const moe_layer_weights* layers, int32_t n_layers,
+                             const void* x0, int32_t T, float* r, void* x_buf, void* x_all, float* y_all,
+                             int32_t* idx_all, float* w_all, float* gamma_all, void* ws, size_t ws_bytes,
+                             moe_stream stream) {
+  moe_status st = stack_enqueue(d, layers, n_layers, x0, T, r, x_buf, x_all, y_all, idx_all, w_all, gamma_all, ws,
+                                ws_bytes, reinterpret_cast<hipStream_t>(stream));
+  return st ? st : ok();
+}
+
+moe_status moe_stack_graph_create(const moe_layer_desc* d, const moe_layer_weights* layers, int32_t n_layers,
+                                  const void* x0, int32_t T, float* r, void* x_buf, void* x_all, float* y_all,
+                                  int32_t* idx_all, float* w_all, float* gamma_all, void* ws, size_t ws_bytes,
+                                  moe_stream capture_stream, moe_graph** out) {
+  if (!out) return fail(MOE_EINVAL, "out is NULL");
+  if (!capture_stream) return fail(MOE_EINVAL, "graph capture needs a non-NULL stream");
+  *out = nullptr;
+  hipStream_t s = reinterpret_cast<hipStream_t>(capture_stream);
+  hipError_t e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamBeginCapture");
+  moe_status st = stack_enqueue(d, layers, n_layers, x0, T, r, x_buf, x_all, y_all, idx_all, w_all, gamma_all, ws,
+                                ws_bytes, s);
+  hipGraph_t g = nullptr;
+  e = hipStreamEndCapture(s, &g);
+  if (st) {
+    if (g) hipGraphDestroy(g);
+    return st;
+  }
+  if (e != hipSuccess) return hip_fail(e, "hipStreamEndCapture");
+  hipGraphExec_t ex = nullptr;
+  e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    hipGraphDestroy(g);
+    return hip_fail(e, "hipGraphInstantiate");
+  }
+  moe_graph* mg = new (std::nothrow) moe_graph;
+  if (!mg) {
+    hipGraphExecDestroy(ex);
+    hipGraphDestroy(g);
+    return fail(MOE_ENOMEM, "graph handle allocation");
+  }
+  mg->graph = g;
+  mg->exec = ex;
+  *out = mg;
+  return ok();
+}
+
+moe_status moe_graph_launch(moe_graph* g, moe_stream stream) {
+  if (!g) return fail(MOE_EINVAL, "graph is NULL");
+  hipError_t e = hipGraphLaunch(g->exec, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "hipGraphLaunch");
+  return ok();
+}
+
+void moe_graph_destroy(moe_graph* g) {
+  if (!g) return;
+  if (g->exec) hipGraphExecDestroy(g->exec);
+  if (g->graph) hipGraphDestroy(g->graph);
+  delete g;
+}
+
+}  // extern "C"

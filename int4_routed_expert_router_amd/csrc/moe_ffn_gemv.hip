@@ -1,0 +1,311 @@
+// Per-row int4 expert GEMVs (decode-sized batches) and the combine.
+//
+// The pages run a cooperative GEMV fast path over MLX-style affine int4/int8
+// group-quantised weights (what-was-built list of the page "Show HN: Run an
+// 80B Qwen in 4.3 GB of RAM on a Mac and a 35B on an iPhone").  Here a
+// 64-lane wavefront reads one 1 KiB block of packed nibbles per 16-byte load,
+// so every weight byte moves in fully coalesced 128-bit loads, and the
+// activations are staged once per workgroup in LDS.
+//
+// Affine group identity used by every kernel: for a group of G input columns
+// with scale s and bias b,  sum_c (s q_c + b) x_c = s sum_c q_c x_c + b sum_c x_c,
+// so the per-column work is an integer-weight dot product and the bias costs
+// one FMA per (row, group) with the group sum of x computed once per row.
+#include "moe_common.h"
+#include "moe_kernels.h"
+
+namespace moe {
+
+__device__ __forceinline__ void row_source(const FfnArgs& a, int j, const uint8_t*& blob, int& t, int& inter) {
+  const int nr = a.T * a.K;
+  if (j < nr) {
+    const int e = a.topk_idx[j];
+    // an index outside [0, E) selects no weights: the row contributes zero
+    blob = (e < 0 || e >= a.E) ? nullptr
+                               : a.experts + (a.offsets ? a.offsets[e] : static_cast<uint64_t>(e) * a.stride);
+    t = j / a.K;
+    inter = a.I;
+  } else {
+    blob = a.shared;
+    t = j - nr;
+    inter = a.Is;
+  }
+}
+
+// gate/up + SwiGLU.  Grid (rows, max(I,Is)/16); one workgroup = one row j and
+// one gate/up pair-tile p (16 gate rows + the 16 matching up rows); its four
+// waves split the 64-column chunks of H.  Per lane and chunk: one 16-byte
+// load = 8 gate + 8 up values for each of two 32-column halves.
+template <int ACT>
+__global__ __launch_bounds__(256) void k_gateup_gemv(FfnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t xs[kMaxH];
+  __shared__ float sx[kMaxH / 32];
+  __shared__ float red[4][2][16];
+  const uint8_t* blob;
+  int t, inter;
+  const int j = blockIdx.x;
+  row_source(a, j, blob, t, inter);
+  const int p = blockIdx.y;
+  if (p * 16 >= inter) return;
+  if (blob == nullptr) {
+    if (threadIdx.x < 16) a.h[static_cast<size_t>(j) * a.hstride + 16 * p + threadIdx.x] = 0.0f;
+    return;
+  }
+  const int H = a.H, G = a.G;
+  const uint16_t* xr = a.x + static_cast<size_t>(t) * H;
+  for (int c = threadIdx.x * 8; c < H; c += 256 * 8)
+    *reinterpret_cast<uint4*>(xs + c) = *reinterpret_cast<const uint4*>(xr + c);
+  __syncthreads();
+  const int ng = H / G;
+  for (int g = threadIdx.x; g < ng; g += 256) {
+    float s = 0.0f;
+    for (int i = 0; i < G; ++i) s += act_to_f32<ACT>(xs[g * G + i]);
+    sx[g] = s;
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, kb = lane >> 4;
+  const int nc = H / 64;
+  const uint4* qblk = reinterpret_cast<const uint4*>(blob) + static_cast<size_t>(p) * nc * 64;
+  const uint8_t* ssec = blob + blob_gu_s(H, inter);
+  float accA = 0.0f, accB = 0.0f;
+  constexpr int kBatch = 8;
+  for (int c0 = wave; c0 < nc; c0 += 4 * kBatch) {
+    uint4 q[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int c = c0 + 4 * b;
+      q[b] = (c < nc) ? qblk[static_cast<size_t>(c) * 64 + lane] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int c = c0 + 4 * b;
+      if (c < nc) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int col = 64 * c + 32 * ks + 8 * kb;
+          const int g = (64 * c + 32 * ks) / G;
+          const ScaleBias sb = load_sb(ssec, p, ng, g, n);
+          const uint4 xv = *reinterpret_cast<const uint4*>(xs + col);
+          const float pA = word_dot_v<ACT>(ks ? q[b].y : q[b].x, xv);
+          const float pB = word_dot_v<ACT>(ks ? q[b].w : q[b].z, xv);
+          accA = fmaf(16.0f * sb.sA, pA, accA);
+          accB = fmaf(16.0f * sb.sB, pB, accB);
+          if (kb == 0 && ((64 * c + 32 * ks) % G) == 0) {
+            accA = fmaf(sb.bA - 16.0f * sb.sA, sx[g], accA);
+            accB = fmaf(sb.bB - 16.0f * sb.sB, sx[g], accB);
+          }
+        }
+      }
+    }
+  }
+  accA += __shfl_xor(accA, 16, kWave);
+  accA += __shfl_xor(accA, 32, kWave);
+  accB += __shfl_xor(accB, 16, kWave);
+  accB += __shfl_xor(accB, 32, kWave);
+  if (kb == 0) {
+    red[wave][0][n] = accA;
+    red[wave][1][n] = accB;
+  }
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    const int i = threadIdx.x;
+    const float ga = ((red[0][0][i] + red[1][0][i]) + red[2][0][i]) + red[3][0][i];
+    const float up = ((red[0][1][i] + red[1][1][i]) + red[2][1][i]) + red[3][1][i];
+    const float hv = ga / (1.0f + expf(-ga)) * up;
+    a.h[static_cast<size_t>(j) * a.hstride + 16 * p + i] = hv;
+  }
+}
+
+// down projection.  Grid (rows, ceil(H/128)); four waves, each one 32-row
+// down pair-tile; the row's h (fp32) is staged in LDS with its group sums.
+__global__ __launch_bounds__(256) void k_down_gemv(FfnArgs a) {
+  __shared__ __attribute__((aligned(16))) float hs[kMaxInter];
+  __shared__ float sh[kMaxInter / 32];
+  const uint8_t* blob;
+  int t, inter;
+  const int j = blockIdx.x;
+  row_source(a, j, blob, t, inter);
+  const int H = a.H, G = a.G;
+  if (blob == nullptr) {
+    for (int n = threadIdx.x; n < H; n += 256) a.yrow[static_cast<size_t>(j) * H + n] = 0.0f;
+    return;
+  }
+  const float* hr = a.h + static_cast<size_t>(j) * a.hstride;
+  for (int i = threadIdx.x * 4; i < inter; i += 256 * 4)
+    *reinterpret_cast<float4*>(hs + i) = *reinterpret_cast<const float4*>(hr + i);
+  __syncthreads();
+  const int ng = inter / G;
+  for (int g = threadIdx.x; g < ng; g += 256) {
+    float s = 0.0f;
+    for (int i = 0; i < G; ++i) s += hs[g * G + i];
+    sh[g] = s;
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int p = blockIdx.y * 4 + wave;
+  if (p * 32 >= H) return;
+  const int n = lane & 15, kb = lane >> 4;
+  const int nc = inter / 64;
+  const uint4* qblk = reinterpret_cast<const uint4*>(blob + blob_d_q(H, inter)) + static_cast<size_t>(p) * nc * 64;
+  const uint8_t* ssec = blob + blob_d_s(H, inter, G);
+  float accA = 0.0f, accB = 0.0f;
+  constexpr int kBatch = 8;
+  for (int c0 = 0; c0 < nc; c0 += kBatch) {
+    uint4 q[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int c = c0 + b;
+      q[b] = (c < nc) ? qblk[static_cast<size_t>(c) * 64 + lane] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int c = c0 + b;
+      if (c < nc) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int col = 64 * c + 32 * ks + 8 * kb;
+          const int g = (64 * c + 32 * ks) / G;
+          const ScaleBias sb = load_sb(ssec, p, ng, g, n);
+          const float pA = word_dot_q(ks ? q[b].y : q[b].x, hs + col);
+          const float pB = word_dot_q(ks ? q[b].w : q[b].z, hs + col);
+          accA = fmaf(sb.sA, pA, accA);
+          accB = fmaf(sb.sB, pB, accB);
+          if (kb == 0 && ((64 * c + 32 * ks) % G) == 0) {
+            accA = fmaf(sb.bA, sh[g], accA);
+            accB = fmaf(sb.bB, sh[g], accB);
+          }
+        }
+      }
+    }
+  }
+  accA += __shfl_xor(accA, 16, kWave);
+  accA += __shfl_xor(accA, 32, kWave);
+  accB += __shfl_xor(accB, 16, kWave);
+  accB += __shfl_xor(accB, 32, kWave);
+  if (kb == 0) {
+    float* yr = a.yrow + static_cast<size_t>(j) * H + 32 * p;
+    yr[n] = accA;
+    yr[16 + n] = accB;
+  }
+}
+
+// Block sum over 256 threads in a fixed order.
+__device__ __forceinline__ float block_sum_256(float v, float* lds4) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) lds4[wave] = v;
+  __syncthreads();
+  const float s = ((lds4[0] + lds4[1]) + lds4[2]) + lds4[3];
+  __syncthreads();
+  return s;
+}
+
+template <int ACT, bool EPI>
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ yrow, const int32_t* __restrict__ inv,
+                                                 const float* __restrict__ w, const float* __restrict__ gamma,
+                                                 int T, int K, int H, int has_shared, float* __restrict__ y,
+                                                 float* __restrict__ r, uint16_t* __restrict__ x_next) {
+  __shared__ float lds4[4];
+  const int t = blockIdx.x;
+  constexpr int kPer = kMaxH / 256;
+  float rr[kPer];
+  float ss = 0.0f;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int n = threadIdx.x + 256 * u;
+    rr[u] = 0.0f;
+    if (n < H) {
+      float acc = 0.0f;
+      for (int k = 0; k < K; ++k) {
+        const int row = inv ? inv[t * K + k] : t * K + k;
+        acc = fmaf(w[t * K + k], yrow[static_cast<size_t>(row) * H + n], acc);
+      }
+      if (has_shared) acc = fmaf(gamma[t], yrow[static_cast<size_t>(T * K + t) * H + n], acc);
+      if (y) y[static_cast<size_t>(t) * H + n] = acc;
+      if constexpr (EPI) {
+        const float v = r[static_cast<size_t>(t) * H + n] + acc;
+        r[static_cast<size_t>(t) * H + n] = v;
+        rr[u] = v;
+        ss = fmaf(v, v, ss);
+      }
+    }
+  }
+  if constexpr (EPI) {
+    const float tot = block_sum_256(ss, lds4);
+    const float inv_rms = 1.0f / sqrtf(tot / static_cast<float>(H) + 1e-6f);
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int n = threadIdx.x + 256 * u;
+      if (n < H) x_next[static_cast<size_t>(t) * H + n] = f32_to_act<ACT>(rr[u] * inv_rms);
+    }
+  }
+}
+
+template <int ACT>
+__global__ __launch_bounds__(256) void k_epilogue(const float* __restrict__ y, float* __restrict__ r,
+                                                  uint16_t* __restrict__ x_next, int H) {
+  __shared__ float lds4[4];
+  const int t = blockIdx.x;
+  constexpr int kPer = kMaxH / 256;
+  float rr[kPer];
+  float ss = 0.0f;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int n = threadIdx.x + 256 * u;
+    rr[u] = 0.0f;
+    if (n < H) {
+      const float v = r[static_cast<size_t>(t) * H + n] + y[static_cast<size_t>(t) * H + n];
+      r[static_cast<size_t>(t) * H + n] = v;
+      rr[u] = v;
+      ss = fmaf(v, v, ss);
+    }
+  }
+  const float tot = block_sum_256(ss, lds4);
+  const float inv_rms = 1.0f / sqrtf(tot / static_cast<float>(H) + 1e-6f);
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int n = threadIdx.x + 256 * u;
+    if (n < H) x_next[static_cast<size_t>(t) * H + n] = f32_to_act<ACT>(rr[u] * inv_rms);
+  }
+}
+
+hipError_t launch_gateup_gemv(int act, const FfnArgs& a, hipStream_t s) {
+  const int rows = a.T * a.K + (a.Is > 0 ? a.T : 0);
+  dim3 grid(rows, (a.hstride + 15) / 16);
+  if (act == 2) hipLaunchKernelGGL(k_gateup_gemv<2>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(k_gateup_gemv<1>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_gemv(const FfnArgs& a, hipStream_t s) {
+  const int rows = a.T * a.K + (a.Is > 0 ? a.T : 0);
+  dim3 grid(rows, (a.H + 127) / 128);
+  hipLaunchKernelGGL(k_down_gemv, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(int act, const float* yrow, const int32_t* inv, const float* w, const float* gamma, int T,
+                          int K, int H, bool has_shared, float* y, float* r, uint16_t* x_next, hipStream_t s) {
+  const int hs = has_shared ? 1 : 0;
+  if (r == nullptr) {
+    hipLaunchKernelGGL((k_combine<2, false>), dim3(T), dim3(256), 0, s, yrow, inv, w, gamma, T, K, H, hs, y, r,
+                       x_next);
+  } else if (act == 2) {
+    hipLaunchKernelGGL((k_combine<2, true>), dim3(T), dim3(256), 0, s, yrow, inv, w, gamma, T, K, H, hs, y, r,
+                       x_next);
+  } else {
+    hipLaunchKernelGGL((k_combine<1, true>), dim3(T), dim3(256), 0, s, yrow, inv, w, gamma, T, K, H, hs, y, r,
+                       x_next);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_epilogue(int act, const float* y, float* r, uint16_t* x_next, int T, int H, hipStream_t s) {
+  if (act == 2) hipLaunchKernelGGL(k_epilogue<2>, dim3(T), dim3(256), 0, s, y, r, x_next, H);
+  else hipLaunchKernelGGL(k_epilogue<1>, dim3(T), dim3(256), 0, s, y, r, x_next, H);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,53 @@
+// Internal launch functions of the MoE kernels (host side).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kMaxH = 8192;        // hidden size limit (router keeps a row in registers)
+constexpr int kMaxInter = 4096;    // intermediate size limit (down GEMV stages h in LDS)
+constexpr int kMaxExperts = 1024;  // top-k holds E/64 logits per lane; bucketing uses one workgroup
+constexpr int kMaxTopK = 64;       // one selected expert per lane
+
+// Routed rows of a batch: row j < T*K is (token j/K, rank j%K) in slot order,
+// or the r-th row of the expert-sorted order in the grouped family; rows
+// T*K + t (t < T) are the shared expert's.
+struct FfnArgs {
+  const uint16_t* x;          // [T][H] activations
+  const int32_t* topk_idx;    // [T][K]
+  const uint8_t* experts;     // routed blob base
+  uint64_t stride;            // blob stride when offsets == nullptr
+  const uint64_t* offsets;    // [E] byte offsets or nullptr
+  const uint8_t* shared;      // shared blob or nullptr
+  float* h;                   // [rows][hstride] SwiGLU activations
+  float* yrow;                // [rows][H] per-row expert outputs (unweighted)
+  // grouped family
+  const int32_t* perm;        // [T*K] sorted row -> slot t*K+k
+  const int32_t* expert_off;  // [E+1]
+  const int32_t* active;      // active experts ascending
+  const int32_t* n_active;    // [1]
+  int T, H, K, I, Is, G, E;
+  int hstride;                // max(I, Is)
+};
+
+hipError_t launch_router_logits(int act, const uint16_t* x, const uint16_t* wr, const float* bias, float* logits,
+                                int T, int H, int E, hipStream_t s);
+hipError_t launch_topk(const float* logits, int T, int E, int K, int32_t* idx, float* w, float* gamma,
+                       hipStream_t s);
+hipError_t launch_permute(const int32_t* idx, int n, int E, int32_t* off, int32_t* perm, int32_t* inv,
+                          int32_t* active, int32_t* n_active, hipStream_t s);
+
+hipError_t launch_gateup_gemv(int act, const FfnArgs& a, hipStream_t s);
+hipError_t launch_down_gemv(const FfnArgs& a, hipStream_t s);
+hipError_t launch_gateup_grouped(int act, const FfnArgs& a, hipStream_t s);
+hipError_t launch_down_grouped(const FfnArgs& a, hipStream_t s);
+
+// y[t] = sum_k w[t,k] yrow[row(t,k)] + gamma[t] yrow[T*K+t]; row(t,k) = inv ? inv[t*K+k] : t*K+k.
+// With r != nullptr also the stack epilogue (r += y; x_next = rne(r / rms(r))).
+hipError_t launch_combine(int act, const float* yrow, const int32_t* inv, const float* w, const float* gamma,
+                          int T, int K, int H, bool has_shared, float* y, float* r, uint16_t* x_next,
+                          hipStream_t s);
+hipError_t launch_epilogue(int act, const float* y, float* r, uint16_t* x_next, int T, int H, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,235 @@
+// Router GEMV, top-K selection, token-to-expert bucketing.
+//
+// Routing step of the block (the how-it-works list of the page "Show HN: Run
+// an 80B Qwen in 4.3 GB of RAM on a Mac and a 35B on an iPhone": every token
+// goes to 10 of 512 or 8 of 256 experts).  Selection order is (logit desc,
+// expert index asc); weights are the softmax restricted to the selected set,
+// which equals a softmax over all experts followed by renormalisation.
+#include "moe_common.h"
+#include "moe_kernels.h"
+
+namespace moe {
+
+// z[t][row] = sum_h x[t][h] * Wr[row][h] (+ bias[row] for row < E).
+// One wave per router row; each lane owns 8 consecutive columns per 512-column
+// stride, so every 16-byte load of the wave is one coalesced 1 KiB run.  Lane
+// partials are sequential fp32 FMAs of exact products (16-bit x times fp16 w),
+// then a fixed butterfly: the summation tree has depth 8*ceil(H/512) + 6.
+template <int ACT>
+__global__ __launch_bounds__(64) void k_router_logits(const uint16_t* __restrict__ x,
+                                                      const uint16_t* __restrict__ wr,
+                                                      const float* __restrict__ bias,
+                                                      float* __restrict__ logits, int T, int H, int E,
+                                                      int tok_per_block) {
+  const int lane = threadIdx.x;
+  const int row = blockIdx.x;
+  const int t0 = blockIdx.y * tok_per_block;
+  const int t1 = min(T, t0 + tok_per_block);
+  const int nit = (H + 511) / 512;
+  uint4 wv[kMaxH / 512];
+#pragma unroll
+  for (int it = 0; it < kMaxH / 512; ++it) {
+    const int col = it * 512 + lane * 8;
+    wv[it] = (it < nit && col < H) ? *reinterpret_cast<const uint4*>(wr + static_cast<size_t>(row) * H + col)
+                                   : make_uint4(0, 0, 0, 0);
+  }
+  const float b = (row < E && bias != nullptr) ? bias[row] : 0.0f;
+  for (int t = t0; t < t1; ++t) {
+    const uint16_t* xr = x + static_cast<size_t>(t) * H;
+    float acc = 0.0f;
+#pragma unroll
+    for (int it = 0; it < kMaxH / 512; ++it) {
+      const int col = it * 512 + lane * 8;
+      if (it < nit && col < H) {
+        const uint4 xv = *reinterpret_cast<const uint4*>(xr + col);
+        const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
+        const uint32_t ws[4] = {wv[it].x, wv[it].y, wv[it].z, wv[it].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc = fmaf(act_to_f32<ACT>(xs[i] & 0xFFFFu), f16_bits_to_f32(ws[i] & 0xFFFFu), acc);
+          acc = fmaf(act_to_f32<ACT>(xs[i] >> 16), f16_bits_to_f32(ws[i] >> 16), acc);
+        }
+      }
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) logits[static_cast<size_t>(t) * (E + 1) + row] = (row < E) ? acc + b : acc;
+  }
+}
+
+// One wave per token: K rounds of a wave-wide arg-max over E/64 values per
+// lane (lane l holds experts l, l+64, ...).  The comparator prefers the larger
+// logit, then the lower index, so ties resolve to the lower expert index.
+__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int T, int E, int K,
+                                              int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+                                              float* __restrict__ gamma) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* z = logits + static_cast<size_t>(t) * (E + 1);
+  constexpr int kJ = kMaxExperts / 64;
+  float v[kJ];
+  uint32_t avail = 0;
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) {
+    const int e = lane + 64 * j;
+    if (e < E) {
+      v[j] = z[e];
+      avail |= 1u << j;
+    } else {
+      v[j] = 0.0f;
+    }
+  }
+  float my_v = 0.0f, v0 = 0.0f;
+  int my_i = 0;
+  for (int k = 0; k < K; ++k) {
+    float bv = 0.0f;
+    int bi = 0x7FFFFFFF;
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+      // j ascending = index ascending, so a strict '>' keeps the lower index on ties
+      if (((avail >> j) & 1u) && (bi == 0x7FFFFFFF || v[j] > bv)) {
+        bv = v[j];
+        bi = lane + 64 * j;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off, kWave);
+      const int oi = __shfl_xor(bi, off, kWave);
+      const bool take = (oi != 0x7FFFFFFF) && (bi == 0x7FFFFFFF || ov > bv || (ov == bv && oi < bi));
+      if (take) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (k == 0) v0 = bv;
+    if (lane == k) {
+      my_v = bv;
+      my_i = bi;
+    }
+    if ((bi & 63) == lane) avail &= ~(1u << (bi >> 6));
+  }
+  const float ex = (lane < K) ? expf(my_v - v0) : 0.0f;
+  const float s = wave_sum(ex);
+  if (lane < K) {
+    topk_idx[static_cast<size_t>(t) * K + lane] = my_i;
+    topk_w[static_cast<size_t>(t) * K + lane] = ex / s;
+  }
+  if (lane == 0 && gamma != nullptr) gamma[t] = 1.0f / (1.0f + expf(-z[E]));
+}
+
+// Inclusive scan over a 1024-thread block (wave shuffles + one LDS pass).
+__device__ __forceinline__ int block_incl_scan_1024(int v, int* lds16, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(v, off, kWave);
+    if (lane >= off) v += o;
+  }
+  if (lane == 63) lds16[wave] = v;
+  __syncthreads();
+  int base = 0, tot = 0;
+  for (int w = 0; w < 16; ++w) {
+    const int s = lds16[w];
+    if (w < wave) base += s;
+    tot += s;
+  }
+  __syncthreads();
+  total = tot;
+  return v + base;
+}
+
+// Stable counting sort of the n = T*K routed rows by expert, one 1024-thread
+// workgroup: histogram (LDS integer atomics), exclusive prefix sum over the
+// experts, then a scatter in which each wave computes the rank of its rows
+// among equal experts with ballots and the waves commit in order, so rows of
+// one expert keep their (t, k) order.  Also lists the active experts in
+// ascending order and their count.
+__global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ topk_idx, int n, int E,
+                                                  int32_t* __restrict__ expert_off, int32_t* __restrict__ perm,
+                                                  int32_t* __restrict__ inv, int32_t* __restrict__ active,
+                                                  int32_t* __restrict__ n_active) {
+  __shared__ int cnt[kMaxExperts];
+  __shared__ int start[kMaxExperts];
+  __shared__ int run[kMaxExperts];
+  __shared__ int scan_tmp[16];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  if (tid < E) {
+    cnt[tid] = 0;
+    run[tid] = 0;
+  }
+  __syncthreads();
+  for (int i = tid; i < n; i += 1024) atomicAdd(&cnt[topk_idx[i]], 1);
+  __syncthreads();
+  const int c = (tid < E) ? cnt[tid] : 0;
+  int total = 0;
+  const int incl = block_incl_scan_1024(c, scan_tmp, total);
+  int n_act_total = 0;
+  const int a_incl = block_incl_scan_1024((tid < E && c > 0) ? 1 : 0, scan_tmp, n_act_total);
+  if (tid < E) {
+    start[tid] = incl - c;
+    expert_off[tid] = incl - c;
+    if (c > 0) active[a_incl - 1] = tid;
+  }
+  if (tid == 0) {
+    expert_off[E] = total;
+    n_active[0] = n_act_total;
+  }
+  __syncthreads();
+  for (int base = 0; base < n; base += 1024) {
+    const int i = base + tid;
+    const bool valid = i < n;
+    const int e = valid ? topk_idx[i] : -1;
+    unsigned long long peers = 0;
+    unsigned long long todo = __ballot(valid);
+    while (todo) {
+      const int leader = __ffsll(static_cast<long long>(todo)) - 1;
+      const int le = __shfl(e, leader, kWave);
+      const unsigned long long m = __ballot(valid && e == le);
+      if (valid && e == le) peers = m;
+      todo &= ~m;
+    }
+    const int rank = __popcll(peers & ((1ull << lane) - 1ull));
+    const bool last_peer = valid && (63 - __clzll(static_cast<long long>(peers))) == lane;
+    for (int w = 0; w < 16; ++w) {
+      if (wave == w && valid) {
+        const int pos = start[e] + run[e] + rank;
+        perm[pos] = i;
+        if (inv != nullptr) inv[i] = pos;
+      }
+      __syncthreads();
+      if (wave == w && last_peer) run[e] += __popcll(peers);
+      __syncthreads();
+    }
+  }
+}
+
+template <int ACT>
+static hipError_t launch_router_t(const uint16_t* x, const uint16_t* wr, const float* bias, float* logits, int T,
+                                  int H, int E, hipStream_t s) {
+  const int tpb = (T <= 8) ? T : 8;
+  dim3 grid(E + 1, (T + tpb - 1) / tpb);
+  hipLaunchKernelGGL(k_router_logits<ACT>, grid, dim3(64), 0, s, x, wr, bias, logits, T, H, E, tpb);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_logits(int act, const uint16_t* x, const uint16_t* wr, const float* bias, float* logits,
+                                int T, int H, int E, hipStream_t s) {
+  return act == 2 ? launch_router_t<2>(x, wr, bias, logits, T, H, E, s)
+                  : launch_router_t<1>(x, wr, bias, logits, T, H, E, s);
+}
+
+hipError_t launch_topk(const float* logits, int T, int E, int K, int32_t* idx, float* w, float* gamma,
+                       hipStream_t s) {
+  hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, K, idx, w, gamma);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute(const int32_t* idx, int n, int E, int32_t* off, int32_t* perm, int32_t* inv,
+                          int32_t* active, int32_t* n_active, hipStream_t s) {
+  hipLaunchKernelGGL(k_permute, dim3(1), dim3(1024), 0, s, idx, n, E, off, perm, inv, active, n_active);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,182 @@
+// Slot pool C ABI: the host policy (slotpool_core.h) plus the HIP side -
+// host-to-device miss copies on a side stream, device offset-table updates
+// on the compute stream, and the RAW / WAR events between the two.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <new>
+#include <vector>
+
+#include "moe_slotpool.h"
+#include "slotpool_core.h"
+
+namespace moe {
+// moe_api.cpp owns the thread-local error string; this file reports through it.
+moe_status set_error(moe_status code, const char* fmt, ...);
+}  // namespace moe
+
+namespace {
+
+constexpr int kOffsetBatch = 32;
+struct OffsetBatch {
+  int32_t n;
+  int32_t expert[kOffsetBatch];
+  uint64_t offset[kOffsetBatch];
+};
+
+__global__ void k_set_offsets(uint64_t* table, OffsetBatch b) {
+  const int i = threadIdx.x;
+  if (i < b.n) table[b.expert[i]] = b.offset[i];
+}
+
+}  // namespace
+
+struct moe_slotpool {
+  moe_slotpool_config cfg{};
+  moe::PoolCore core;
+  std::vector<hipEvent_t> ready, released;  // per layer
+  std::vector<uint8_t> released_recorded;
+  uint64_t bytes_h2d = 0;
+  std::vector<moe::PoolEvent> events;
+  moe_slotpool(const moe_slotpool_config& c)
+      : cfg(c), core(c.n_layers, c.n_experts, c.slots_per_layer, c.aging_period) {}
+  bool host_only() const { return (cfg.flags & MOE_POOL_HOST_ONLY) != 0; }
+};
+
+using moe::set_error;
+
+extern "C" {
+
+moe_status slotpool_create(const moe_slotpool_config* c, moe_slotpool** out) {
+  if (!c || !out) return set_error(MOE_EINVAL, "NULL config or out");
+  *out = nullptr;
+  if (c->n_layers <= 0 || c->n_experts <= 0 || c->slots_per_layer <= 0 || c->aging_period < 0)
+    return set_error(MOE_ESHAPE, "bad pool geometry (layers=%d experts=%d slots=%d aging=%d)", c->n_layers,
+                     c->n_experts, c->slots_per_layer, c->aging_period);
+  if (c->slots_per_layer > c->n_experts)
+    return set_error(MOE_ESHAPE, "slots_per_layer=%d exceeds n_experts=%d", c->slots_per_layer, c->n_experts);
+  if (c->flags & ~MOE_POOL_HOST_ONLY) return set_error(MOE_EINVAL, "unknown flags 0x%x", c->flags);
+  const bool host_only = (c->flags & MOE_POOL_HOST_ONLY) != 0;
+  if (!host_only) {
+    if (c->blob_stride == 0 || c->blob_stride % 256 || c->blob_bytes == 0 || c->blob_bytes > c->blob_stride)
+      return set_error(MOE_EINVAL, "blob_stride must be a positive multiple of 256 and >= blob_bytes");
+    if (!c->host_blobs || !c->device_slab || !c->device_offsets || !c->copy_stream)
+      return set_error(MOE_EINVAL, "host_blobs, device_slab, device_offsets and copy_stream are required");
+    if (reinterpret_cast<uintptr_t>(c->device_slab) % 256)
+      return set_error(MOE_EINVAL, "device_slab must be 256-byte aligned");
+  }
+  moe_slotpool* p = new (std::nothrow) moe_slotpool(*c);
+  if (!p) return set_error(MOE_ENOMEM, "pool metadata allocation");
+  if (!host_only) {
+    p->ready.assign(c->n_layers, nullptr);
+    p->released.assign(c->n_layers, nullptr);
+    p->released_recorded.assign(c->n_layers, 0);
+    for (int l = 0; l < c->n_layers; ++l) {
+      hipError_t e1 = hipEventCreateWithFlags(&p->ready[l], hipEventDisableTiming);
+      hipError_t e2 = hipEventCreateWithFlags(&p->released[l], hipEventDisableTiming);
+      if (e1 != hipSuccess || e2 != hipSuccess) {
+        slotpool_destroy(p);
+        return set_error(MOE_EHIP, "hipEventCreate: %s", hipGetErrorString(e1 != hipSuccess ? e1 : e2));
+      }
+    }
+  }
+  *out = p;
+  return set_error(MOE_OK, "");
+}
+
+moe_status slotpool_acquire(moe_slotpool* p, int32_t layer, const int32_t* experts, int32_t n, uint64_t step,
+                            moe_stream compute, int32_t* slot_out, int32_t* victim_out, uint8_t* hit_out) {
+  if (!p) return set_error(MOE_EINVAL, "pool is NULL");
+  if (layer < 0 || layer >= p->cfg.n_layers) return set_error(MOE_EINVAL, "layer %d out of range", layer);
+  if (n < 0 || (n > 0 && !experts)) return set_error(MOE_EINVAL, "bad expert list");
+  const moe::PoolCore::Result r = p->core.acquire(layer, experts, n, step, p->events);
+  if (r == moe::PoolCore::kBadInput) return set_error(MOE_EINVAL, "expert ids must be distinct and in [0, %d)", p->cfg.n_experts);
+  if (r == moe::PoolCore::kFull)
+    return set_error(MOE_EPOOLFULL, "layer %d: more misses than free or evictable slots", layer);
+  int n_miss = 0;
+  for (int i = 0; i < n; ++i) {
+    if (slot_out) slot_out[i] = p->events[i].slot;
+    if (victim_out) victim_out[i] = p->events[i].victim;
+    if (hit_out) hit_out[i] = p->events[i].hit ? 1 : 0;
+    if (!p->events[i].hit) ++n_miss;
+  }
+  if (p->host_only()) {
+    p->bytes_h2d += static_cast<uint64_t>(n_miss) * p->cfg.blob_bytes;
+    return set_error(MOE_OK, "");
+  }
+  if (n_miss == 0) return set_error(MOE_OK, "");
+  hipStream_t cs = reinterpret_cast<hipStream_t>(p->cfg.copy_stream);
+  hipStream_t ks = reinterpret_cast<hipStream_t>(compute);
+  const uint64_t stride = p->cfg.blob_stride;
+  const uint64_t S = static_cast<uint64_t>(p->cfg.slots_per_layer), E = static_cast<uint64_t>(p->cfg.n_experts);
+  hipError_t e = hipSuccess;
+  if (p->released_recorded[layer]) e = hipStreamWaitEvent(cs, p->released[layer], 0);  // WAR
+  uint8_t* slab = p->cfg.device_slab + static_cast<uint64_t>(layer) * S * stride;
+  const uint8_t* host = p->cfg.host_blobs + static_cast<uint64_t>(layer) * E * stride;
+  OffsetBatch batch{};
+  for (int i = 0; i < n && e == hipSuccess; ++i) {
+    const moe::PoolEvent& ev = p->events[i];
+    if (ev.hit) continue;
+    e = hipMemcpyAsync(slab + static_cast<uint64_t>(ev.slot) * stride, host + static_cast<uint64_t>(ev.expert) * stride,
+                       p->cfg.blob_bytes, hipMemcpyHostToDevice, cs);
+    p->bytes_h2d += p->cfg.blob_bytes;
+    batch.expert[batch.n] = ev.expert;
+    batch.offset[batch.n] = static_cast<uint64_t>(ev.slot) * stride;
+    if (++batch.n == kOffsetBatch) {
+      hipLaunchKernelGGL(k_set_offsets, dim3(1), dim3(kOffsetBatch), 0, ks,
+                         p->cfg.device_offsets + static_cast<uint64_t>(layer) * E, batch);
+      batch.n = 0;
+      if (e == hipSuccess) e = hipGetLastError();
+    }
+  }
+  if (e == hipSuccess && batch.n > 0) {
+    hipLaunchKernelGGL(k_set_offsets, dim3(1), dim3(kOffsetBatch), 0, ks,
+                       p->cfg.device_offsets + static_cast<uint64_t>(layer) * E, batch);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) e = hipEventRecord(p->ready[layer], cs);
+  if (e == hipSuccess) e = hipStreamWaitEvent(ks, p->ready[layer], 0);  // RAW
+  if (e != hipSuccess) return set_error(MOE_EHIP, "slot pool copy/offset enqueue: %s", hipGetErrorString(e));
+  return set_error(MOE_OK, "");
+}
+
+moe_status slotpool_release(moe_slotpool* p, int32_t layer, moe_stream compute) {
+  if (!p) return set_error(MOE_EINVAL, "pool is NULL");
+  if (layer < 0 || layer >= p->cfg.n_layers) return set_error(MOE_EINVAL, "layer %d out of range", layer);
+  p->core.release(layer);
+  if (!p->host_only()) {
+    hipError_t e = hipEventRecord(p->released[layer], reinterpret_cast<hipStream_t>(compute));
+    if (e != hipSuccess) return set_error(MOE_EHIP, "release event: %s", hipGetErrorString(e));
+    p->released_recorded[layer] = 1;
+  }
+  return set_error(MOE_OK, "");
+}
+
+moe_status slotpool_evict(moe_slotpool* p, int32_t layer, int32_t expert) {
+  if (!p) return set_error(MOE_EINVAL, "pool is NULL");
+  const moe::PoolCore::Result r = p->core.evict(layer, expert);
+  if (r == moe::PoolCore::kBadInput) return set_error(MOE_EINVAL, "layer/expert out of range");
+  if (r == moe::PoolCore::kBusy) return set_error(MOE_EBUSY, "layer %d expert %d is pinned", layer, expert);
+  return set_error(MOE_OK, "");
+}
+
+moe_status slotpool_stats(const moe_slotpool* p, moe_slotpool_stats* out) {
+  if (!p || !out) return set_error(MOE_EINVAL, "NULL pool or out");
+  out->hits = p->core.hits();
+  out->misses = p->core.misses();
+  out->evictions = p->core.evictions();
+  out->bytes_h2d = p->bytes_h2d;
+  return set_error(MOE_OK, "");
+}
+
+void slotpool_destroy(moe_slotpool* p) {
+  if (!p) return;
+  for (hipEvent_t ev : p->ready)
+    if (ev) hipEventDestroy(ev);
+  for (hipEvent_t ev : p->released)
+    if (ev) hipEventDestroy(ev);
+  delete p;
+}
+
+}  // extern "C"

@@ -1,0 +1,155 @@
+"""CPU-side checks of the C ABI library: it loads, exports what the headers
+declare, the host packer and the pool policy match the oracle, and argument
+validation rejects bad calls before touching the GPU."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import blob_ref
+from oracle.pool_sim import PoolFull, PoolSim
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    from int4_routed_expert_router_amd import _lib as L
+    return L
+
+
+def header_symbols():
+    syms = set()
+    for name in os.listdir(os.path.join(ROOT, "include")):
+        if name.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", name)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            for m in re.finditer(r"\b(moe_[a-z_0-9]+|slotpool_[a-z_]+)\s*\(", text):
+                syms.add(m.group(1))
+    return syms
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib()
+    lib = L.lib()
+    syms = header_symbols()
+    assert len(syms) >= 20
+    for s in sorted(syms):
+        assert hasattr(lib, s), f"{s} declared in include/ but not exported"
+    assert set(L.PROTOS) <= syms | {"moe_last_error", "moe_version"}
+
+
+def test_blob_bytes_and_packer_match_oracle():
+    from int4_routed_expert_router_amd import api
+    assert api.blob_bytes(2048, 512, 64) == 1_769_472 == blob_ref.blob_bytes(2048, 512, 64)
+    assert api.blob_bytes(100, 64, 32) == 0
+    for wl in (synth.TINY, synth.DEC80):
+        raw = synth.expert_raw(wl, 1, 2)
+        got = api.pack_expert(raw, wl.hidden, wl.inter, wl.group)
+        back = blob_ref.parse_blob(got, wl.hidden, wl.inter, wl.group)
+        for name in raw:
+            for a, b in zip(raw[name], back[name]):
+                assert np.array_equal(a, b)
+
+
+def test_packer_rejects_bad_nibbles():
+    from int4_routed_expert_router_amd import api, MoeError
+    raw = synth.expert_raw(synth.TINY, 0, 0)
+    q = raw["gate"][0].copy()
+    q[3, 4] = 16
+    raw["gate"] = (q, raw["gate"][1], raw["gate"][2])
+    with pytest.raises(MoeError, match="MOE_EINVAL"):
+        api.pack_expert(raw, 256, 64, 32)
+
+
+def test_workspace_and_validation_errors():
+    from int4_routed_expert_router_amd import api, MoeError
+    from int4_routed_expert_router_amd._lib import LayerDesc, LayerWeights, lib
+    d = api.Desc(2048, 512, 10, 512, 512, 64)
+    n = api.workspace_bytes(d, 64)
+    assert n > 64 * 11 * 2048 * 4
+    assert api.workspace_bytes(d, 0) > 0
+    bad = [api.Desc(100, 16, 2, 64, 64, 32), api.Desc(256, 16, 17, 64, 64, 32), api.Desc(256, 16, 2, 96, 64, 32),
+           api.Desc(256, 16, 2, 64, 64, 48), api.Desc(256, 2000, 2, 64, 64, 32), api.Desc(256, 16, 2, 64, 32, 32)]
+    for b in bad:
+        with pytest.raises(MoeError, match="MOE_ESHAPE"):
+            api.workspace_bytes(b, 4)
+    with pytest.raises(MoeError, match="MOE_EINVAL"):
+        api.workspace_bytes(api.Desc(256, 16, 2, 64, 64, 32, act_dtype="fp8"), 4)
+    # layer call with NULL weights / misaligned pointers is rejected before any GPU work
+    L = lib()
+    dc = api.Desc(256, 16, 2, 64, 64, 32, "f16").c()
+    w = LayerWeights(None, None, None, 0, None, None)
+    st = L.moe_layer_forward(C.byref(dc), C.byref(w), 16, 4, 16, None, None, None, 256, 10 ** 6, None)
+    assert st == -1 and b"router_w" in L.moe_last_error()
+    w = LayerWeights(4096, None, 4096 + 8, 30720, None, 8192)
+    st = L.moe_layer_forward(C.byref(dc), C.byref(w), 16, 4, 16, None, None, None, 256, 10 ** 6, None)
+    assert st == -1 and b"experts" in L.moe_last_error()
+    w = LayerWeights(4096, None, 8192, 30720, None, 8192)
+    st = L.moe_layer_forward(C.byref(dc), C.byref(w), 16, 4, 16, None, None, None, 256, 16, None)
+    assert st == -3 and b"workspace" in L.moe_last_error()
+    # zero tokens is a no-op even with no buffers
+    assert L.moe_layer_forward(C.byref(dc), C.byref(w), None, 0, None, None, None, None, None, 0, None) == 0
+    assert L.moe_last_error() == b""
+    # graph capture refuses the NULL stream
+    h = C.c_void_p()
+    st = L.moe_stack_graph_create(C.byref(dc), None, 0, None, 0, None, None, None, None, None, None, None, None, 0,
+                                  None, C.byref(h))
+    assert st == -1
+
+
+def _pool_trace(seed, layers, experts, slots, period, steps, k):
+    rng = np.random.default_rng(seed)
+    perm = [rng.permutation(experts) for _ in range(layers)]
+    for s in range(steps):
+        if s and s % 17 == 0:
+            perm = [rng.permutation(experts) for _ in range(layers)]
+        for l in range(layers):
+            p = 1.0 / (1.0 + perm[l]) ** 1.1
+            p /= p.sum()
+            yield s, l, rng.choice(experts, size=k, replace=False, p=p)
+
+
+@pytest.mark.parametrize("seed,slots,period", [(1, 8, 4), (2, 3, 0), (3, 12, 1), (4, 5, 32)])
+def test_pool_core_matches_oracle_simulator(seed, slots, period):
+    from int4_routed_expert_router_amd import api
+    layers, experts, k = 3, 24, 3
+    pool = api.SlotPool(layers, experts, slots, period, blob_bytes_=100, host_only=True)
+    sim = PoolSim(layers, experts, slots, period, blob_bytes=100)
+    for s, l, ex in _pool_trace(seed, layers, experts, slots, period, 120, k):
+        got = pool.acquire(l, ex, s, compute_stream=False)
+        want = sim.acquire(l, ex, s)
+        assert got == want, (s, l, ex)
+        pool.release(l, compute_stream=False)
+        sim.release(l)
+        if s % 11 == 5:
+            pool.evict(l, int(ex[0]))
+            sim.evict(l, int(ex[0]))
+    assert pool.stats() == sim.stats()
+
+
+def test_pool_error_paths():
+    from int4_routed_expert_router_amd import api, MoeError
+    pool = api.SlotPool(1, 6, 2, 4, host_only=True)
+    sim = PoolSim(1, 6, 2, 4)
+    assert pool.acquire(0, [0, 1], 0, False) == sim.acquire(0, [0, 1], 0)
+    with pytest.raises(MoeError, match="MOE_EBUSY"):
+        pool.evict(0, 1)
+    with pytest.raises(MoeError, match="MOE_EPOOLFULL"):
+        pool.acquire(0, [2], 1, False)
+    with pytest.raises(PoolFull):
+        sim.acquire(0, [2], 1)
+    with pytest.raises(MoeError, match="MOE_EINVAL"):
+        pool.acquire(0, [3, 3], 1, False)
+    with pytest.raises(MoeError, match="MOE_EINVAL"):
+        pool.acquire(0, [6], 1, False)
+    pool.release(0, False)
+    sim.release(0)
+    assert pool.acquire(0, [2], 1, False) == sim.acquire(0, [2], 1)
+    assert pool.stats() == sim.stats()
+    with pytest.raises(MoeError, match="MOE_ESHAPE"):
+        api.SlotPool(1, 4, 5, 4, host_only=True)
+    with pytest.raises(MoeError, match="MOE_EINVAL"):
+        api.SlotPool(1, 8, 4, 4)               # device pool without buffers
