@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""Benchmark of the int4 routed-expert MoE block on one MI355X.
+
+Default workload: the 80B-shaped batched layer stack (48 layers, hidden 2048,
+512 experts, top-10, expert and shared intermediate 512, int4 affine group 64,
+64 tokens per step, Zipf(1.3) router bias), all experts resident in HBM with
+distinct seeded weights per layer.  One step = the whole stack (router, top-k,
+bucketing, gate/up+SwiGLU, down, combine, residual epilogue) for 64 tokens,
+replayed as one captured HIP graph.
+
+Prints one JSON line: tokens/s, int4-expert-byte GB/s, the dominant kernel's
+roofline (HIP events around it, inside a replay of the same graph) and the
+fp64 oracle's throughput on the host cores for a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="bat80", choices=["bat80", "dec80", "dec35"])
+    ap.add_argument("--layers", type=int, default=0, help="override the number of layers (0 = workload's)")
+    ap.add_argument("--path", type=int, default=0, help="0 auto, 1 GEMV family, 2 grouped family")
+    ap.add_argument("--eager", action="store_true", help="launch kernels one by one instead of a HIP graph")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true")
+    return ap.parse_args()
+
+
+class Stack:
+    """Device-resident synthetic layer stack (weights generated on the GPU)."""
+
+    def __init__(self, wl, n_layers, path=0):
+        import torch
+        import synth
+        from int4_routed_expert_router_amd import api
+        self.wl, self.L = wl, n_layers
+        self.desc = api.Desc(wl.hidden, wl.n_experts, wl.top_k, wl.inter, wl.shared_inter, wl.group, wl.act_dtype,
+                             path)
+        self.stride = api.blob_bytes(wl.hidden, wl.inter, wl.group)
+        self.sstride = api.blob_bytes(wl.hidden, wl.shared_inter, wl.group)
+        E = wl.n_experts
+        self.slab = torch.empty(n_layers * E * self.stride, dtype=torch.uint8, device="cuda")
+        self.shared = torch.empty(n_layers * self.sstride, dtype=torch.uint8, device="cuda")
+        self.layers = []
+        for l in range(n_layers):
+            ex = self.slab[l * E * self.stride:(l + 1) * E * self.stride]
+            sh = self.shared[l * self.sstride:(l + 1) * self.sstride]
+            api.synth_fill_experts(wl.weight_seed, l, 0, E, wl.hidden, wl.inter, wl.group, wl.scale_lo, wl.scale_hi,
+                                   ex, self.stride)
+            api.synth_fill_experts(wl.weight_seed, l, E, 1, wl.hidden, wl.shared_inter, wl.group, wl.scale_lo,
+                                   wl.scale_hi, sh, self.sstride)
+            wr = torch.from_numpy(synth.router_weights(wl, l).view(np.int16).copy()).cuda()
+            b = synth.router_bias(wl, l)
+            bt = None if b is None else torch.from_numpy(b).cuda()
+            self.layers.append(api.Layer(wr, bt, ex, self.stride, None, sh))
+        T = wl.tokens
+        self.T = T
+        x_bits = synth.tokens(wl)
+        self.x0 = torch.from_numpy(x_bits.view(np.int16).copy()).cuda()
+        xf = (x_bits.astype(np.uint32) << 16).view(np.float32) if wl.act_dtype == "bf16" else \
+            x_bits.view(np.float16).astype(np.float32)
+        self.r0 = torch.from_numpy(xf.copy()).cuda()
+        self.r = self.r0.clone()
+        self.x_buf = torch.empty_like(self.x0)
+        self.ws = api.workspace(self.desc, T)
+        self.idx_all = torch.empty(n_layers, T, wl.top_k, dtype=torch.int32, device="cuda")
+        torch.cuda.synchronize()
+
+    def run_eager(self, stream=None):
+        from int4_routed_expert_router_amd import api
+        self.r.copy_(self.r0)
+        api.stack_forward(self.desc, self.layers, self.x0, self.r, self.x_buf, self.ws, idx_all=self.idx_all,
+                          stream=stream)
+
+    def capture(self, stream):
+        from int4_routed_expert_router_amd import api
+        return api.StackGraph(self.desc, self.layers, self.x0, self.r, self.x_buf, self.ws, stream,
+                              idx_all=self.idx_all)
+
+    def active_experts(self):
+        idx = self.idx_all.cpu().numpy()
+        return [len(np.unique(idx[l])) for l in range(self.L)]
+
+
+def kernel_events(n):
+    import torch
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n)] for _ in range(2)]
+    for e in ev[0] + ev[1]:
+        e.record()          # torch creates the underlying hipEvent on first record
+    torch.cuda.synchronize()
+    return ev[0], ev[1]
+
+
+def set_timer(begin, end, kind):
+    import ctypes as C
+    from int4_routed_expert_router_amd._lib import check, lib
+    arr_b = (C.c_void_p * len(begin))(*[e.cuda_event for e in begin])
+    arr_e = (C.c_void_p * len(end))(*[e.cuda_event for e in end])
+    check(lib().moe_stack_set_kernel_events(arr_b, arr_e, len(begin), kind))
+
+
+def clear_timer():
+    from int4_routed_expert_router_amd._lib import check, lib
+    check(lib().moe_stack_set_kernel_events(None, None, 0, 0))
+
+
+def cpu_baseline(wl, budget_s):
+    """fp64 oracle on a bounded sample: whole layers of the same workload
+    (all tokens), as many as fit the budget (at least one)."""
+    import synth
+    from oracle import moe_oracle as mo
+    cores = len(os.sched_getaffinity(0))
+    x64 = mo.act_bits_to_f64(synth.tokens(wl), wl.act_dtype)
+    t0 = time.perf_counter()
+    done = 0
+    while True:
+        l = done
+
+        def expert(e, shared=False, l=l):
+            r = synth.expert_raw(wl, l, e, shared=shared)
+            return mo.ExpertWeights.from_quant(r["gate"], r["up"], r["down"], wl.group)
+
+        wr = mo.f16_bits_to_f64(synth.router_weights(wl, l))
+        b = synth.router_bias(wl, l)
+        mo.layer_forward(x64, wr, None if b is None else b.astype(np.float64), expert, expert(0, True), wl.top_k)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or done >= wl.layers:
+            break
+    per_layer = el / done
+    tok_s = wl.tokens / (per_layer * wl.layers)
+    return dict(value=tok_s, unit="tokens/s", cores=cores, kind="oracle",
+                sample=f"{done} whole layer(s) x {wl.tokens} tokens of the same workload in {el:.1f} s, "
+                       f"scaled to the {wl.layers}-layer stack (weights generated and dequantised per layer)")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": f"--gpus {args.gpus}: this benchmark runs on exactly one GPU; "
+                                   "multi-GPU sharding is designed (DESIGN.md) but not built"}))
+        sys.exit(2)
+    import torch
+    import synth
+    from int4_routed_expert_router_amd._lib import MOE_TIME_GATEUP
+    wl = synth.WORKLOADS[args.workload]
+    L = args.layers or wl.layers
+    print(f"[bench] building {L}-layer {wl.name} stack ...", file=sys.stderr, flush=True)
+    t0 = time.time()
+    st = Stack(wl, L, args.path)
+    print(f"[bench] stack ready in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+    stream = torch.cuda.Stream()
+    graph = None
+    with torch.cuda.stream(stream):
+        if not args.eager:
+            graph = st.capture(stream)
+
+        def step():
+            st.r.copy_(st.r0)
+            if graph is not None:
+                graph.launch(stream)
+            else:
+                st.run_eager(stream)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t_start
+    ms_per_step = 1e3 * elapsed / args.steps
+    tokens_s = wl.tokens * args.steps / elapsed
+    act = st.active_experts()
+    B = st.stride  # routed and shared blobs have the same size in these workloads
+    int4_bytes = sum((a + 1) * B for a in act)
+    int4_gbs = int4_bytes / (ms_per_step * 1e-3) / 1e9
+    print(f"[bench] {ms_per_step:.3f} ms/step, {tokens_s:.0f} tok/s, int4 {int4_gbs:.0f} GB/s, "
+          f"active experts/layer mean {np.mean(act):.1f}", file=sys.stderr, flush=True)
+
+    roof = None
+    kernel_us = {}
+    if not args.no_kernel_timing:
+        # HIP events around each layer's kernel of one kind, recorded on the
+        # stream that launches it, over eager (launch-by-launch) replays of the
+        # same steps; event nodes inside a captured graph perturb the replay.
+        from int4_routed_expert_router_amd._lib import MOE_TIME_DOWN, MOE_TIME_ROUTER
+        reps = max(3, min(args.steps, 10))
+        for kind, name in ((MOE_TIME_GATEUP, "gateup"), (MOE_TIME_DOWN, "down"), (MOE_TIME_ROUTER, "router")):
+            begin, end = kernel_events(L)
+            durs = []
+            with torch.cuda.stream(stream):
+                for _ in range(reps):
+                    set_timer(begin, end, kind)
+                    st.run_eager(stream)
+                    clear_timer()
+                    torch.cuda.synchronize()
+                    durs.append([begin[l].elapsed_time(end[l]) for l in range(L)])
+            kernel_us[name] = float(np.mean(durs)) * 1e3
+        avg_us = kernel_us["gateup"]
+        gu_bytes = (st.desc.inter * st.desc.hidden + 8 * st.desc.inter * st.desc.hidden // st.desc.group_size)
+        per_launch = float(np.mean([(a + 1) * gu_bytes for a in act]))
+        achieved = per_launch / (avg_us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "k_gateup_grouped (int4 gate/up + SwiGLU)" if (args.path == 2 or (
+                    args.path == 0 and wl.tokens * wl.top_k > 32)) else "k_gateup_gemv (int4 gate/up + SwiGLU)",
+                "avg_us": round(avg_us, 2), "bytes_per_launch": int(per_launch),
+                "events": "HIP events on the launch stream around each layer's gate/up kernel, eager replay"}
+        print(f"[bench] kernel avg us: " + ", ".join(f"{k} {v:.2f}" for k, v in kernel_us.items())
+              + f"; gate/up {achieved:.0f} GB/s", file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the fp64 oracle on the host ...", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+
+    out = {
+        "metric": "MoE-layer tokens/sec + achieved HBM GB/s on int4 expert bytes (80B-shaped)",
+        "value": round(tokens_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 activations, int4 weights, fp32 accumulate",
+        "data": "synthetic (seeded; random-init weights of the stated shapes)",
+        "int4_expert_GBps": round(int4_gbs, 1),
+        "int4_frac_of_hbm_peak": round(int4_gbs / HBM_PEAK_GBS, 4),
+        "active_experts_per_layer": round(float(np.mean(act)), 2),
+        "config": {"workload": f"{wl.name}: {L} layers, hidden {wl.hidden}, {wl.n_experts} experts top-{wl.top_k}, "
+                               f"inter {wl.inter}, shared {wl.shared_inter}, int4 group {wl.group}, "
+                               f"{wl.tokens} tokens/step, Zipf {wl.zipf_s}",
+                   "global_batch": wl.tokens, "layers": L, "path": ["auto", "gemv", "grouped"][args.path],
+                   "graph": not args.eager, "parallelism": "single GPU"},
+        "roofline": roof,
+        "kernel_avg_us": {k: round(v, 2) for k, v in kernel_us.items()},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -213,6 +213,15 @@ moe_status moe_stack_graph_create(const moe_layer_desc* desc, const moe_layer_we
 moe_status moe_graph_launch(moe_graph* g, moe_stream stream);
 void moe_graph_destroy(moe_graph* g);
 
+/* Optional timing of one kernel per layer inside moe_stack_forward and
+ * graphs captured by moe_stack_graph_create on this thread: when set,
+ * begin[l] and end[l] (hipEvent_t handles created by the caller with timing
+ * enabled) are recorded on the stream right before and right after layer l's
+ * kernel of the chosen kind (MOE_TIME_*).  n_layers = 0 disables it.  The
+ * setting is read when the stack is enqueued or captured. */
+enum { MOE_TIME_GATEUP = 0, MOE_TIME_DOWN = 1, MOE_TIME_ROUTER = 2 };
+moe_status moe_stack_set_kernel_events(void* const* begin, void* const* end, int32_t n_layers, int32_t kind);
+
 /* Thread-local description of the last error on this thread (valid until
  * the next call on the thread); "" when the last call succeeded. */
 const char* moe_last_error(void);

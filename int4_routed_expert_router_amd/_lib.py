@@ -14,6 +14,7 @@ MOE_F16, MOE_BF16 = 1, 2
 MOE_PATH_AUTO, MOE_PATH_GEMV, MOE_PATH_GROUPED = 0, 1, 2
 MOE_GEMV_MAX_ROWS = 32
 MOE_POOL_HOST_ONLY = 1
+MOE_TIME_GATEUP, MOE_TIME_DOWN, MOE_TIME_ROUTER = 0, 1, 2
 
 STATUS_NAMES = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_ESHAPE", -3: "MOE_EWORKSPACE", -4: "MOE_EHIP",
                 -5: "MOE_EPOOLFULL", -6: "MOE_EBUSY", -7: "MOE_ENOMEM"}
@@ -65,6 +66,7 @@ PROTOS = {
     "moe_stack_graph_create": (i32, [vp, vp, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, C.c_size_t, vp,
                                      C.POINTER(vp)]),
     "moe_graph_launch": (i32, [vp, vp]),
+    "moe_stack_set_kernel_events": (i32, [vp, vp, i32, i32]),
     "moe_graph_destroy": (None, [vp]),
     "moe_synth_fill_experts": (i32, [u64, i32, i32, i32, i32, i32, i32, f32, f32, vp, u64, vp]),
     "moe_synth_philox": (i32, [vp, vp, vp, i32, vp]),

@@ -28,6 +28,17 @@ moe_status hip_fail(hipError_t e, const char* what) {
   return fail(MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+struct KernelTimer {
+  std::vector<hipEvent_t> begin, end;
+  int kind = 0;
+};
+thread_local KernelTimer g_timer;
+
+hipError_t timer_mark(bool at_begin, int kind, int layer, hipStream_t s) {
+  if (layer < 0 || kind != g_timer.kind || layer >= static_cast<int>(g_timer.begin.size())) return hipSuccess;
+  return hipEventRecord(at_begin ? g_timer.begin[layer] : g_timer.end[layer], s);
+}
+
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 uint64_t blob_size(int H, int I, int G) { return 3ull * I * H / 2 + 12ull * I * H / G; }
@@ -107,9 +118,12 @@ bool use_grouped(const moe_layer_desc* d, int T) {
 }
 
 moe_status do_route(const moe_layer_desc* d, const moe_layer_weights* w, const void* x, int T, int32_t* idx,
-                    float* tw, float* gamma, float* logits, hipStream_t s) {
-  hipError_t e = moe::launch_router_logits(d->act_dtype, static_cast<const uint16_t*>(x), w->router_w,
-                                           w->router_bias, logits, T, d->hidden, d->n_experts, s);
+                    float* tw, float* gamma, float* logits, hipStream_t s, int layer = -1) {
+  hipError_t e = timer_mark(true, MOE_TIME_ROUTER, layer, s);
+  if (e == hipSuccess)
+    e = moe::launch_router_logits(d->act_dtype, static_cast<const uint16_t*>(x), w->router_w, w->router_bias, logits,
+                                  T, d->hidden, d->n_experts, s);
+  if (e == hipSuccess) e = timer_mark(false, MOE_TIME_ROUTER, layer, s);
   if (e != hipSuccess) return hip_fail(e, "router kernel launch");
   e = moe::launch_topk(logits, T, d->n_experts, d->top_k, idx, tw, gamma, s);
   if (e != hipSuccess) return hip_fail(e, "top-k kernel launch");
@@ -118,7 +132,7 @@ moe_status do_route(const moe_layer_desc* d, const moe_layer_weights* w, const v
 
 moe_status do_ffn(const moe_layer_desc* d, const moe_layer_weights* w, const void* x, int T, const int32_t* idx,
                   const float* tw, const float* gamma, float* y, float* r, void* x_next, void* ws, const Ws& L,
-                  hipStream_t s) {
+                  hipStream_t s, int layer = -1) {
   moe::FfnArgs a{};
   a.x = static_cast<const uint16_t*>(x);
   a.topk_idx = idx;
@@ -146,15 +160,23 @@ moe_status do_ffn(const moe_layer_desc* d, const moe_layer_weights* w, const voi
     e = moe::launch_permute(idx, T * d->top_k, d->n_experts, at<int32_t>(ws, L.off), at<int32_t>(ws, L.perm),
                             at<int32_t>(ws, L.inv), at<int32_t>(ws, L.active), at<int32_t>(ws, L.nact), s);
     if (e != hipSuccess) return hip_fail(e, "permute kernel launch");
-    e = moe::launch_gateup_grouped(d->act_dtype, a, s);
+    e = timer_mark(true, MOE_TIME_GATEUP, layer, s);
+    if (e == hipSuccess) e = moe::launch_gateup_grouped(d->act_dtype, a, s);
+    if (e == hipSuccess) e = timer_mark(false, MOE_TIME_GATEUP, layer, s);
     if (e != hipSuccess) return hip_fail(e, "grouped gate/up kernel launch");
-    e = moe::launch_down_grouped(a, s);
+    e = timer_mark(true, MOE_TIME_DOWN, layer, s);
+    if (e == hipSuccess) e = moe::launch_down_grouped(a, s);
+    if (e == hipSuccess) e = timer_mark(false, MOE_TIME_DOWN, layer, s);
     if (e != hipSuccess) return hip_fail(e, "grouped down kernel launch");
     inv = at<int32_t>(ws, L.inv);
   } else {
-    e = moe::launch_gateup_gemv(d->act_dtype, a, s);
+    e = timer_mark(true, MOE_TIME_GATEUP, layer, s);
+    if (e == hipSuccess) e = moe::launch_gateup_gemv(d->act_dtype, a, s);
+    if (e == hipSuccess) e = timer_mark(false, MOE_TIME_GATEUP, layer, s);
     if (e != hipSuccess) return hip_fail(e, "gate/up GEMV kernel launch");
-    e = moe::launch_down_gemv(a, s);
+    e = timer_mark(true, MOE_TIME_DOWN, layer, s);
+    if (e == hipSuccess) e = moe::launch_down_gemv(a, s);
+    if (e == hipSuccess) e = timer_mark(false, MOE_TIME_DOWN, layer, s);
     if (e != hipSuccess) return hip_fail(e, "down GEMV kernel launch");
   }
   e = moe::launch_combine(d->act_dtype, a.yrow, inv, tw, gamma, T, d->top_k, d->hidden, d->shared_inter > 0, y, r,
@@ -388,8 +410,8 @@ static moe_status stack_enqueue(const moe_layer_desc* d, const moe_layer_weights
     float* tw = w_all ? w_all + l * TK : at<float>(ws, L.w);
     float* gamma = gamma_all ? gamma_all + static_cast<size_t>(l) * T : at<float>(ws, L.gamma);
     float* y = y_all ? y_all + l * TH : nullptr;
-    if ((st = do_route(d, &layers[l], xl, T, idx, tw, gamma, at<float>(ws, L.logits), s))) return st;
-    if ((st = do_ffn(d, &layers[l], xl, T, idx, tw, gamma, y, r, x_buf, ws, L, s))) return st;
+    if ((st = do_route(d, &layers[l], xl, T, idx, tw, gamma, at<float>(ws, L.logits), s, l))) return st;
+    if ((st = do_ffn(d, &layers[l], xl, T, idx, tw, gamma, y, r, x_buf, ws, L, s, l))) return st;
   }
   return MOE_OK;
 }
@@ -437,6 +459,20 @@ moe_status moe_stack_graph_create(const moe_layer_desc* d, const moe_layer_weigh
   mg->graph = g;
   mg->exec = ex;
   *out = mg;
+  return ok();
+}
+
+moe_status moe_stack_set_kernel_events(void* const* begin, void* const* end, int32_t n_layers, int32_t kind) {
+  if (n_layers < 0 || (n_layers > 0 && (!begin || !end))) return fail(MOE_EINVAL, "bad event arrays");
+  if (kind < MOE_TIME_GATEUP || kind > MOE_TIME_ROUTER) return fail(MOE_EINVAL, "kind=%d is not a MOE_TIME_*", kind);
+  g_timer.begin.assign(n_layers, nullptr);
+  g_timer.end.assign(n_layers, nullptr);
+  for (int l = 0; l < n_layers; ++l) {
+    if (!begin[l] || !end[l]) return fail(MOE_EINVAL, "NULL event for layer %d", l);
+    g_timer.begin[l] = static_cast<hipEvent_t>(begin[l]);
+    g_timer.end[l] = static_cast<hipEvent_t>(end[l]);
+  }
+  g_timer.kind = kind;
   return ok();
 }
 

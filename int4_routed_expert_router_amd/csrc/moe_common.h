@@ -31,11 +31,40 @@ __device__ __forceinline__ uint16_t f32_to_act(float v) {
   }
 }
 
-// ---- wave reductions (fixed butterfly order: every lane ends with the same bits)
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+// ---- wave all-reductions without LDS round trips ---------------------------
+// DPP within rows of 16 lanes (pairs, quads, 8-lane halves, rows), then the
+// gfx950 row-swap permutes across rows.  At every step a lane combines its
+// value with exactly one partner that holds the same pair of operands, and
+// the operation is commutative, so all 64 lanes end with identical bits and
+// the order of the reduction is fixed.
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), kCtrl, 0xF, 0xF, false));
+}
+template <class Op>
+__device__ __forceinline__ uint32_t wave_allreduce_u32(uint32_t v, Op op) {
+  v = op(v, dpp_u32<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = op(v, dpp_u32<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = op(v, dpp_u32<0x141>(v));  // row_half_mirror
+  v = op(v, dpp_u32<0x140>(v));  // row_mirror
+  const auto a = __builtin_amdgcn_permlane16_swap(static_cast<int>(v), static_cast<int>(v), false, false);
+  v = op(static_cast<uint32_t>(a[0]), static_cast<uint32_t>(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(static_cast<int>(v), static_cast<int>(v), false, false);
+  v = op(static_cast<uint32_t>(b[0]), static_cast<uint32_t>(b[1]));
   return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  return __uint_as_float(wave_allreduce_u32(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+  }));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  return __uint_as_float(wave_allreduce_u32(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+  }));
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  return wave_allreduce_u32(v, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
 }
 
 // ---- int4 nibble words -------------------------------------------------------

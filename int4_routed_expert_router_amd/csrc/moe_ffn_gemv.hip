@@ -191,54 +191,94 @@ __global__ __launch_bounds__(256) void k_down_gemv(FfnArgs a) {
   }
 }
 
-// Block sum over 256 threads in a fixed order.
-__device__ __forceinline__ float block_sum_256(float v, float* lds4) {
+// Block sum over blockDim threads (multiple of 64, <= 1024) in a fixed order.
+__device__ __forceinline__ float block_sum(float v, float* lds16) {
   v = wave_sum(v);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) lds4[wave] = v;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  if (lane == 0) lds16[wave] = v;
   __syncthreads();
-  const float s = ((lds4[0] + lds4[1]) + lds4[2]) + lds4[3];
+  float s = 0.0f;
+  for (int w = 0; w < nw; ++w) s += lds16[w];
   __syncthreads();
   return s;
 }
 
+// One workgroup of 512 threads per token; each thread owns float4 columns and
+// issues the loads of all K+1 source rows before the FMAs, so a token costs
+// one memory round trip per 2048 columns.  Sum order: rank 0..K-1, shared last.
 template <int ACT, bool EPI>
-__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ yrow, const int32_t* __restrict__ inv,
+__global__ __launch_bounds__(512) void k_combine(const float* __restrict__ yrow, const int32_t* __restrict__ inv,
                                                  const float* __restrict__ w, const float* __restrict__ gamma,
                                                  int T, int K, int H, int has_shared, float* __restrict__ y,
                                                  float* __restrict__ r, uint16_t* __restrict__ x_next) {
-  __shared__ float lds4[4];
-  const int t = blockIdx.x;
-  constexpr int kPer = kMaxH / 256;
-  float rr[kPer];
+  __shared__ float lds16[16];
+  __shared__ int src[kMaxTopK + 1];
+  __shared__ float wt[kMaxTopK + 1];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  if (tid < K) {
+    src[tid] = inv ? inv[t * K + tid] : t * K + tid;
+    wt[tid] = w[t * K + tid];
+  }
+  if (tid == K && has_shared) {
+    src[K] = T * K + t;
+    wt[K] = gamma[t];
+  }
+  __syncthreads();
+  const int ns = K + (has_shared ? 1 : 0);
+  const int H4 = H / 4;
+  constexpr int kPer = kMaxH / 4 / 512;
+  constexpr int kB = 16;
+  float4 rr[kPer];
   float ss = 0.0f;
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
-    const int n = threadIdx.x + 256 * u;
-    rr[u] = 0.0f;
-    if (n < H) {
-      float acc = 0.0f;
-      for (int k = 0; k < K; ++k) {
-        const int row = inv ? inv[t * K + k] : t * K + k;
-        acc = fmaf(w[t * K + k], yrow[static_cast<size_t>(row) * H + n], acc);
+    const int c4 = tid + 512 * u;
+    rr[u] = make_float4(0, 0, 0, 0);
+    if (c4 < H4) {
+      float4 acc = make_float4(0, 0, 0, 0);
+      for (int k0 = 0; k0 < ns; k0 += kB) {
+        float4 v[kB];
+#pragma unroll
+        for (int b = 0; b < kB; ++b)
+          if (k0 + b < ns) v[b] = reinterpret_cast<const float4*>(yrow + static_cast<size_t>(src[k0 + b]) * H)[c4];
+#pragma unroll
+        for (int b = 0; b < kB; ++b) {
+          if (k0 + b < ns) {
+            const float wk = wt[k0 + b];
+            acc.x = fmaf(wk, v[b].x, acc.x);
+            acc.y = fmaf(wk, v[b].y, acc.y);
+            acc.z = fmaf(wk, v[b].z, acc.z);
+            acc.w = fmaf(wk, v[b].w, acc.w);
+          }
+        }
       }
-      if (has_shared) acc = fmaf(gamma[t], yrow[static_cast<size_t>(T * K + t) * H + n], acc);
-      if (y) y[static_cast<size_t>(t) * H + n] = acc;
+      if (y) reinterpret_cast<float4*>(y + static_cast<size_t>(t) * H)[c4] = acc;
       if constexpr (EPI) {
-        const float v = r[static_cast<size_t>(t) * H + n] + acc;
-        r[static_cast<size_t>(t) * H + n] = v;
-        rr[u] = v;
-        ss = fmaf(v, v, ss);
+        float4 rv = reinterpret_cast<float4*>(r + static_cast<size_t>(t) * H)[c4];
+        rv.x += acc.x;
+        rv.y += acc.y;
+        rv.z += acc.z;
+        rv.w += acc.w;
+        reinterpret_cast<float4*>(r + static_cast<size_t>(t) * H)[c4] = rv;
+        rr[u] = rv;
+        ss = fmaf(rv.x, rv.x, ss);
+        ss = fmaf(rv.y, rv.y, ss);
+        ss = fmaf(rv.z, rv.z, ss);
+        ss = fmaf(rv.w, rv.w, ss);
       }
     }
   }
   if constexpr (EPI) {
-    const float tot = block_sum_256(ss, lds4);
+    const float tot = block_sum(ss, lds16);
     const float inv_rms = 1.0f / sqrtf(tot / static_cast<float>(H) + 1e-6f);
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
-      const int n = threadIdx.x + 256 * u;
-      if (n < H) x_next[static_cast<size_t>(t) * H + n] = f32_to_act<ACT>(rr[u] * inv_rms);
+      const int c4 = tid + 512 * u;
+      if (c4 < H4) {
+        const uint32_t a0 = f32_to_act<ACT>(rr[u].x * inv_rms), a1 = f32_to_act<ACT>(rr[u].y * inv_rms);
+        const uint32_t a2 = f32_to_act<ACT>(rr[u].z * inv_rms), a3 = f32_to_act<ACT>(rr[u].w * inv_rms);
+        reinterpret_cast<uint2*>(x_next + static_cast<size_t>(t) * H)[c4] = make_uint2(a0 | (a1 << 16), a2 | (a3 << 16));
+      }
     }
   }
 }
@@ -246,7 +286,7 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ yrow,
 template <int ACT>
 __global__ __launch_bounds__(256) void k_epilogue(const float* __restrict__ y, float* __restrict__ r,
                                                   uint16_t* __restrict__ x_next, int H) {
-  __shared__ float lds4[4];
+  __shared__ float lds16[16];
   const int t = blockIdx.x;
   constexpr int kPer = kMaxH / 256;
   float rr[kPer];
@@ -262,7 +302,7 @@ __global__ __launch_bounds__(256) void k_epilogue(const float* __restrict__ y, f
       ss = fmaf(v, v, ss);
     }
   }
-  const float tot = block_sum_256(ss, lds4);
+  const float tot = block_sum(ss, lds16);
   const float inv_rms = 1.0f / sqrtf(tot / static_cast<float>(H) + 1e-6f);
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
@@ -290,13 +330,13 @@ hipError_t launch_combine(int act, const float* yrow, const int32_t* inv, const 
                           int K, int H, bool has_shared, float* y, float* r, uint16_t* x_next, hipStream_t s) {
   const int hs = has_shared ? 1 : 0;
   if (r == nullptr) {
-    hipLaunchKernelGGL((k_combine<2, false>), dim3(T), dim3(256), 0, s, yrow, inv, w, gamma, T, K, H, hs, y, r,
+    hipLaunchKernelGGL((k_combine<2, false>), dim3(T), dim3(512), 0, s, yrow, inv, w, gamma, T, K, H, hs, y, r,
                        x_next);
   } else if (act == 2) {
-    hipLaunchKernelGGL((k_combine<2, true>), dim3(T), dim3(256), 0, s, yrow, inv, w, gamma, T, K, H, hs, y, r,
+    hipLaunchKernelGGL((k_combine<2, true>), dim3(T), dim3(512), 0, s, yrow, inv, w, gamma, T, K, H, hs, y, r,
                        x_next);
   } else {
-    hipLaunchKernelGGL((k_combine<1, true>), dim3(T), dim3(256), 0, s, yrow, inv, w, gamma, T, K, H, hs, y, r,
+    hipLaunchKernelGGL((k_combine<1, true>), dim3(T), dim3(512), 0, s, yrow, inv, w, gamma, T, K, H, hs, y, r,
                        x_next);
   }
   return hipGetLastError();

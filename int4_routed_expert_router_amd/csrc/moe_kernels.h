@@ -9,6 +9,7 @@ constexpr int kMaxH = 8192;        // hidden size limit (router keeps a row in r
 constexpr int kMaxInter = 4096;    // intermediate size limit (down GEMV stages h in LDS)
 constexpr int kMaxExperts = 1024;  // top-k holds E/64 logits per lane; bucketing uses one workgroup
 constexpr int kMaxTopK = 64;       // one selected expert per lane
+constexpr int kRouterMfmaMinTokens = 16;  // router GEMM on the matrix cores from this batch size
 
 // Routed rows of a batch: row j < T*K is (token j/K, rank j%K) in slot order,
 // or the r-th row of the expert-sorted order in the grouped family; rows

@@ -57,8 +57,10 @@ __global__ __launch_bounds__(64) void k_router_logits(const uint16_t* __restrict
 }
 
 // One wave per token: K rounds of a wave-wide arg-max over E/64 values per
-// lane (lane l holds experts l, l+64, ...).  The comparator prefers the larger
-// logit, then the lower index, so ties resolve to the lower expert index.
+// lane (lane l holds experts l, l+64, ...).  Each round takes the wave maximum
+// of the lanes' best remaining logits, then the lowest expert index among the
+// lanes holding that maximum, so ties resolve to the lower expert index.  Both
+// reductions run on DPP/row-swap permutes (no LDS round trips).
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int T, int E, int K,
                                               int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
                                               float* __restrict__ gamma) {
@@ -82,32 +84,25 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
   float my_v = 0.0f, v0 = 0.0f;
   int my_i = 0;
   for (int k = 0; k < K; ++k) {
-    float bv = 0.0f;
-    int bi = 0x7FFFFFFF;
+    float bv = -INFINITY;
+    int bj = -1;
 #pragma unroll
     for (int j = 0; j < kJ; ++j) {
       // j ascending = index ascending, so a strict '>' keeps the lower index on ties
-      if (((avail >> j) & 1u) && (bi == 0x7FFFFFFF || v[j] > bv)) {
+      if (((avail >> j) & 1u) && (bj < 0 || v[j] > bv)) {
         bv = v[j];
-        bi = lane + 64 * j;
+        bj = j;
       }
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, kWave);
-      const int oi = __shfl_xor(bi, off, kWave);
-      const bool take = (oi != 0x7FFFFFFF) && (bi == 0x7FFFFFFF || ov > bv || (ov == bv && oi < bi));
-      if (take) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if (k == 0) v0 = bv;
+    const float m = wave_max(bv);
+    const uint32_t key = (bj >= 0 && bv == m) ? static_cast<uint32_t>(lane + 64 * bj) : 0xFFFFFFFFu;
+    const int e = static_cast<int>(wave_min_u32(key));
+    if (k == 0) v0 = m;
     if (lane == k) {
-      my_v = bv;
-      my_i = bi;
+      my_v = m;
+      my_i = e;
     }
-    if ((bi & 63) == lane) avail &= ~(1u << (bi >> 6));
+    if ((e & 63) == lane) avail &= ~(1u << (e >> 6));
   }
   const float ex = (lane < K) ? expf(my_v - v0) : 0.0f;
   const float s = wave_sum(ex);
@@ -141,10 +136,14 @@ __device__ __forceinline__ int block_incl_scan_1024(int v, int* lds16, int& tota
 
 // Stable counting sort of the n = T*K routed rows by expert, one 1024-thread
 // workgroup: histogram (LDS integer atomics), exclusive prefix sum over the
-// experts, then a scatter in which each wave computes the rank of its rows
-// among equal experts with ballots and the waves commit in order, so rows of
-// one expert keep their (t, k) order.  Also lists the active experts in
-// ascending order and their count.
+// experts, then a scatter.  The rank of a row among earlier rows of the same
+// expert is: rows of earlier 1024-row chunks (a running count), plus rows of
+// earlier waves of this chunk (per-wave counts in LDS), plus earlier lanes of
+// its own wave (ballot of the lanes holding the same expert).  Rows of one
+// expert therefore keep their (t, k) order.  Also lists the active experts,
+// most tokens first (the work order of the grouped kernels; the order among
+// experts with equal counts is unspecified and affects scheduling only), and
+// their count.
 __global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ topk_idx, int n, int E,
                                                   int32_t* __restrict__ expert_off, int32_t* __restrict__ perm,
                                                   int32_t* __restrict__ inv, int32_t* __restrict__ active,
@@ -152,6 +151,8 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ to
   __shared__ int cnt[kMaxExperts];
   __shared__ int start[kMaxExperts];
   __shared__ int run[kMaxExperts];
+  __shared__ unsigned short wcnt[16][kMaxExperts];
+  __shared__ int cbin[1024];
   __shared__ int scan_tmp[16];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -159,6 +160,7 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ to
     cnt[tid] = 0;
     run[tid] = 0;
   }
+  cbin[tid] = 0;
   __syncthreads();
   for (int i = tid; i < n; i += 1024) atomicAdd(&cnt[topk_idx[i]], 1);
   __syncthreads();
@@ -167,16 +169,26 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ to
   const int incl = block_incl_scan_1024(c, scan_tmp, total);
   int n_act_total = 0;
   const int a_incl = block_incl_scan_1024((tid < E && c > 0) ? 1 : 0, scan_tmp, n_act_total);
+  (void)a_incl;
   if (tid < E) {
     start[tid] = incl - c;
     expert_off[tid] = incl - c;
-    if (c > 0) active[a_incl - 1] = tid;
   }
   if (tid == 0) {
     expert_off[E] = total;
     n_active[0] = n_act_total;
   }
+  // active experts by descending count: bucket by count (clamped), scan the
+  // buckets from the largest count down, place with LDS atomics
+  const int ckey = min(c, 1023);
+  if (tid < E && c > 0) atomicAdd(&cbin[ckey], 1);
   __syncthreads();
+  const int hv = cbin[1023 - tid];
+  int dummy = 0;
+  const int hincl = block_incl_scan_1024(hv, scan_tmp, dummy);
+  cbin[1023 - tid] = hincl - hv;
+  __syncthreads();
+  if (tid < E && c > 0) active[atomicAdd(&cbin[ckey], 1)] = tid;
   for (int base = 0; base < n; base += 1024) {
     const int i = base + tid;
     const bool valid = i < n;
@@ -191,16 +203,82 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ to
       todo &= ~m;
     }
     const int rank = __popcll(peers & ((1ull << lane) - 1ull));
-    const bool last_peer = valid && (63 - __clzll(static_cast<long long>(peers))) == lane;
-    for (int w = 0; w < 16; ++w) {
-      if (wave == w && valid) {
-        const int pos = start[e] + run[e] + rank;
-        perm[pos] = i;
-        if (inv != nullptr) inv[i] = pos;
+    const bool first_peer = valid && rank == 0;
+    for (int k = tid; k < 16 * E; k += 1024) wcnt[k / E][k % E] = 0;
+    __syncthreads();
+    if (first_peer) wcnt[wave][e] = static_cast<unsigned short>(__popcll(peers));
+    __syncthreads();
+    if (valid) {
+      int before = 0;
+      for (int w = 0; w < wave; ++w) before += wcnt[w][e];
+      const int pos = start[e] + run[e] + before + rank;
+      perm[pos] = i;
+      if (inv != nullptr) inv[i] = pos;
+    }
+    __syncthreads();
+    if (first_peer) atomicAdd(&run[e], __popcll(peers));
+    __syncthreads();
+  }
+}
+
+// Router logits on the matrix cores for batches of 16+ tokens.  One workgroup
+// = 16 router rows x 16 tokens; its waves split H into 32-column steps and
+// their fp32 partial tiles are summed in a fixed order.  The fp16 router
+// weights enter bf16 MFMAs as an exact hi + lo pair (fp16 has 11 significant
+// bits); with fp16 activations they enter as they are.
+template <int ACT>
+__global__ __launch_bounds__(1024) void k_router_mfma(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+                                                      const float* __restrict__ bias, float* __restrict__ logits,
+                                                      int T, int H, int E) {
+  typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+  typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  __shared__ float part[16][16][17];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int n = lane & 15, kb = lane >> 4;
+  const int row = blockIdx.x * 16 + n;      // router row this lane loads (B operand column)
+  const int tok = blockIdx.y * 16 + n;      // token this lane loads (A operand row)
+  const int nsteps = H / 32;
+  f32x4_t acc = {0, 0, 0, 0};
+  for (int st = wave; st < nsteps; st += nw) {
+    const int col = 32 * st + 8 * kb;
+    const uint4 av = (tok < T) ? *reinterpret_cast<const uint4*>(x + static_cast<size_t>(tok) * H + col)
+                               : make_uint4(0, 0, 0, 0);
+    const uint4 bv = (row <= E) ? *reinterpret_cast<const uint4*>(wr + static_cast<size_t>(row) * H + col)
+                                : make_uint4(0, 0, 0, 0);
+    if constexpr (ACT == 2) {
+      const uint32_t bw[4] = {bv.x, bv.y, bv.z, bv.w};
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float f0 = f16_bits_to_f32(bw[i] & 0xFFFFu), f1 = f16_bits_to_f32(bw[i] >> 16);
+        const uint32_t h0 = __float_as_uint(f0) & 0xFFFF0000u, h1 = __float_as_uint(f1) & 0xFFFF0000u;
+        const uint32_t l0 = f32_to_act<2>(f0 - __uint_as_float(h0)), l1 = f32_to_act<2>(f1 - __uint_as_float(h1));
+        hi[i] = (h0 >> 16) | h1;
+        lo[i] = l0 | (l1 << 16);
       }
-      __syncthreads();
-      if (wave == w && last_peer) run[e] += __popcll(peers);
-      __syncthreads();
+      const uint4 bh = make_uint4(hi[0], hi[1], hi[2], hi[3]), bl = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, bh),
+                                                    acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, bl),
+                                                    acc, 0, 0, 0);
+    } else {
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, av), __builtin_bit_cast(f16x8_t, bv),
+                                                   acc, 0, 0, 0);
+    }
+  }
+  // lane holds tokens 4kb..4kb+3 (tile rows) of router row n (tile column)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) part[wave][4 * kb + i][n] = acc[i];
+  __syncthreads();
+  if (threadIdx.x < 256) {
+    const int m = threadIdx.x >> 4, c = threadIdx.x & 15;
+    const int t = blockIdx.y * 16 + m, r = blockIdx.x * 16 + c;
+    float sum = 0.0f;
+    for (int w = 0; w < nw; ++w) sum += part[w][m][c];
+    if (t < T && r <= E) {
+      if (r < E && bias != nullptr) sum += bias[r];
+      logits[static_cast<size_t>(t) * (E + 1) + r] = sum;
     }
   }
 }
@@ -208,9 +286,16 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ to
 template <int ACT>
 static hipError_t launch_router_t(const uint16_t* x, const uint16_t* wr, const float* bias, float* logits, int T,
                                   int H, int E, hipStream_t s) {
-  const int tpb = (T <= 8) ? T : 8;
-  dim3 grid(E + 1, (T + tpb - 1) / tpb);
-  hipLaunchKernelGGL(k_router_logits<ACT>, grid, dim3(64), 0, s, x, wr, bias, logits, T, H, E, tpb);
+  if (T >= kRouterMfmaMinTokens) {
+    const int steps = H / 32;
+    const int nw = steps < 16 ? steps : 16;
+    dim3 grid((E + 1 + 15) / 16, (T + 15) / 16);
+    hipLaunchKernelGGL(k_router_mfma<ACT>, grid, dim3(64 * nw), 0, s, x, wr, bias, logits, T, H, E);
+  } else {
+    const int tpb = (T <= 8) ? T : 8;
+    dim3 grid(E + 1, (T + tpb - 1) / tpb);
+    hipLaunchKernelGGL(k_router_logits<ACT>, grid, dim3(64), 0, s, x, wr, bias, logits, T, H, E, tpb);
+  }
   return hipGetLastError();
 }
 
