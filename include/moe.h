@@ -59,7 +59,9 @@ enum { MOE_F16 = 1, MOE_BF16 = 2 };
 
 /* Kernel family for the expert FFN. AUTO picks the batched grouped-GEMM
  * (matrix-core) family when the batch has more than MOE_GEMV_MAX_ROWS
- * routed rows (T*K), the per-row GEMV family otherwise. */
+ * routed rows (T*K) and the shape fits it (hidden <= 2048, inter and
+ * shared_inter <= 512), the per-row GEMV family otherwise.  Asking for
+ * GROUPED with a shape beyond those limits is MOE_ESHAPE. */
 enum { MOE_PATH_AUTO = 0, MOE_PATH_GEMV = 1, MOE_PATH_GROUPED = 2 };
 #define MOE_GEMV_MAX_ROWS 32
 

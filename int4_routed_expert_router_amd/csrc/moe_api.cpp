@@ -43,6 +43,8 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 uint64_t blob_size(int H, int I, int G) { return 3ull * I * H / 2 + 12ull * I * H / G; }
 
+bool grouped_fits(const moe_layer_desc* d);
+
 moe_status check_desc(const moe_layer_desc* d) {
   if (!d) return fail(MOE_EINVAL, "desc is NULL");
   const int H = d->hidden, E = d->n_experts, K = d->top_k, I = d->inter, Is = d->shared_inter, G = d->group_size;
@@ -56,6 +58,9 @@ moe_status check_desc(const moe_layer_desc* d) {
   if (H % G || I % G || (Is && Is % G)) return fail(MOE_ESHAPE, "group_size=%d must divide hidden, inter and shared_inter", G);
   if (d->act_dtype != MOE_F16 && d->act_dtype != MOE_BF16) return fail(MOE_EINVAL, "act_dtype=%d is not MOE_F16/MOE_BF16", d->act_dtype);
   if (d->path < MOE_PATH_AUTO || d->path > MOE_PATH_GROUPED) return fail(MOE_EINVAL, "path=%d is not a MOE_PATH_*", d->path);
+  if (d->path == MOE_PATH_GROUPED && !grouped_fits(d))
+    return fail(MOE_ESHAPE, "the grouped family needs hidden <= %d and inter, shared_inter <= %d", moe::kGroupedMaxH,
+                moe::kGroupedMaxInter);
   return MOE_OK;
 }
 
@@ -77,8 +82,10 @@ moe_status check_weights(const moe_layer_desc* d, const moe_layer_weights* w) {
 size_t al(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct Ws {
-  size_t logits, idx, w, gamma, off, perm, inv, active, nact, h, yrow, total;
+  size_t logits, idx, w, gamma, off, perm, inv, active, nact, tok, work_gu, work_d, nwork, h, yrow, total;
 };
+
+int down_blocks(int H) { return (H + moe::kDownBlockRows - 1) / moe::kDownBlockRows; }
 
 Ws layout(const moe_layer_desc* d, int T) {
   const size_t E = d->n_experts, K = d->top_k, H = d->hidden;
@@ -95,6 +102,13 @@ Ws layout(const moe_layer_desc* d, int T) {
   s.inv = o; o += al(T * K * 4);
   s.active = o; o += al((E + 1) * 4);
   s.nact = o; o += al(16);
+  s.tok = o; o += al(T * K * 4);
+  const int nbd = down_blocks(d->hidden);
+  s.work_gu = o;
+  o += al(16ull * moe::work_upper(d->inter / 64, d->shared_inter / 64, T, d->top_k, d->n_experts));
+  s.work_d = o;
+  o += al(16ull * moe::work_upper(nbd, d->shared_inter ? nbd : 0, T, d->top_k, d->n_experts));
+  s.nwork = o; o += al(16);
   s.h = o; o += al(rows * hstride * 4);
   s.yrow = o; o += al(rows * H * 4);
   s.total = o;
@@ -111,10 +125,15 @@ moe_status check_ws(const moe_layer_desc* d, int T, void* ws, size_t ws_bytes, W
   return MOE_OK;
 }
 
+bool grouped_fits(const moe_layer_desc* d) {
+  return d->hidden <= moe::kGroupedMaxH && d->inter <= moe::kGroupedMaxInter &&
+         d->shared_inter <= moe::kGroupedMaxInter;
+}
+
 bool use_grouped(const moe_layer_desc* d, int T) {
   if (d->path == MOE_PATH_GEMV) return false;
   if (d->path == MOE_PATH_GROUPED) return true;
-  return static_cast<long long>(T) * d->top_k > MOE_GEMV_MAX_ROWS;
+  return static_cast<long long>(T) * d->top_k > MOE_GEMV_MAX_ROWS && grouped_fits(d);
 }
 
 moe_status do_route(const moe_layer_desc* d, const moe_layer_weights* w, const void* x, int T, int32_t* idx,
@@ -157,8 +176,23 @@ moe_status do_ffn(const moe_layer_desc* d, const moe_layer_weights* w, const voi
     a.expert_off = at<int32_t>(ws, L.off);
     a.active = at<int32_t>(ws, L.active);
     a.n_active = at<int32_t>(ws, L.nact);
+    a.tok_sorted = at<int32_t>(ws, L.tok);
+    a.work_gu = at<int4>(ws, L.work_gu);
+    a.work_d = at<int4>(ws, L.work_d);
+    a.n_work = at<int32_t>(ws, L.nwork);
+    moe::WorkLists wl{};
+    wl.tok_sorted = at<int32_t>(ws, L.tok);
+    wl.work_gu = at<int4>(ws, L.work_gu);
+    wl.work_d = at<int4>(ws, L.work_d);
+    wl.n_work = at<int32_t>(ws, L.nwork);
+    wl.T = T;
+    wl.K = d->top_k;
+    wl.nb_gu = d->inter / 64;
+    wl.nb_gu_s = d->shared_inter / 64;
+    wl.nb_d = down_blocks(d->hidden);
+    wl.nb_d_s = d->shared_inter ? wl.nb_d : 0;
     e = moe::launch_permute(idx, T * d->top_k, d->n_experts, at<int32_t>(ws, L.off), at<int32_t>(ws, L.perm),
-                            at<int32_t>(ws, L.inv), at<int32_t>(ws, L.active), at<int32_t>(ws, L.nact), s);
+                            at<int32_t>(ws, L.inv), at<int32_t>(ws, L.active), at<int32_t>(ws, L.nact), &wl, s);
     if (e != hipSuccess) return hip_fail(e, "permute kernel launch");
     e = timer_mark(true, MOE_TIME_GATEUP, layer, s);
     if (e == hipSuccess) e = moe::launch_gateup_grouped(d->act_dtype, a, s);
@@ -327,7 +361,7 @@ moe_status moe_permute(const moe_layer_desc* d, const int32_t* topk_idx, int32_t
   Ws L;
   if ((st = check_ws(d, T, ws, ws_bytes, L))) return st;
   hipError_t e = moe::launch_permute(topk_idx, T * d->top_k, d->n_experts, expert_off, perm, inv_or_null,
-                                     at<int32_t>(ws, L.active), at<int32_t>(ws, L.nact),
+                                     at<int32_t>(ws, L.active), at<int32_t>(ws, L.nact), nullptr,
                                      reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "permute kernel launch");
   return ok();

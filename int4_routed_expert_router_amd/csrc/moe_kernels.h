@@ -26,18 +26,51 @@ struct FfnArgs {
   // grouped family
   const int32_t* perm;        // [T*K] sorted row -> slot t*K+k
   const int32_t* expert_off;  // [E+1]
-  const int32_t* active;      // active experts ascending
+  const int32_t* active;      // active experts, most tokens first
   const int32_t* n_active;    // [1]
+  const int32_t* tok_sorted;  // [T*K] token of each sorted row
+  const int4* work_gu;        // gate/up work items (see WorkLists)
+  const int4* work_d;         // down work items
+  const int32_t* n_work;      // [2] number of gate/up and down work items
   int T, H, K, I, Is, G, E;
   int hstride;                // max(I, Is)
 };
+
+// Work lists of the grouped kernels, built by the bucketing kernel.  A unit
+// is (expert, block of output rows); it splits into sub-items of up to 16
+// tokens.  Item = int4 {row0, mc | block << 8, expert (-1 = shared), 0}: rows
+// row0..row0+mc-1 of the row space (sorted routed rows, then T*K + t for the
+// shared expert).  Units run longest first (shared, then experts by
+// descending token count).  When the blocks per unit are a multiple of 8,
+// item index = 8 * position + block % 8 with the sub-items of a unit at
+// consecutive positions, so a persistent grid whose size is a multiple of 8
+// runs them on one XCD.
+struct WorkLists {
+  int32_t* tok_sorted;
+  int4* work_gu;
+  int4* work_d;
+  int32_t* n_work;
+  int T, K;
+  int nb_gu, nb_gu_s;   // gate/up blocks (64 rows of I) per routed / shared unit
+  int nb_d, nb_d_s;     // down blocks (256 rows of H) per routed / shared unit
+};
+constexpr int kSubTokens = 16;
+constexpr int kDownBlockRows = 256;
+// limits of the grouped family (larger shapes use the GEMV family)
+constexpr int kGroupedMaxH = 2048;
+constexpr int kGroupedMaxInter = 512;
+inline int work_upper(int nb, int nb_s, int T, int K, int E) {
+  const int rows = T * K;
+  const int n_act = rows < E ? rows : E;
+  return nb * ((rows + kSubTokens - 1) / kSubTokens + n_act) + nb_s * ((T + kSubTokens - 1) / kSubTokens);
+}
 
 hipError_t launch_router_logits(int act, const uint16_t* x, const uint16_t* wr, const float* bias, float* logits,
                                 int T, int H, int E, hipStream_t s);
 hipError_t launch_topk(const float* logits, int T, int E, int K, int32_t* idx, float* w, float* gamma,
                        hipStream_t s);
 hipError_t launch_permute(const int32_t* idx, int n, int E, int32_t* off, int32_t* perm, int32_t* inv,
-                          int32_t* active, int32_t* n_active, hipStream_t s);
+                          int32_t* active, int32_t* n_active, const WorkLists* wl, hipStream_t s);
 
 hipError_t launch_gateup_gemv(int act, const FfnArgs& a, hipStream_t s);
 hipError_t launch_down_gemv(const FfnArgs& a, hipStream_t s);
