@@ -177,9 +177,11 @@ def logit_error_bound(x_row, router_w, bias, e: int) -> float:
     """Bound on |fp32 logit - exact logit| for a lane-blocked fp32 GEMV.
 
     Products of a 16-bit float activation with an fp16 weight are exact in
-    binary32; a summation tree of depth d adds at most d*u*sum|terms|
-    (u = 2**-24).  A depth of 64 covers any blocking of H <= 2**32 terms
-    whose sequential runs are at most 32 long, plus the bias add.
+    binary32; a summation of depth d (the longest chain of fp32 additions
+    any term passes through) adds at most d*u*sum|terms| (u = 2**-24).
+    Depth 64 covers sequential runs of up to 32 terms followed by up to 31
+    further additions (partial sums and the bias), which bounds every
+    lane- or wave-blocked order of H <= 2048 terms used by the kernels.
     """
     terms = np.abs(np.asarray(x_row, np.float64) * np.asarray(router_w, np.float64)[e])
     extra = 0.0 if bias is None else abs(float(bias[e]))
