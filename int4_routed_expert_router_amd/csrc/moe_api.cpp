@@ -82,10 +82,8 @@ moe_status check_weights(const moe_layer_desc* d, const moe_layer_weights* w) {
 size_t al(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct Ws {
-  size_t logits, idx, w, gamma, off, perm, inv, active, nact, tok, work_gu, work_d, nwork, h, yrow, total;
+  size_t logits, idx, w, gamma, off, perm, inv, units, nunits, h, hsum, yrow, total;
 };
-
-int down_blocks(int H) { return (H + moe::kDownBlockRows - 1) / moe::kDownBlockRows; }
 
 Ws layout(const moe_layer_desc* d, int T) {
   const size_t E = d->n_experts, K = d->top_k, H = d->hidden;
@@ -100,16 +98,10 @@ Ws layout(const moe_layer_desc* d, int T) {
   s.off = o; o += al((E + 1) * 4);
   s.perm = o; o += al(T * K * 4);
   s.inv = o; o += al(T * K * 4);
-  s.active = o; o += al((E + 1) * 4);
-  s.nact = o; o += al(16);
-  s.tok = o; o += al(T * K * 4);
-  const int nbd = down_blocks(d->hidden);
-  s.work_gu = o;
-  o += al(16ull * moe::work_upper(d->inter / 64, d->shared_inter / 64, T, d->top_k, d->n_experts));
-  s.work_d = o;
-  o += al(16ull * moe::work_upper(nbd, d->shared_inter ? nbd : 0, T, d->top_k, d->n_experts));
-  s.nwork = o; o += al(16);
+  s.units = o; o += al(4ull * moe::kUnitInts * moe::max_units(T, d->top_k, d->n_experts, d->shared_inter > 0));
+  s.nunits = o; o += al(16);
   s.h = o; o += al(rows * hstride * 4);
+  s.hsum = o; o += al(rows * (hstride / 16) * 4);
   s.yrow = o; o += al(rows * H * 4);
   s.total = o;
   return s;
@@ -172,27 +164,17 @@ moe_status do_ffn(const moe_layer_desc* d, const moe_layer_weights* w, const voi
   const int32_t* inv = nullptr;
   hipError_t e;
   if (use_grouped(d, T)) {
-    a.perm = at<int32_t>(ws, L.perm);
-    a.expert_off = at<int32_t>(ws, L.off);
-    a.active = at<int32_t>(ws, L.active);
-    a.n_active = at<int32_t>(ws, L.nact);
-    a.tok_sorted = at<int32_t>(ws, L.tok);
-    a.work_gu = at<int4>(ws, L.work_gu);
-    a.work_d = at<int4>(ws, L.work_d);
-    a.n_work = at<int32_t>(ws, L.nwork);
-    moe::WorkLists wl{};
-    wl.tok_sorted = at<int32_t>(ws, L.tok);
-    wl.work_gu = at<int4>(ws, L.work_gu);
-    wl.work_d = at<int4>(ws, L.work_d);
-    wl.n_work = at<int32_t>(ws, L.nwork);
-    wl.T = T;
-    wl.K = d->top_k;
-    wl.nb_gu = d->inter / 64;
-    wl.nb_gu_s = d->shared_inter / 64;
-    wl.nb_d = down_blocks(d->hidden);
-    wl.nb_d_s = d->shared_inter ? wl.nb_d : 0;
+    a.units = at<int32_t>(ws, L.units);
+    a.n_units = at<int32_t>(ws, L.nunits);
+    a.hsum = at<float>(ws, L.hsum);
+    moe::UnitPlan plan{};
+    plan.units = at<int32_t>(ws, L.units);
+    plan.n_units = at<int32_t>(ws, L.nunits);
+    plan.T = T;
+    plan.K = d->top_k;
+    plan.shared = d->shared_inter > 0 ? 1 : 0;
     e = moe::launch_permute(idx, T * d->top_k, d->n_experts, at<int32_t>(ws, L.off), at<int32_t>(ws, L.perm),
-                            at<int32_t>(ws, L.inv), at<int32_t>(ws, L.active), at<int32_t>(ws, L.nact), &wl, s);
+                            at<int32_t>(ws, L.inv), &plan, s);
     if (e != hipSuccess) return hip_fail(e, "permute kernel launch");
     e = timer_mark(true, MOE_TIME_GATEUP, layer, s);
     if (e == hipSuccess) e = moe::launch_gateup_grouped(d->act_dtype, a, s);
@@ -360,8 +342,7 @@ moe_status moe_permute(const moe_layer_desc* d, const int32_t* topk_idx, int32_t
   if (!topk_idx || !expert_off || !perm) return fail(MOE_EINVAL, "topk_idx, expert_off and perm are required");
   Ws L;
   if ((st = check_ws(d, T, ws, ws_bytes, L))) return st;
-  hipError_t e = moe::launch_permute(topk_idx, T * d->top_k, d->n_experts, expert_off, perm, inv_or_null,
-                                     at<int32_t>(ws, L.active), at<int32_t>(ws, L.nact), nullptr,
+  hipError_t e = moe::launch_permute(topk_idx, T * d->top_k, d->n_experts, expert_off, perm, inv_or_null, nullptr,
                                      reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "permute kernel launch");
   return ok();

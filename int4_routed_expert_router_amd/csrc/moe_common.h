@@ -53,6 +53,16 @@ __device__ __forceinline__ uint32_t wave_allreduce_u32(uint32_t v, Op op) {
   v = op(static_cast<uint32_t>(b[0]), static_cast<uint32_t>(b[1]));
   return v;
 }
+// Sum over each row of 16 lanes (the first four steps of the all-reduce):
+// every lane of a row ends with the row's sum, with identical bits.
+__device__ __forceinline__ uint32_t dpp_row_sum(uint32_t v) {
+  auto add = [](uint32_t a, uint32_t b) { return __float_as_uint(__uint_as_float(a) + __uint_as_float(b)); };
+  v = add(v, dpp_u32<0xB1>(v));
+  v = add(v, dpp_u32<0x4E>(v));
+  v = add(v, dpp_u32<0x141>(v));
+  v = add(v, dpp_u32<0x140>(v));
+  return v;
+}
 __device__ __forceinline__ float wave_sum(float v) {
   return __uint_as_float(wave_allreduce_u32(__float_as_uint(v), [](uint32_t a, uint32_t b) {
     return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));

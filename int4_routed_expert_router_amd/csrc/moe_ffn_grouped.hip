@@ -1,22 +1,41 @@
 // Batched grouped-GEMM family on the gfx950 matrix cores.
 //
 // When a batch routes many tokens to the same experts, each expert's weights
-// are streamed for all of its tokens together: the rows of the batch are
-// bucketed by expert (stable counting sort), and work items of up to 16 of one
-// expert's token rows are multiplied by a slice of that expert's weights with
-// v_mfma_f32_16x16x32_{bf16,f16}.
+// are streamed once per run of up to 16 of its token rows (a *unit*, built by
+// the bucketing kernel) and multiplied on the matrix cores with
+// v_mfma_f32_16x16x32_f16: A = the unit's activations, B = the weights.
 //
-// Precision.  The weight operand is the nibble itself, exactly: each 16-bit
-// lane value encodes v = 1 + q/16 (exact in bf16 and fp16), so one MFMA over a
-// 32-column half computes P = sum v*x with exact products and fp32
-// accumulation.  The affine group dequantisation is applied in fp32:
-//     sum_c (s q_c + b) x_c = 16 s P + (b - 16 s) sum_c x_c,
-// the scale term per 64-column chunk (one FMA per output), the bias term once
-// per work item as one more matrix product over the groups,
-// [tokens x groups](sum x) . [groups x rows](b - 16 s), with both operands
-// split into bf16 hi + lo pairs (four MFMAs).  Activations are exact in the
-// operand type; the SwiGLU output h enters the down projection as a hi + lo
-// bf16 pair (h = hi + lo to 16 significant bits).
+// Work split.  A unit's output is cut into pair-tiles (gate/up: 16 rows of
+// gate plus the same 16 rows of up; down: 32 rows of the output).  All
+// pair-tiles of all units form one list, and workgroup w (one per CU) takes
+// the contiguous range [w L / W, (w+1) L / W) of it, so every CU streams the
+// same number of weight bytes.  Logical workgroup indices are assigned so that
+// consecutive ranges (the tiles of one unit, and the units of one expert) run
+// on one XCD and share its L2.  Inside a workgroup the reduction dimension is
+// split across waves (gate/up: 8 waves take every 8th 64-column chunk of one
+// pair-tile; down: 4 pair-tiles at a time, 2 waves each), and the partial
+// tiles are summed through LDS in a fixed order.
+//
+// Weight stream.  Each wave keeps the chunks of the next kDepth tiles in
+// flight in register slots: the slot of a chunk is refilled (with the same
+// chunk of the tile kDepth steps ahead) as soon as it has been decoded, so the
+// loads never wait for the products and never cross a barrier.
+//
+// Operands.  A nibble q becomes an fp16 operand with a single mask: the
+// blob word keeps values 2m, 2m+1 of a 16-byte lane group in nibbles m and
+// m + 4, so w & 0x000F000F and (w >> 8) & 0x000F000F are two fp16 subnormals
+// q * 2^-24 (values 0, 1 and 4, 5) and w & 0x00F000F0, (w >> 8) & 0x00F000F0
+// are q * 2^-20 (values 2, 3 and 6, 7).  The matrix cores take fp16
+// subnormal inputs exactly, so the activations at the second kind of
+// position are given scaled by 1/16 and every product is q * x * 2^-24,
+// exact in fp32.  The affine group dequantisation is applied in fp32:
+//     sum_c (s q_c + b) x_c = s * 2^24 * P + b * sum_c x_c,
+// with the column sums of the unit's activations computed once per unit.
+// Activations become fp16 (bf16 inputs are exact in fp16 within its range;
+// the grouped family needs |x| and |h| below 65504); the SwiGLU output h
+// enters the down projection as an fp16 hi + lo pair (22 significant bits),
+// written operand-ready by the gate/up kernel together with the fp32 sums of
+// hi + lo over 16-column blocks for the down kernel's bias term.
 //
 // Operand layout of v_mfma_f32_16x16x32 (64 lanes, lane l: n = l % 16,
 // kb = l / 16): A lane holds row m = n, k = 8kb..8kb+7; B lane holds column n,
@@ -24,51 +43,226 @@
 // stores each lane's B values contiguously (see the public header), so one
 // 16-byte load per lane fetches the B operands of two 16-row tiles for a
 // 64-column chunk.
-//
-// Scheduling.  Both kernels are persistent: workgroup w runs work items
-// w, w + grid, ... of the list built by the bucketing kernel (longest units
-// first; sub-items of one unit on one XCD).  Each wave streams its weight
-// chunks through kPF register slots; the refills issued while the last chunks
-// of an item are processed already fetch the next item's first chunks, and the
-// next item's descriptor and token ids are loaded during the current item, so
-// the weight stream does not stop between items.  An item's activations are
-// staged in LDS once, with direct global-to-LDS loads.
 #include "moe_common.h"
 #include "moe_kernels.h"
 
 namespace moe {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
 constexpr int kSub = kSubTokens;
-constexpr int kPF = 16;                              // gate/up weight chunks in flight per wave
-constexpr int kPFD = 2 * kGroupedMaxInter / 64;      // down: a whole item's stream (two pair-tiles)
-constexpr int kGridGU = 1024;                        // persistent grids (multiples of 8)
-constexpr int kGridD = 1024;
+constexpr int kWaves = 8;              // waves per workgroup (both kernels)
+constexpr int kSlot = 4;               // weight chunks per wave and tile step
+constexpr float kQScale = 16777216.0f; // 2^24: products are q * x * 2^-24
 
-template <int ACT>
 __device__ __forceinline__ f32x4_t mfma(uint4 a, uint4 b, f32x4_t c) {
-  if constexpr (ACT == 2)
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
-                                                   c, 0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
-                                                  0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c, 0,
+                                                0, 0);
 }
 
-// The 8 values of a blob word as an MFMA operand (value j -> slot j).
-template <int ACT>
+// B operand of one blob word (8 values): fp16 subnormals, see above.
 __device__ __forceinline__ uint4 word_operand(uint32_t w) {
-  return make_uint4(q_pair<ACT>(w, 0), q_pair<ACT>(w, 1), q_pair<ACT>(w, 2), q_pair<ACT>(w, 3));
+  const uint32_t t = w >> 8;
+  return make_uint4(w & 0x000F000Fu, w & 0x00F000F0u, t & 0x000F000Fu, t & 0x00F000F0u);
 }
 
-// fp32 -> (hi, lo) bf16 bit patterns with hi + lo = v to 16 significant bits.
-__device__ __forceinline__ void split_bf16(float v, uint32_t& hi, uint32_t& lo) {
-  hi = f32_to_act<2>(v);
-  lo = f32_to_act<2>(v - bf16_bits_to_f32(hi));
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float v) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
+}
+__device__ __forceinline__ float f16_bits_f32(uint32_t b) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(b)));
+}
+
+// A operand from 8 activations (16 bytes, value j at half j): fp16, values
+// 2, 3, 6, 7 scaled by 1/16.  Adds the 8 activations to sum.
+template <int ACT>
+__device__ __forceinline__ uint4 act_operand(uint4 raw, float& sum) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const float v0 = act_to_f32<ACT>(w[d] & 0xFFFFu), v1 = act_to_f32<ACT>(w[d] >> 16);
+    sum += v0 + v1;
+    const float f = (d & 1) ? 0.0625f : 1.0f;
+    o[d] = f32_to_f16_bits(v0 * f) | (f32_to_f16_bits(v1 * f) << 16);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// Wave-uniform read of memory that no kernel of the launch writes (unit
+// records, counts, expert offsets): through the constant address space, so
+// the compiler uses scalar loads, which do not enter the vector-memory
+// counter that orders the weight stream.
+template <class T>
+__device__ __forceinline__ T load_uniform(const T* p) {
+  return *reinterpret_cast<const __attribute__((address_space(4))) T*>(
+      reinterpret_cast<const __attribute__((address_space(4))) char*>(reinterpret_cast<uintptr_t>(p)));
+}
+
+template <int V>
+struct Half {
+  static constexpr int value = V;
+};
+
+struct UnitHdr {
+  int row0, mc, expert;
+};
+__device__ __forceinline__ UnitHdr unit_hdr(const int32_t* units, int u) {
+  const int32_t* r = units + static_cast<size_t>(u) * kUnitInts;
+  return UnitHdr{load_uniform(r), load_uniform(r + 1), load_uniform(r + 2)};
+}
+
+__device__ __forceinline__ const uint8_t* expert_blob(const FfnArgs& a, int expert) {
+  return expert < 0 ? a.shared
+                    : a.experts + (a.offsets ? load_uniform(a.offsets + expert) : static_cast<uint64_t>(expert) * a.stride);
+}
+
+// Logical index of this workgroup: consecutive logical indices share an XCD
+// (hardware assigns workgroups to the 8 XCDs round-robin).
+__device__ __forceinline__ int logical_wg() {
+  const int W = gridDim.x;
+  return (blockIdx.x & 7) * (W >> 3) + (blockIdx.x >> 3);
+}
+
+// One slot of the weight stream: 16 bytes of nibbles and the fp16 (s, b) pairs
+// of the chunk's group(s) for the lane's row n of both tiles.
+struct Slot {
+  uint4 q;
+  uint2 s0, s1;   // s1: second group of the chunk (G = 32 only)
+};
+template <int G>
+__device__ __forceinline__ void load_slot(Slot& sl, const uint4* qb, const uint8_t* sb, int c) {
+  sl.q = qb[static_cast<size_t>(c) * 64];
+  if constexpr (G == 32) {
+    sl.s0 = *reinterpret_cast<const uint2*>(sb + static_cast<size_t>(2 * c) * 128);
+    sl.s1 = *reinterpret_cast<const uint2*>(sb + static_cast<size_t>(2 * c + 1) * 128);
+  } else {
+    sl.s0 = *reinterpret_cast<const uint2*>(sb + static_cast<size_t>((64 * c) / G) * 128);
+  }
+}
+
+// Pins a value as computed at this point: the compiler may not move its
+// computation below a later memory access.  Used to make sure a weight slot is
+// fully decoded before its refill is issued, so that the refill lands in the
+// same registers (no copies, no early waits on the refill).
+__device__ __forceinline__ void pin(uint4& v) {
+  asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w) : : "memory");
+}
+__device__ __forceinline__ void pin(float& v) { asm volatile("" : "+v"(v) : : "memory"); }
+
+
+
+// Decoded slot: B operands of both tiles for both 32-column halves, scales
+// and biases (per half; equal unless G = 32).
+struct Decoded {
+  uint4 bA0, bA1, bB0, bB1;
+  float sA0, sB0, sA1, sB1;
+  float cA0, cB0, cA1, cB1;
+};
+template <int G>
+__device__ __forceinline__ Decoded decode_slot(const Slot& sl) {
+  Decoded d;
+  d.bA0 = word_operand(sl.q.x);
+  d.bA1 = word_operand(sl.q.y);
+  d.bB0 = word_operand(sl.q.z);
+  d.bB1 = word_operand(sl.q.w);
+  d.sA0 = f16_bits_to_f32(sl.s0.x & 0xFFFFu);
+  d.sB0 = f16_bits_to_f32(sl.s0.y & 0xFFFFu);
+  d.cA0 = f16_bits_to_f32(sl.s0.x >> 16);
+  d.cB0 = f16_bits_to_f32(sl.s0.y >> 16);
+  if constexpr (G == 32) {
+    d.sA1 = f16_bits_to_f32(sl.s1.x & 0xFFFFu);
+    d.sB1 = f16_bits_to_f32(sl.s1.y & 0xFFFFu);
+    d.cA1 = f16_bits_to_f32(sl.s1.x >> 16);
+    d.cB1 = f16_bits_to_f32(sl.s1.y >> 16);
+  } else {
+    d.sA1 = d.sA0;
+    d.sB1 = d.sB0;
+    d.cA1 = d.cA0;
+    d.cB1 = d.cB0;
+  }
+  pin(d.bA0);
+  pin(d.bA1);
+  pin(d.bB0);
+  pin(d.bB1);
+  pin(d.sA0);
+  pin(d.sB0);
+  pin(d.cA0);
+  pin(d.cB0);
+  if constexpr (G == 32) {
+    pin(d.sA1);
+    pin(d.sB1);
+    pin(d.cA1);
+    pin(d.cB1);
+  }
+  return d;
+}
+
+// Products of one chunk: P = A . B for both tiles (per 32-column half when
+// the halves belong to different groups).  With DUAL the A operand is a hi +
+// lo pair (a0 + l0, a1 + l1), both multiplied.
+struct Prod {
+  f32x4_t pA0, pB0, pA1, pB1;   // pA1, pB1: second half (G = 32 only)
+};
+template <int G, bool DUAL>
+__device__ __forceinline__ Prod chunk_mfma(const Decoded& d, uint4 a0, uint4 a1, uint4 l0, uint4 l1) {
+  const f32x4_t z = {0, 0, 0, 0};
+  Prod p;
+  if constexpr (G == 32) {
+    p.pA0 = mfma(a0, d.bA0, z);
+    p.pB0 = mfma(a0, d.bB0, z);
+    p.pA1 = mfma(a1, d.bA1, z);
+    p.pB1 = mfma(a1, d.bB1, z);
+    if constexpr (DUAL) {
+      p.pA0 = mfma(l0, d.bA0, p.pA0);
+      p.pB0 = mfma(l0, d.bB0, p.pB0);
+      p.pA1 = mfma(l1, d.bA1, p.pA1);
+      p.pB1 = mfma(l1, d.bB1, p.pB1);
+    }
+  } else {
+    p.pA0 = mfma(a0, d.bA0, z);
+    p.pB0 = mfma(a0, d.bB0, z);
+    if constexpr (DUAL) {
+      p.pA0 = mfma(l0, d.bA0, p.pA0);
+      p.pB0 = mfma(l0, d.bB0, p.pB0);
+    }
+    p.pA0 = mfma(a1, d.bA1, p.pA0);
+    p.pB0 = mfma(a1, d.bB1, p.pB0);
+    if constexpr (DUAL) {
+      p.pA0 = mfma(l1, d.bA1, p.pA0);
+      p.pB0 = mfma(l1, d.bB1, p.pB0);
+    }
+  }
+  return p;
+}
+
+// Scale and bias of one chunk: acc += s * P, bias += b * colsum.  cs0, cs1:
+// column sums of the two halves for the lane's 4 output rows (tokens).
+struct Coef {
+  float sA0, sB0, cA0, cB0, sA1, sB1, cA1, cB1;
+};
+__device__ __forceinline__ Coef coef_of(const Decoded& d) {
+  return Coef{d.sA0, d.sB0, d.cA0, d.cB0, d.sA1, d.sB1, d.cA1, d.cB1};
+}
+template <int G>
+__device__ __forceinline__ void chunk_scale(const Prod& p, const Coef& k, const float* cs0, const float* cs1,
+                                            f32x4_t& accA, f32x4_t& accB, f32x4_t& biasA, f32x4_t& biasB) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (G == 32) {
+      accA[i] = fmaf(k.sA1, p.pA1[i], fmaf(k.sA0, p.pA0[i], accA[i]));
+      accB[i] = fmaf(k.sB1, p.pB1[i], fmaf(k.sB0, p.pB0[i], accB[i]));
+      biasA[i] = fmaf(k.cA1, cs1[i], fmaf(k.cA0, cs0[i], biasA[i]));
+      biasB[i] = fmaf(k.cB1, cs1[i], fmaf(k.cB0, cs0[i], biasB[i]));
+    } else {
+      accA[i] = fmaf(k.sA0, p.pA0[i], accA[i]);
+      accB[i] = fmaf(k.sB0, p.pB0[i], accB[i]);
+      biasA[i] = fmaf(k.cA0, cs0[i], biasA[i]);
+      biasB[i] = fmaf(k.cB0, cs0[i], biasB[i]);
+    }
+  }
 }
 
 // 16-byte global -> LDS copy by the active lanes of a wave; lane i writes
@@ -82,521 +276,490 @@ __device__ __forceinline__ void dma16(const void* g, void* lds_base) {
 // the 16 rows hit different banks.
 __device__ __forceinline__ int unit_pos(int m, int u8, int upr) { return m * upr + (u8 ^ (m & 7)); }
 
-// Marks a weight slot's decoded operands and scales as computed here: the
-// compiler may not sink the decoding below the slot's refill (a later memory
-// access), which would keep the old and the new slot contents live together.
-__device__ __forceinline__ void consumed(uint4& a, uint4& b, uint4& c, uint4& d, float& s0, float& s1) {
-  asm volatile("" : "+v"(a.x), "+v"(a.y), "+v"(a.z), "+v"(a.w), "+v"(b.x), "+v"(b.y), "+v"(b.z), "+v"(b.w) : : "memory");
-  asm volatile("" : "+v"(c.x), "+v"(c.y), "+v"(c.z), "+v"(c.w), "+v"(d.x), "+v"(d.y), "+v"(d.z), "+v"(d.w), "+v"(s0),
-               "+v"(s1) : : "memory");
-}
-
-struct Item {
-  int row0, mc, block, expert;
-};
-__device__ __forceinline__ Item decode_item(int4 w) { return Item{w.x, w.y & 0xFF, w.y >> 8, w.z}; }
-
-__device__ __forceinline__ const uint8_t* item_blob(const FfnArgs& a, int expert) {
-  return expert < 0 ? a.shared : a.experts + (a.offsets ? a.offsets[expert] : static_cast<uint64_t>(expert) * a.stride);
-}
-
-__device__ __forceinline__ int row_token(const FfnArgs& a, int row) {
-  const int tk = a.T * a.K;
-  return row < tk ? a.tok_sorted[row] : row - tk;
-}
-
-// Bias MFMA B operands for groups g0 + 8kb + 0..7 of the lane's rows:
-// (b - 16 s) of tile A and tile B as hi/lo bf16 (zero beyond ng).
-struct BiasRaw {
-  uint2 v[8];
-};
-__device__ __forceinline__ BiasRaw bias_load(const uint8_t* ssec, int p, int ng, int g0, int n, int kb) {
-  BiasRaw r;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int g = min(g0 + 8 * kb + j, ng - 1);
-    r.v[j] = *reinterpret_cast<const uint2*>(ssec + ((static_cast<uint64_t>(p) * ng + g) * 16 + n) * 8);
+// Stages rows m < mc of a 16-row activation tile (row m = src + off[m] * pitch,
+// width `cols` 16-bit values) into LDS at lds, in the swizzled unit layout.
+// All threads of the workgroup call it; the caller waits and synchronises.
+__device__ __forceinline__ void stage_rows(const uint16_t* src, const int* off, int mc, size_t pitch, int cols,
+                                           uint16_t* lds, int wave, int lane) {
+  const int upr = cols / 8;
+  for (int op = wave; op * 64 < kSub * upr; op += kWaves) {
+    const int u = op * 64 + lane;
+    const int m = u / upr, ph = u - m * upr;
+    if (m < mc) dma16(src + static_cast<size_t>(off[m]) * pitch + 8 * (ph ^ (m & 7)), &lds[op * 64 * 8]);
   }
-  return r;
-}
-__device__ __forceinline__ void bias_operands(const BiasRaw& r, int ng, int g0, int kb, uint4& ah, uint4& al,
-                                              uint4& bh, uint4& bl) {
-  uint32_t vah[4], val[4], vbh[4], vbl[4];
-#pragma unroll
-  for (int j2 = 0; j2 < 4; ++j2) {
-    uint32_t h2[2][2], l2[2][2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int j = 2 * j2 + h;
-      const bool in = g0 + 8 * kb + j < ng;
-      const float ba = in ? fmaf(-16.0f, f16_bits_to_f32(r.v[j].x & 0xFFFFu), f16_bits_to_f32(r.v[j].x >> 16)) : 0.0f;
-      const float bb = in ? fmaf(-16.0f, f16_bits_to_f32(r.v[j].y & 0xFFFFu), f16_bits_to_f32(r.v[j].y >> 16)) : 0.0f;
-      split_bf16(ba, h2[0][h], l2[0][h]);
-      split_bf16(bb, h2[1][h], l2[1][h]);
-    }
-    vah[j2] = h2[0][0] | (h2[0][1] << 16);
-    val[j2] = l2[0][0] | (l2[0][1] << 16);
-    vbh[j2] = h2[1][0] | (h2[1][1] << 16);
-    vbl[j2] = l2[1][0] | (l2[1][1] << 16);
-  }
-  ah = make_uint4(vah[0], vah[1], vah[2], vah[3]);
-  al = make_uint4(val[0], val[1], val[2], val[3]);
-  bh = make_uint4(vbh[0], vbh[1], vbh[2], vbh[3]);
-  bl = make_uint4(vbl[0], vbl[1], vbl[2], vbl[3]);
 }
 
-// A operand of the bias MFMA: group sums of row n, groups g0 + 8kb + 0..7, hi/lo.
-__device__ __forceinline__ void sum_operands(const float* sums, int stride, int ng, int g0, int n, int kb, uint4& hi,
-                                             uint4& lo) {
-  uint32_t vh[4], vl[4];
-#pragma unroll
-  for (int j2 = 0; j2 < 4; ++j2) {
-    uint32_t h[2], l[2];
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int g = g0 + 8 * kb + 2 * j2 + k;
-      split_bf16(g < ng ? sums[n * stride + g] : 0.0f, h[k], l[k]);
-    }
-    vh[j2] = h[0] | (h[1] << 16);
-    vl[j2] = l[0] | (l[1] << 16);
-  }
-  hi = make_uint4(vh[0], vh[1], vh[2], vh[3]);
-  lo = make_uint4(vl[0], vl[1], vl[2], vl[3]);
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (gfx9 encoding; lgkm and export counts untouched).
+constexpr int vmcnt_imm(int n) { return ((n >> 4) << 14) | (0xF << 8) | (0x7 << 4) | (n & 0xF); }
+constexpr int kLgkm0 = (3 << 14) | (0x7 << 4) | 0xF;   // lgkmcnt(0) only
+
+// Workgroup barrier after this wave's direct-to-LDS loads issued before the
+// last `after` vector-memory operations have landed.  Unlike __syncthreads(),
+// whose fence waits for every outstanding load, it leaves the newest `after`
+// loads (the weight prefetch) in flight.
+template <int after>
+__device__ __forceinline__ void staged_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(after));
+  __builtin_amdgcn_s_waitcnt(kLgkm0);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
-__device__ __forceinline__ f32x4_t bias_mfma(uint4 sh, uint4 sl, uint4 bh, uint4 bl, f32x4_t c) {
-  c = mfma<2>(sh, bh, c);
-  c = mfma<2>(sh, bl, c);
-  c = mfma<2>(sl, bh, c);
-  c = mfma<2>(sl, bl, c);
-  return c;
-}
 
 // ---------------------------------------------------------------------------
-// gate/up + SwiGLU.  Item block b = 64 rows of I; wave w owns gate/up pair-tile
-// p = 4b + w, i.e. weight chunks p*nc .. p*nc + nc - 1 of the GU section.
-// Output: h as hi and lo bf16 planes.
+// gate/up + SwiGLU.  Tile = gate/up pair-tile pt of a unit (16 rows of gate
+// and of up for the unit's <= 16 tokens, full hidden width); wave w takes the
+// chunks c_j = w + 8 j (j < 4).  Each wave holds the A operands of its own
+// chunks for the current unit in registers (no LDS staging), and loads the
+// next unit's activations as soon as its weight stream reaches that unit.
+// Output: h as fp16 hi and lo planes, operand-ready for the down projection
+// (columns with (col & 2) != 0 scaled by 1/16), at rows row0.., columns
+// 16 pt.., and hsum[row][pt] = sum over the 16 columns of h (hi + lo).
 // ---------------------------------------------------------------------------
-// NCT > 0: the hidden size is 64*NCT (compile-time chunk count, refills run into
-// the next item when NCT % kPF == 0); NCT == 0: any hidden size up to the
-// family's maximum, slots reloaded per item.
-template <int ACT, int G, int NCT>
-__global__ __launch_bounds__(256) void k_gateup_grouped(FfnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t xs[kSub * kGroupedMaxH];
-  __shared__ float gsum[kSub][kGroupedMaxH / 32 + 1];
-  __shared__ int tok[kSub];
+template <int ACT, int G>
+__global__ __launch_bounds__(512) void k_gateup_tiles(FfnArgs a) {
+  // tiles are processed in pairs (one barrier per pair); the two tiles of a
+  // pair use the two slot groups, so kDepth = 2 tiles are in flight per wave
+  constexpr int kDepth = 2;
+  constexpr int kHalves = G == 32 ? 2 : 1;  // groups per chunk
+  // partial tiles of a pair: buffer, tile, wave, gate / up, row e, lane.  The
+  // row stride of 80 floats puts rows e and e + 1 on opposite bank halves, so
+  // the reduction reads (64 lanes: 4 rows x 16 consecutive lanes) take the
+  // minimum two LDS cycles.
+  constexpr int kRowStride = 80;
+  __shared__ float red[2][2][kWaves][2][4][kRowStride];
+  // A operands of the current unit's activations, per wave: chunk j, half,
+  // lane (16 bytes; only this wave reads them)
+  __shared__ uint4 xop[kWaves][kSlot][2][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, kb = lane >> 4;
-  const int H = NCT > 0 ? 64 * NCT : a.H;
-  const int nc = H / 64, ng = H / G, upr = H / 8;
-  const int n_work = a.n_work[0];
+  const int H = a.H, nc = H / 64, ng = H / G;
+  const int n_su = load_uniform(a.n_units), n_ru = load_uniform(a.n_units + 1);
+  const int nts = a.Is / 16, ntr = a.I / 16;
+  const int L = n_su * nts + n_ru * ntr, lw = logical_wg();
+  const int t0 = static_cast<int>((static_cast<long long>(lw) * L) >> kGridTilesLog2);
+  const int t1 = static_cast<int>((static_cast<long long>(lw + 1) * L) >> kGridTilesLog2);
+  if (t0 >= t1) return;
   const int hplane = (a.T * a.K + (a.Is > 0 ? a.T : 0)) * a.hstride;
   uint16_t* h_hi = reinterpret_cast<uint16_t*>(a.h);
   uint16_t* h_lo = h_hi + hplane;
-  int wi = blockIdx.x;
-  if (wi >= n_work) return;
-  Item it = decode_item(a.work_gu[wi]);
-  const uint8_t* blob = item_blob(a, it.expert);
-  int p = 4 * it.block + wave;
-  const uint4* qblk = reinterpret_cast<const uint4*>(blob) + static_cast<size_t>(p) * nc * 64;
-  const uint8_t* ssec = blob + blob_gu_s(H, it.expert < 0 ? a.Is : a.I);
-  // weight stream: slot u holds the chunk c with c % kPF == u
-  uint4 qn[kPF];
-  uint2 sn[kPF];
+  const int hs_stride = a.hstride / 16;
+  // tile cursor: (unit, pair-tile); units before n_su have nts tiles, the rest ntr
+  struct Cursor {
+    int u, pt;
+  };
+  auto locate = [&](int t) -> Cursor {
+    const int tsh = n_su * nts;
+    if (t < tsh) return Cursor{t / nts, t % nts};
+    return Cursor{n_su + (t - tsh) / ntr, (t - tsh) % ntr};
+  };
+  auto advance = [&](Cursor& cr) {
+    if (++cr.pt == (cr.u < n_su ? nts : ntr)) {
+      ++cr.u;
+      cr.pt = 0;
+    }
+  };
+  // ---- activations: raw prefetch (xr) of unit pu, operands (xa) of unit xu
+  uint4 xr[kSlot][2];   // raw activations of the prefetched unit
+  float csv[kSlot][kHalves][4];   // column sums for the lane's output rows 4kb..4kb+3
+  int pu = -1, prow0 = 0, pmc = 0;
+  int xu = -1, row0 = 0, mc = 0;
+  // issue the activation loads of unit u (record rec) into xr
+  auto prefetch_x = [&](int u, const int32_t* rec) {
+    const int r0 = load_uniform(rec), m_c = load_uniform(rec + 1);
+    int tk = load_uniform(rec + 4);   // lanes beyond the unit's rows read row 0 (unused)
 #pragma unroll
-  for (int u = 0; u < kPF; ++u) {
-    const int c = min(u, nc - 1);
-    qn[u] = qblk[static_cast<size_t>(c) * 64 + lane];
-    sn[u] = *reinterpret_cast<const uint2*>(ssec + ((static_cast<uint64_t>(p) * ng + (64 * c) / G) * 16 + n) * 8);
+    for (int i = 1; i < kSub; ++i) {
+      const int ti = load_uniform(rec + 4 + i);
+      tk = (n == i && i < m_c) ? ti : tk;
+    }
+    const uint16_t* xrow = a.x + static_cast<size_t>(tk) * H + 8 * kb;
+#pragma unroll
+    for (int j = 0; j < kSlot; ++j) {
+      const int c = min(wave + kWaves * j, nc - 1);
+      xr[j][0] = *reinterpret_cast<const uint4*>(xrow + 64 * c);
+      xr[j][1] = *reinterpret_cast<const uint4*>(xrow + 64 * c + 32);
+    }
+    pu = u;
+    prow0 = r0;
+    pmc = m_c;
+  };
+  // xr -> A operands (this wave's LDS area) and the column sums (32-column
+  // halves) for the C layout rows
+  auto take_x = [&]() {
+#pragma unroll
+    for (int j = 0; j < kSlot; ++j) {
+      float s0 = 0.0f, s1 = 0.0f;
+      xop[wave][j][0][lane] = act_operand<ACT>(xr[j][0], s0);
+      xop[wave][j][1][lane] = act_operand<ACT>(xr[j][1], s1);
+      float hs[kHalves];
+      if constexpr (G == 32) {
+        hs[0] = s0;
+        hs[1] = s1;
+      } else {
+        hs[0] = s0 + s1;
+      }
+#pragma unroll
+      for (int hh = 0; hh < kHalves; ++hh) {
+        // sum over the 4 lane rows (kb) holding token n, then fetch the sums of
+        // tokens 4kb..4kb+3 (the rows of this lane's accumulator)
+        uint32_t v = __float_as_uint(hs[hh]);
+        const auto p16 = __builtin_amdgcn_permlane16_swap(static_cast<int>(v), static_cast<int>(v), false, false);
+        v = __float_as_uint(__uint_as_float(static_cast<uint32_t>(p16[0])) + __uint_as_float(static_cast<uint32_t>(p16[1])));
+        const auto p32 = __builtin_amdgcn_permlane32_swap(static_cast<int>(v), static_cast<int>(v), false, false);
+        v = __float_as_uint(__uint_as_float(static_cast<uint32_t>(p32[0])) + __uint_as_float(static_cast<uint32_t>(p32[1])));
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          csv[j][hh][i] = __uint_as_float(static_cast<uint32_t>(__shfl(static_cast<int>(v), 4 * kb + i, kWave)));
+      }
+    }
+    xu = pu;
+    row0 = prow0;
+    mc = pmc;
+    pu = -1;
+  };
+  // ---- weight stream: the refill cursor runs kDepth tiles ahead (clamped to
+  // the last tile); the unit's expert is looked up only when the unit
+  // changes, and a new unit's activations are fetched right away when the
+  // raw buffer is free, else after the current unit's are taken
+  int su = -1;
+  const uint8_t* sblob = nullptr;
+  int sI = 0;
+  int want = -1;   // unit whose activations still have to be fetched
+  auto tile_src = [&](const Cursor cr, const uint4*& qb, const uint8_t*& sb) {
+    if (cr.u != su) {
+      const int32_t* rec = a.units + static_cast<size_t>(cr.u) * kUnitInts;
+      const int ex = load_uniform(rec + 2);
+      su = cr.u;
+      sblob = expert_blob(a, ex);
+      sI = ex < 0 ? a.Is : a.I;
+      if (cr.u != xu && cr.u != pu) {
+        if (pu < 0) prefetch_x(cr.u, rec);
+        else want = cr.u;
+      }
+    }
+    qb = reinterpret_cast<const uint4*>(sblob) + static_cast<size_t>(cr.pt) * nc * 64 + lane;
+    sb = sblob + blob_gu_s(H, sI) + (static_cast<size_t>(cr.pt) * ng * 16 + n) * 8;
+  };
+  Cursor cc = locate(t0);   // compute cursor (tile t)
+  Cursor rc = cc;           // refill cursor (tile min(t + kDepth, t1 - 1))
+  int rt = t0;
+  // first unit: activations first, then the weights of the first kDepth tiles
+  prefetch_x(cc.u, a.units + static_cast<size_t>(cc.u) * kUnitInts);
+  Slot sl[kDepth * kSlot];
+#pragma unroll
+  for (int hf = 0; hf < kDepth; ++hf) {
+    const uint4* qb;
+    const uint8_t* sb;
+    tile_src(rc, qb, sb);
+#pragma unroll
+    for (int j = 0; j < kSlot; ++j) load_slot<G>(sl[hf * kSlot + j], qb, sb, min(wave + kWaves * j, nc - 1));
+    if (rt + 1 < t1) {
+      ++rt;
+      advance(rc);
+    }
   }
-  int tok_next = (tid < it.mc) ? row_token(a, it.row0 + tid) : 0;
-  // the refills run into the next item only when its chunks land in the slots
-  // they are read from (c % kPF), i.e. when an item has a multiple of kPF chunks
-  static_assert(NCT == 0 || NCT % kPF == 0, "compile-time chunk count must fill whole slot blocks");
-  constexpr bool cross = NCT > 0;
-  bool first = true;
-  while (true) {
-    if (!cross && !first) {
-#pragma unroll
-      for (int u = 0; u < kPF; ++u) {
-        const int c = min(u, nc - 1);
-        qn[u] = qblk[static_cast<size_t>(c) * 64 + lane];
-        sn[u] = *reinterpret_cast<const uint2*>(ssec + ((static_cast<uint64_t>(p) * ng + (64 * c) / G) * 16 + n) * 8);
+  // chunk products of tile t (slot group hf) -> this wave's partial in
+  // red[pb][hf]; returns the tile's rows and pair-tile for the reduction
+  struct TileOut {
+    int row0, mc, pt;
+  };
+  auto compute = [&](const int t, auto hfc, const int pb) -> TileOut {
+    constexpr int hf = decltype(hfc)::value;
+    if (cc.u != xu) {
+      take_x();
+      if (want >= 0) {
+        prefetch_x(want, a.units + static_cast<size_t>(want) * kUnitInts);
+        want = -1;
       }
     }
-    first = false;
-    // ---- item setup: tokens, next descriptor, activation staging, bias operands
-    __syncthreads();                  // previous item's LDS readers are done
-    if (tid < it.mc) tok[tid] = tok_next;
-    const int wi2 = wi + gridDim.x;
-    const bool has_next = wi2 < n_work;
-    const int4 w2 = has_next ? a.work_gu[wi2] : make_int4(0, 0, 0, 0);
-    const int nbias = (ng + 31) / 32;
-    BiasRaw braw[kGroupedMaxH / 32 / 32];
-#pragma unroll
-    for (int gb = 0; gb < kGroupedMaxH / 32 / 32; ++gb)
-      if (gb < nbias) braw[gb] = bias_load(ssec, p, ng, 32 * gb, n, kb);
-    __syncthreads();                  // tok visible
-    for (int op = wave; op * 64 < kSub * upr; op += 4) {
-      const int u = op * 64 + lane;
-      const int m = u / upr, ph = u - m * upr;
-      if (m < it.mc) dma16(a.x + static_cast<size_t>(tok[m]) * H + 8 * (ph ^ (m & 7)), &xs[op * 64 * 8]);
+    const TileOut out{row0, mc, cc.pt};
+    // refill source: tile t + kDepth (the last tile again near the end; unused)
+    const uint4* qnx;
+    const uint8_t* snx;
+    tile_src(rc, qnx, snx);
+    if (rt + 1 < t1) {
+      ++rt;
+      advance(rc);
     }
-    __builtin_amdgcn_s_waitcnt(0);    // this wave's direct-to-LDS loads have landed
-    __syncthreads();
-    for (int idx = tid; idx < kSub * ng; idx += 256) {
-      const int m = idx / ng, g = idx - m * ng;
-      float s = 0.0f;
-      if (m < it.mc) {
-        for (int c8 = 0; c8 < G / 8; ++c8) {
-          const uint4 v = *reinterpret_cast<const uint4*>(&xs[unit_pos(m, g * (G / 8) + c8, upr) * 8]);
-          const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+    f32x4_t accA = {0, 0, 0, 0}, accB = {0, 0, 0, 0}, biasA = {0, 0, 0, 0}, biasB = {0, 0, 0, 0};
+    // the scale of chunk j is applied after the products of chunk j + 1 are
+    // issued, so that the matrix-core latency is covered
+    Prod pp;
+    Coef pk;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) s += act_to_f32<ACT>(w4[i] & 0xFFFFu) + act_to_f32<ACT>(w4[i] >> 16);
-        }
+    for (int j = 0; j < kSlot; ++j) {
+      const int c = wave + kWaves * j;
+      Slot& s = sl[hf * kSlot + j];
+      const Decoded d = decode_slot<G>(s);
+      load_slot<G>(s, qnx, snx, min(c, nc - 1));
+      Prod p;
+      if (c < nc) {
+        const uint4 a0 = xop[wave][j][0][lane], a1 = xop[wave][j][1][lane];
+        p = chunk_mfma<G, false>(d, a0, a1, a0, a1);
       }
-      gsum[m][g] = s;
+      if (j > 0 && c - kWaves < nc) chunk_scale<G>(pp, pk, csv[j - 1][0], csv[j - 1][kHalves - 1], accA, accB, biasA, biasB);
+      pp = p;
+      pk = coef_of(d);
     }
-    __syncthreads();
-    f32x4_t bsg = {0, 0, 0, 0}, bsu = {0, 0, 0, 0};
-#pragma unroll
-    for (int gb = 0; gb < kGroupedMaxH / 32 / 32; ++gb) {
-      if (gb < nbias) {
-        uint4 sh, sl, bah, bal, bbh, bbl;
-        sum_operands(&gsum[0][0], kGroupedMaxH / 32 + 1, ng, 32 * gb, n, kb, sh, sl);
-        bias_operands(braw[gb], ng, 32 * gb, kb, bah, bal, bbh, bbl);
-        bsg = bias_mfma(sh, sl, bah, bal, bsg);
-        bsu = bias_mfma(sh, sl, bbh, bbl, bsu);
-      }
-    }
-    // ---- next item's weight addresses (its first chunks are fetched by the refills)
-    const Item it2 = decode_item(w2);
-    const uint8_t* blob2 = has_next ? item_blob(a, it2.expert) : blob;
-    const int p2 = has_next ? 4 * it2.block + wave : p;
-    const uint4* qblk2 = reinterpret_cast<const uint4*>(blob2) + static_cast<size_t>(p2) * nc * 64;
-    const uint8_t* ssec2 = has_next ? blob2 + blob_gu_s(H, it2.expert < 0 ? a.Is : a.I) : ssec;
-    // (without a next item these point at this item's own first chunks: the
-    // refills then repeat loads of valid memory and are never read)
-    // ---- main loop: blocks of kPF chunks; within a block chunk cb + u sits in
-    // slot u and is replaced by chunk cb + kPF + u, or, past the item's end,
-    // by the next item's chunk u (cross) / this item's last chunk (repeat, unused)
-    f32x4_t accg = {0, 0, 0, 0}, accu = {0, 0, 0, 0}, pg = {0, 0, 0, 0}, pu = {0, 0, 0, 0};
-    // A operand of chunk c: unit (n, 8c + kb) = lane base + 8c units (the XOR
-    // swizzle only touches the low 3 bits, which 8c leaves free)
-    const uint16_t* xa0 = &xs[(n * upr + (kb ^ (n & 7))) * 8];
-    const uint16_t* xa1 = &xs[(n * upr + ((kb + 4) ^ (n & 7))) * 8];
-    const uint8_t* srow = ssec + (static_cast<uint64_t>(p) * ng * 16 + n) * 8;   // scales of (p, group 0, n)
-    const uint8_t* srow2 = ssec2 + (static_cast<uint64_t>(p2) * ng * 16 + n) * 8;
-#pragma unroll 1
-    for (int cb = 0; cb < nc; cb += kPF) {
-      const bool nxt = cross && cb + kPF >= nc;
-      const uint4* qsrc = nxt ? qblk2 : qblk;
-      const uint8_t* ssrc = nxt ? srow2 : srow;
-      const int cr = nxt ? 0 : cb + kPF;
-#pragma unroll
-      for (int u = 0; u < kPF; ++u) {
-        const int c = cb + u;
-        if (cross || c < nc) {
-          const uint4 q = qn[u];
-          const uint2 sr = sn[u];
-          uint4 bg0 = word_operand<ACT>(q.x), bg1 = word_operand<ACT>(q.y);
-          uint4 bu0 = word_operand<ACT>(q.z), bu1 = word_operand<ACT>(q.w);
-          float sg = f16_bits_to_f32(sr.x & 0xFFFFu), su = f16_bits_to_f32(sr.y & 0xFFFFu);
-          // the slot is fully consumed before its refill is issued, so the refill
-          // lands in the same registers (no copies, no early waits at the back-edge)
-          consumed(bg0, bg1, bu0, bu1, sg, su);
-          {
-            const int cn = cross ? cr + u : min(cr + u, nc - 1);
-            qn[u] = qsrc[static_cast<size_t>(cn) * 64 + lane];
-            sn[u] = *reinterpret_cast<const uint2*>(ssrc + static_cast<size_t>((64 * cn) / G) * 128);
-          }
-          const uint4 a0 = *reinterpret_cast<const uint4*>(xa0 + 64 * c);
-          const uint4 a1 = *reinterpret_cast<const uint4*>(xa1 + 64 * c);
-          if constexpr (G == 32) {
-            const uint2 sr1 = *reinterpret_cast<const uint2*>(srow + static_cast<size_t>(2 * c + 1) * 128);
-            const float sg1 = f16_bits_to_f32(sr1.x & 0xFFFFu), su1 = f16_bits_to_f32(sr1.y & 0xFFFFu);
-            const f32x4_t z = {0, 0, 0, 0};
-            const f32x4_t g0v = mfma<ACT>(a0, bg0, z), u0v = mfma<ACT>(a0, bu0, z);
-            const f32x4_t g1v = mfma<ACT>(a1, bg1, z), u1v = mfma<ACT>(a1, bu1, z);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              accg[i] = fmaf(sg, g0v[i], accg[i]);
-              accu[i] = fmaf(su, u0v[i], accu[i]);
-              accg[i] = fmaf(sg1, g1v[i], accg[i]);
-              accu[i] = fmaf(su1, u1v[i], accu[i]);
-            }
-          } else {
-            pg = mfma<ACT>(a0, bg0, pg);
-            pu = mfma<ACT>(a0, bu0, pu);
-            pg = mfma<ACT>(a1, bg1, pg);
-            pu = mfma<ACT>(a1, bu1, pu);
-            // G = 128 spans chunks c, c + 1 (c even; cb is a multiple of kPF, which is even)
-            if (G == 64 || (u & 1)) {
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                accg[i] = fmaf(sg, pg[i], accg[i]);
-                accu[i] = fmaf(su, pu[i], accu[i]);
-              }
-              pg = f32x4_t{0, 0, 0, 0};
-              pu = f32x4_t{0, 0, 0, 0};
-            }
-          }
-        }
-      }
-    }
-    // tokens of the next item (read during this item's tail)
-    if (has_next) tok_next = (tid < it2.mc) ? row_token(a, it2.row0 + tid) : 0;
-    // ---- SwiGLU; lane holds tokens 4kb..4kb+3 of column n of pair-tile p
+    if (wave + kWaves * (kSlot - 1) < nc)
+      chunk_scale<G>(pp, pk, csv[kSlot - 1][0], csv[kSlot - 1][kHalves - 1], accA, accB, biasA, biasB);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int m = 4 * kb + i;
-      if (m < it.mc) {
-        const float ga = fmaf(16.0f, accg[i], bsg[i]);
-        const float up = fmaf(16.0f, accu[i], bsu[i]);
-        const float hv = ga / (1.0f + expf(-ga)) * up;
-        uint32_t hi, lo;
-        split_bf16(hv, hi, lo);
-        const size_t o = static_cast<size_t>(it.row0 + m) * a.hstride + 16 * p + n;
-        h_hi[o] = static_cast<uint16_t>(hi);
-        h_lo[o] = static_cast<uint16_t>(lo);
+      red[pb][hf][wave][0][i][lane] = fmaf(kQScale, accA[i], biasA[i]);
+      red[pb][hf][wave][1][i][lane] = fmaf(kQScale, accB[i], biasB[i]);
+    }
+    advance(cc);
+    return out;
+  };
+  // after the barrier: thread (tile tt, row m, column n) sums the 8 wave
+  // slices of gate and up in wave order and applies SwiGLU
+  auto reduce = [&](const int pb, const TileOut& o0, const TileOut& o1, const int ntiles) {
+    const int tt = tid >> 8, m = (tid >> 4) & 15, nn = tid & 15;
+    if (tt < ntiles) {
+      const TileOut& o = tt == 0 ? o0 : o1;
+      const int src = nn + 16 * (m >> 2), e = m & 3;
+      float ga = 0.0f, up = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        ga += red[pb][tt][w][0][e][src];
+        up += red[pb][tt][w][1][e][src];
+      }
+      const float hv = ga / (1.0f + expf(-ga)) * up;
+      // operand-ready fp16 hi + lo of h * f, f = 1/16 on the columns the down
+      // projection's B operand carries as q * 2^-20 (column 16 pt + nn)
+      const bool sc = (nn & 2) != 0;
+      const float hf_v = sc ? hv * 0.0625f : hv;
+      const uint32_t hi = f32_to_f16_bits(hf_v);
+      const uint32_t lo = f32_to_f16_bits(hf_v - f16_bits_f32(hi));
+      float hs = f16_bits_f32(hi) + f16_bits_f32(lo);
+      hs = sc ? hs * 16.0f : hs;
+      // sum over the 16 columns of this row of the tile (one 16-lane DPP row)
+      hs = __uint_as_float(dpp_row_sum(__float_as_uint(hs)));
+      if (m < o.mc) {
+        const size_t off = static_cast<size_t>(o.row0 + m) * a.hstride + 16 * o.pt + nn;
+        h_hi[off] = static_cast<uint16_t>(hi);
+        h_lo[off] = static_cast<uint16_t>(lo);
+        if (nn == 0) a.hsum[static_cast<size_t>(o.row0 + m) * hs_stride + o.pt] = hs;
       }
     }
-    if (!has_next) break;
-    wi = wi2;
-    it = it2;
-    blob = blob2;
-    p = p2;
-    qblk = qblk2;
-    ssec = ssec2;
+  };
+  // pairs of tiles: both slot groups, one barrier, then the shared reduction
+  // (buffers alternate, so the next pair's partials never overwrite a pair
+  // that is still being reduced)
+  int tb = t0, pb = 0;
+  for (; tb + 2 <= t1; tb += 2, pb ^= 1) {
+    const TileOut o0 = compute(tb, Half<0>{}, pb);
+    const TileOut o1 = compute(tb + 1, Half<1>{}, pb);
+    __syncthreads();
+    reduce(pb, o0, o1, 2);
+  }
+  if (tb < t1) {
+    const TileOut o0 = compute(tb, Half<0>{}, pb);
+    __syncthreads();
+    reduce(pb, o0, o0, 1);
   }
 }
 
 // ---------------------------------------------------------------------------
-// down projection.  Item block b = 256 output rows; wave w owns the two down
-// pair-tiles p0 = 8b + 2w and p0 + 1 (64 rows).  Its weight stream is chunk j
-// = (pair-tile p0 + j / nc, chunk j % nc), j < 2 nc <= kPFD, so an item's whole
-// stream sits in the kPFD slots: slot j is refilled with the next item's chunk
-// j as soon as it is consumed, and the next item's weights are in flight while
-// this one computes.  Reads h (hi/lo planes) of its tokens.
+// down projection.  Tiles are down pair-tiles (32 output rows); a step takes 4
+// consecutive tiles of one unit (quad), tile q4 = wave % 4, and the two waves
+// w, w + 4 split the reduction (chunks w / 4 + 2 j).  h (operand-ready fp16
+// hi, lo) of the unit's rows is staged in LDS.  The second wave's partial
+// goes through LDS; the first adds it and stores yrow (unweighted, fp32).
 // ---------------------------------------------------------------------------
-// NJT > 0: every expert (routed and shared) streams NJT chunks (inter = 32 NJT,
-// compile-time tile split); NJT == 0: any inter up to the family's maximum.
-template <int G, int NJT>
-__global__ __launch_bounds__(256) void k_down_grouped(FfnArgs a) {
+template <int G>
+__global__ __launch_bounds__(512) void k_down_tiles(FfnArgs a) {
+  constexpr int kDepth = G == 32 ? 2 : 4;
+  constexpr int kHalves = G == 32 ? 2 : 1;
   __shared__ __attribute__((aligned(16))) uint16_t hsh[kSub * kGroupedMaxInter];
   __shared__ __attribute__((aligned(16))) uint16_t hsl[kSub * kGroupedMaxInter];
-  __shared__ float gsum[kSub][kGroupedMaxInter / 32 + 1];
-  static_assert(NJT == 0 || (NJT <= kPFD && NJT % 2 == 0), "stream must fit the slots");
+  __shared__ float red[2][4][8][65];
+  __shared__ __attribute__((aligned(16))) float cs[kGroupedMaxInter / 32][kSub];   // 32-column sums of h
+  __shared__ int urow[kSub];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, kb = lane >> 4;
-  const int H = a.H;
-  const int n_pairs = H / 32;
-  const int n_work = a.n_work[1];
+  const int q4 = wave & 3, kh = wave >> 2;
+  const int H = a.H, n_pairs = H / 32;
+  const int qpu = (n_pairs + 3) / 4;   // quads per unit
+  const int n_units = load_uniform(a.n_units) + load_uniform(a.n_units + 1);
+  const int Q = n_units * qpu, lw = logical_wg();
+  const int s0 = static_cast<int>((static_cast<long long>(lw) * Q) >> kGridTilesLog2);
+  const int s1 = static_cast<int>((static_cast<long long>(lw + 1) * Q) >> kGridTilesLog2);
+  if (s0 >= s1) return;
   const int hplane = (a.T * a.K + (a.Is > 0 ? a.T : 0)) * a.hstride;
   const uint16_t* h_hi = reinterpret_cast<const uint16_t*>(a.h);
   const uint16_t* h_lo = h_hi + hplane;
-  int wi = blockIdx.x;
-  if (wi >= n_work) return;
-  Item it = decode_item(a.work_d[wi]);
-  const uint8_t* blob = item_blob(a, it.expert);
-  int I = it.expert < 0 ? a.Is : a.I;
-  int p0 = 8 * it.block + 2 * wave;
-  // weights of pair-tile pp (clamped to the last pair-tile of H) of a blob
-  auto qtile = [&](const uint8_t* bl, int Ii, int pp) -> const uint4* {
-    return reinterpret_cast<const uint4*>(bl + blob_d_q(H, Ii)) +
-           static_cast<size_t>(min(pp, n_pairs - 1)) * (Ii / 64) * 64 + lane;
-  };
-  auto stile = [&](const uint8_t* bl, int Ii, int pp) -> const uint8_t* {
-    return bl + blob_d_s(H, Ii, G) + (static_cast<uint64_t>(min(pp, n_pairs - 1)) * (Ii / G) * 16 + n) * 8;
-  };
-  // stream chunk u of the item (blob, Ii, pair-tiles pp0, pp0 + 1); u past the
-  // stream's end repeats its last chunk (loaded, never used)
-  auto load_chunk = [&](const uint8_t* bl, int Ii, int pp0, int u, uint4& q, uint2& sc) {
-    const int nci = NJT > 0 ? NJT / 2 : Ii / 64;
-    const int j = NJT > 0 ? u : min(u, 2 * nci - 1);
-    const int t = j >= nci ? 1 : 0, c = j - t * nci;
-    q = qtile(bl, Ii, pp0 + t)[static_cast<size_t>(c) * 64];
-    sc = *reinterpret_cast<const uint2*>(stile(bl, Ii, pp0 + t) + static_cast<size_t>((64 * c) / G) * 128);
-  };
-  uint4 qn[kPFD];
-  uint2 sn[kPFD];
-#pragma unroll
-  for (int u = 0; u < kPFD; ++u) load_chunk(blob, I, p0, u, qn[u], sn[u]);
-  while (true) {
-    const int nc = NJT > 0 ? NJT / 2 : I / 64;
-    const int ng = 64 * nc / G, upr = 8 * nc;
-    const uint8_t* dsec = blob + blob_d_s(H, I, G);
-    __syncthreads();
-    const int wi2 = wi + gridDim.x;
-    const bool has_next = wi2 < n_work;
-    const int4 w2 = has_next ? a.work_d[wi2] : make_int4(0, 0, 0, 0);
-    const bool v0 = p0 < n_pairs, v1 = p0 + 1 < n_pairs;
-    BiasRaw braw[2];
-    braw[0] = bias_load(dsec, min(p0, n_pairs - 1), ng, 0, n, kb);
-    braw[1] = bias_load(dsec, min(p0 + 1, n_pairs - 1), ng, 0, n, kb);
-    for (int op = wave; op * 64 < kSub * upr; op += 4) {
-      const int u = op * 64 + lane;
-      const int m = u / upr, ph = u - m * upr;
-      if (m < it.mc) {
-        const size_t src = static_cast<size_t>(it.row0 + m) * a.hstride + 8 * (ph ^ (m & 7));
-        dma16(h_hi + src, &hsh[op * 64 * 8]);
-        dma16(h_lo + src, &hsl[op * 64 * 8]);
-      }
+  const int hs_stride = a.hstride / 16;
+  int xu = s0 / qpu;
+  const UnitHdr hd0 = unit_hdr(a.units, xu);
+  int row0 = hd0.row0, mc = hd0.mc;
+  const int ex0 = hd0.expert;
+  int su = xu;
+  const uint8_t* sblob = expert_blob(a, ex0);
+  int sI = ex0 < 0 ? a.Is : a.I;
+  // weights of this wave's tile of quad q (pair-tile clamped to the last one)
+  auto tile_src = [&](int q, const uint4*& qb, const uint8_t*& sb, int& ncq) {
+    const int u = q / qpu;
+    const int pt = min((q - u * qpu) * 4 + q4, n_pairs - 1);
+    if (u != su) {
+      const UnitHdr hd = unit_hdr(a.units, u);
+      su = u;
+      sblob = expert_blob(a, hd.expert);
+      sI = hd.expert < 0 ? a.Is : a.I;
     }
-    __builtin_amdgcn_s_waitcnt(0);
+    ncq = sI / 64;
+    qb = reinterpret_cast<const uint4*>(sblob + blob_d_q(H, sI)) + static_cast<size_t>(pt) * ncq * 64 + lane;
+    sb = sblob + blob_d_s(H, sI, G) + (static_cast<size_t>(pt) * (sI / G) * 16 + n) * 8;
+  };
+  // stage h (hi, lo) of a unit's rows (direct-to-LDS) and fetch the sums of
+  // h over 16-column blocks; the 32-column sums are stored afterwards, so
+  // that loads issued in between stay in flight (kSub * inter / 32 <= 512:
+  // one sum per thread)
+  static_assert(kSub * (kGroupedMaxInter / 32) <= 512, "one column sum per thread");
+  auto stage_issue = [&](int r0, int mcu, int Iu, float& p0, float& p1) {
+    if (tid < kSub) urow[tid] = r0 + tid;
     __syncthreads();
-    for (int idx = tid; idx < kSub * ng; idx += 256) {
-      const int m = idx / ng, g = idx - m * ng;
-      float s = 0.0f;
-      if (m < it.mc) {
-        for (int c8 = 0; c8 < G / 8; ++c8) {
-          const int pos = unit_pos(m, g * (G / 8) + c8, upr) * 8;
-          const uint4 vh = *reinterpret_cast<const uint4*>(&hsh[pos]);
-          const uint4 vl = *reinterpret_cast<const uint4*>(&hsl[pos]);
-          const uint32_t wh[4] = {vh.x, vh.y, vh.z, vh.w}, wl[4] = {vl.x, vl.y, vl.z, vl.w};
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            s += (bf16_bits_to_f32(wh[i] & 0xFFFFu) + bf16_bits_to_f32(wl[i] & 0xFFFFu)) +
-                 (bf16_bits_to_f32(wh[i] >> 16) + bf16_bits_to_f32(wl[i] >> 16));
-        }
-      }
-      gsum[m][g] = s;
+    stage_rows(h_hi, urow, mcu, a.hstride, Iu, hsh, wave, lane);
+    stage_rows(h_lo, urow, mcu, a.hstride, Iu, hsl, wave, lane);
+    const int m = tid & (kSub - 1), j = tid >> 4;
+    p0 = p1 = 0.0f;
+    if (j < Iu / 32 && m < mcu) {
+      const float* hs = a.hsum + static_cast<size_t>(r0 + m) * hs_stride + 2 * j;
+      p0 = hs[0];
+      p1 = hs[1];
     }
-    __syncthreads();
-    f32x4_t bias[4];
-    {
-      uint4 sh, sl;
-      sum_operands(&gsum[0][0], kGroupedMaxInter / 32 + 1, ng, 0, n, kb, sh, sl);
+  };
+  auto stage_finish = [&](int Iu, float p0, float p1) {
+    const int m = tid & (kSub - 1), j = tid >> 4;
+    if (j < Iu / 32) cs[j][m] = p0 + p1;
+  };
+  int nc = sI / 64, upr = sI / 8;
+  float hp0, hp1;
+  stage_issue(row0, mc, sI, hp0, hp1);
+  asm volatile("" ::: "memory");
+  Slot sl[kDepth * kSlot];
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        uint4 bah, bal, bbh, bbl;
-        bias_operands(braw[t2], ng, 0, kb, bah, bal, bbh, bbl);
-        bias[2 * t2] = bias_mfma(sh, sl, bah, bal, f32x4_t{0, 0, 0, 0});
-        bias[2 * t2 + 1] = bias_mfma(sh, sl, bbh, bbl, f32x4_t{0, 0, 0, 0});
-      }
+  for (int hf = 0; hf < kDepth; ++hf) {
+    const uint4* qb;
+    const uint8_t* sb;
+    int ncq;
+    tile_src(min(s0 + hf, s1 - 1), qb, sb, ncq);
+#pragma unroll
+    for (int j = 0; j < kSlot; ++j) load_slot<G>(sl[hf * kSlot + j], qb, sb, min(kh + 2 * j, ncq - 1));
+  }
+  staged_barrier<kDepth * kSlot * (G == 32 ? 3 : 2)>();
+  stage_finish(nc * 64, hp0, hp1);
+  staged_barrier<kDepth * kSlot * (G == 32 ? 3 : 2)>();
+  auto process = [&](const int q, auto hfc) {
+    constexpr int hf = decltype(hfc)::value;
+    const int u = q / qpu;
+    const int pt = (q - u * qpu) * 4 + q4;
+    if (u != xu) {
+      __syncthreads();   // previous unit's readers are done
+      const UnitHdr hd = unit_hdr(a.units, u);
+      const int Iu = hd.expert < 0 ? a.Is : a.I;
+      float p0, p1;
+      stage_issue(hd.row0, hd.mc, Iu, p0, p1);
+      stage_finish(Iu, p0, p1);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      xu = u;
+      row0 = hd.row0;
+      mc = hd.mc;
+      nc = Iu / 64;
+      upr = Iu / 8;
     }
-    // the refills fetch the next item's stream (this item's again when there is none)
-    const Item it2 = decode_item(w2);
-    const uint8_t* blob2 = has_next ? item_blob(a, it2.expert) : blob;
-    const int I2 = has_next ? (it2.expert < 0 ? a.Is : a.I) : I;
-    const int p02 = has_next ? 8 * it2.block + 2 * wave : p0;
-    f32x4_t acc[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
-    f32x4_t pa = {0, 0, 0, 0}, pb = {0, 0, 0, 0};
+    const uint4* qnx;
+    const uint8_t* snx;
+    int ncn;
+    tile_src(min(q + kDepth, s1 - 1), qnx, snx, ncn);
     const uint16_t* ha0 = &hsh[(n * upr + (kb ^ (n & 7))) * 8];
     const uint16_t* ha1 = &hsh[(n * upr + ((kb + 4) ^ (n & 7))) * 8];
     const uint16_t* la0 = &hsl[(n * upr + (kb ^ (n & 7))) * 8];
     const uint16_t* la1 = &hsl[(n * upr + ((kb + 4) ^ (n & 7))) * 8];
-    const uint8_t* st0 = stile(blob, I, p0);
-    const uint8_t* st1 = stile(blob, I, p0 + 1);
+    f32x4_t accA = {0, 0, 0, 0}, accB = {0, 0, 0, 0}, biasA = {0, 0, 0, 0}, biasB = {0, 0, 0, 0};
+    // the scale of chunk j is applied after the products of chunk j + 1 are
+    // issued (matrix-core latency)
+    Prod pp;
+    Coef pk;
+    float pcs0[4], pcs1[4];
 #pragma unroll
-    for (int u = 0; u < (NJT > 0 ? NJT : kPFD); ++u) {
-      if (NJT > 0 || u < 2 * nc) {
-        const uint4 q = qn[u];
-        const uint2 sr = sn[u];
-        uint4 ba0 = word_operand<2>(q.x), ba1 = word_operand<2>(q.y);
-        uint4 bb0 = word_operand<2>(q.z), bb1 = word_operand<2>(q.w);
-        float sa = f16_bits_to_f32(sr.x & 0xFFFFu), sb = f16_bits_to_f32(sr.y & 0xFFFFu);
-        consumed(ba0, ba1, bb0, bb1, sa, sb);
-        load_chunk(blob2, I2, p02, u, qn[u], sn[u]);
-        const int t2 = u >= nc ? 1 : 0;  // which pair-tile of the wave
-        const int c = u - t2 * nc;
+    for (int j = 0; j < kSlot; ++j) {
+      const int c = kh + 2 * j;
+      Slot& s = sl[hf * kSlot + j];
+      const Decoded d = decode_slot<G>(s);
+      load_slot<G>(s, qnx, snx, min(c, ncn - 1));
+      Prod p;
+      float cs0[4], cs1[4];
+      if (c < nc) {
         const uint4 h0 = *reinterpret_cast<const uint4*>(ha0 + 64 * c);
         const uint4 h1 = *reinterpret_cast<const uint4*>(ha1 + 64 * c);
         const uint4 l0 = *reinterpret_cast<const uint4*>(la0 + 64 * c);
         const uint4 l1 = *reinterpret_cast<const uint4*>(la1 + 64 * c);
-        f32x4_t ra, rb;  // scaled products of this chunk (or chunk pair)
-        bool flush = true;
+        const float4 c0 = *reinterpret_cast<const float4*>(&cs[2 * c][4 * kb]);
+        const float4 c1 = *reinterpret_cast<const float4*>(&cs[2 * c + 1][4 * kb]);
         if constexpr (G == 32) {
-          const uint2 sr1 = *reinterpret_cast<const uint2*>((t2 ? st1 : st0) + static_cast<size_t>(2 * c + 1) * 128);
-          const float sa1 = f16_bits_to_f32(sr1.x & 0xFFFFu), sb1 = f16_bits_to_f32(sr1.y & 0xFFFFu);
-          const f32x4_t z = {0, 0, 0, 0};
-          const f32x4_t x0 = mfma<2>(l0, ba0, mfma<2>(h0, ba0, z));
-          const f32x4_t y0 = mfma<2>(l0, bb0, mfma<2>(h0, bb0, z));
-          const f32x4_t x1 = mfma<2>(l1, ba1, mfma<2>(h1, ba1, z));
-          const f32x4_t y1 = mfma<2>(l1, bb1, mfma<2>(h1, bb1, z));
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            ra[i] = fmaf(sa1, x1[i], sa * x0[i]);
-            rb[i] = fmaf(sb1, y1[i], sb * y0[i]);
-          }
+          cs0[0] = c0.x; cs0[1] = c0.y; cs0[2] = c0.z; cs0[3] = c0.w;
+          cs1[0] = c1.x; cs1[1] = c1.y; cs1[2] = c1.z; cs1[3] = c1.w;
         } else {
-          pa = mfma<2>(h0, ba0, pa);
-          pa = mfma<2>(l0, ba0, pa);
-          pb = mfma<2>(h0, bb0, pb);
-          pb = mfma<2>(l0, bb0, pb);
-          pa = mfma<2>(h1, ba1, pa);
-          pa = mfma<2>(l1, ba1, pa);
-          pb = mfma<2>(h1, bb1, pb);
-          pb = mfma<2>(l1, bb1, pb);
-          // G = 128 spans chunks c, c + 1 (nc is even then, so c and u agree in parity)
-          flush = G == 64 || (u & 1);
-          ra = pa;
-          rb = pb;
+          cs0[0] = c0.x + c1.x; cs0[1] = c0.y + c1.y; cs0[2] = c0.z + c1.z; cs0[3] = c0.w + c1.w;
+          cs1[0] = cs0[0]; cs1[1] = cs0[1]; cs1[2] = cs0[2]; cs1[3] = cs0[3];
         }
-        if (flush) {
-          if (NJT > 0) {
+        p = chunk_mfma<G, true>(d, h0, h1, l0, l1);
+      }
+      if (j > 0 && c - 2 < nc) chunk_scale<G>(pp, pk, pcs0, pcs1, accA, accB, biasA, biasB);
+      pp = p;
+      pk = coef_of(d);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              acc[2 * t2][i] = G == 32 ? acc[2 * t2][i] + ra[i] : fmaf(sa, ra[i], acc[2 * t2][i]);
-              acc[2 * t2 + 1][i] = G == 32 ? acc[2 * t2 + 1][i] + rb[i] : fmaf(sb, rb[i], acc[2 * t2 + 1][i]);
-            }
-          } else {
-            // tile chosen at run time: update both accumulator pairs by select
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float na = G == 32 ? (t2 ? acc[2][i] : acc[0][i]) + ra[i]
-                                       : fmaf(sa, ra[i], t2 ? acc[2][i] : acc[0][i]);
-              const float nb = G == 32 ? (t2 ? acc[3][i] : acc[1][i]) + rb[i]
-                                       : fmaf(sb, rb[i], t2 ? acc[3][i] : acc[1][i]);
-              acc[0][i] = t2 ? acc[0][i] : na;
-              acc[2][i] = t2 ? na : acc[2][i];
-              acc[1][i] = t2 ? acc[1][i] : nb;
-              acc[3][i] = t2 ? nb : acc[3][i];
-            }
-          }
-          // pin the scaling here: otherwise every chunk's products stay live
-          // in their own registers until the end of the stream
-          asm volatile("" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]));
-          pa = f32x4_t{0, 0, 0, 0};
-          pb = f32x4_t{0, 0, 0, 0};
-        }
-        // keep each chunk's LDS reads next to its products (hoisting all of
-        // them costs more registers than the latency they would hide)
-        __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < 4; ++i) {
+        pcs0[i] = cs0[i];
+        pcs1[i] = cs1[i];
       }
     }
+    if (kh + 2 * (kSlot - 1) < nc) chunk_scale<G>(pp, pk, pcs0, pcs1, accA, accB, biasA, biasB);
+    (void)kHalves;
+    constexpr int rb = hf & 1;
+    if (kh == 1) {
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
-      if (t2 == 0 ? v0 : v1) {
+      for (int i = 0; i < 4; ++i) {
+        red[rb][q4][i][lane] = fmaf(kQScale, accA[i], biasA[i]);
+        red[rb][q4][4 + i][lane] = fmaf(kQScale, accB[i], biasB[i]);
+      }
+    }
+    __syncthreads();
+    if (kh == 0 && pt < n_pairs) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = 4 * kb + i;
-          if (m < it.mc) {
-            float* yr = a.yrow + static_cast<size_t>(it.row0 + m) * H + 32 * (p0 + t2);
-            yr[n] = fmaf(16.0f, acc[2 * t2][i], bias[2 * t2][i]);
-            yr[16 + n] = fmaf(16.0f, acc[2 * t2 + 1][i], bias[2 * t2 + 1][i]);
-          }
+      for (int i = 0; i < 4; ++i) {
+        const int m = 4 * kb + i;
+        if (m < mc) {
+          float* yr = a.yrow + static_cast<size_t>(row0 + m) * H + 32 * pt;
+          yr[n] = fmaf(kQScale, accA[i], biasA[i]) + red[rb][q4][i][lane];
+          yr[16 + n] = fmaf(kQScale, accB[i], biasB[i]) + red[rb][q4][4 + i][lane];
         }
       }
     }
-    if (!has_next) break;
-    wi = wi2;
-    it = it2;
-    blob = blob2;
-    I = I2;
-    p0 = p02;
+  };
+  int sb0 = s0;
+  for (; sb0 + kDepth <= s1; sb0 += kDepth) {
+    process(sb0, Half<0>{});
+    process(sb0 + 1, Half<1>{});
+    if constexpr (kDepth == 4) {
+      process(sb0 + 2, Half<2>{});
+      process(sb0 + 3, Half<3>{});
+    }
+  }
+  if (sb0 < s1) process(sb0, Half<0>{});
+  if constexpr (kDepth == 4) {
+    if (sb0 + 1 < s1) process(sb0 + 1, Half<1>{});
+    if (sb0 + 2 < s1) process(sb0 + 2, Half<2>{});
   }
 }
 
-static int grid_cap(int upper, int cap) { return upper < cap ? (upper > 0 ? upper : 1) : cap; }
-
 hipError_t launch_gateup_grouped(int act, const FfnArgs& a, hipStream_t s) {
-  const int grid = grid_cap(work_upper(a.I / 64, a.Is / 64, a.T, a.K, a.E), kGridGU);
-#define GU_LAUNCH(A_, G_)                                                                   \
-  do {                                                                                      \
-    if (a.H == 2048) hipLaunchKernelGGL((k_gateup_grouped<A_, G_, 32>), dim3(grid), dim3(256), 0, s, a); \
-    else hipLaunchKernelGGL((k_gateup_grouped<A_, G_, 0>), dim3(grid), dim3(256), 0, s, a);           \
-  } while (0)
+#define GU_LAUNCH(A_, G_) hipLaunchKernelGGL((k_gateup_tiles<A_, G_>), dim3(kGridTiles), dim3(512), 0, s, a)
   if (act == 2) {
     if (a.G == 32) GU_LAUNCH(2, 32);
     else if (a.G == 64) GU_LAUNCH(2, 64);
@@ -611,18 +774,9 @@ hipError_t launch_gateup_grouped(int act, const FfnArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_down_grouped(const FfnArgs& a, hipStream_t s) {
-  const int nb = (a.H + kDownBlockRows - 1) / kDownBlockRows;
-  const int grid = grid_cap(work_upper(nb, a.Is > 0 ? nb : 0, a.T, a.K, a.E), kGridD);
-  const bool i512 = a.I == 512 && (a.Is == 0 || a.Is == 512);
-#define D_LAUNCH(G_)                                                                     \
-  do {                                                                                   \
-    if (i512) hipLaunchKernelGGL((k_down_grouped<G_, kPFD>), dim3(grid), dim3(256), 0, s, a); \
-    else hipLaunchKernelGGL((k_down_grouped<G_, 0>), dim3(grid), dim3(256), 0, s, a);        \
-  } while (0)
-  if (a.G == 32) D_LAUNCH(32);
-  else if (a.G == 64) D_LAUNCH(64);
-  else D_LAUNCH(128);
-#undef D_LAUNCH
+  if (a.G == 32) hipLaunchKernelGGL((k_down_tiles<32>), dim3(kGridTiles), dim3(512), 0, s, a);
+  else if (a.G == 64) hipLaunchKernelGGL((k_down_tiles<64>), dim3(kGridTiles), dim3(512), 0, s, a);
+  else hipLaunchKernelGGL((k_down_tiles<128>), dim3(kGridTiles), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

@@ -140,54 +140,17 @@ __device__ __forceinline__ int block_incl_scan_1024(int v, int* lds16, int& tota
 // expert is: rows of earlier 1024-row chunks (a running count), plus rows of
 // earlier waves of this chunk (per-wave counts in LDS), plus earlier lanes of
 // its own wave (ballot of the lanes holding the same expert).  Rows of one
-// expert therefore keep their (t, k) order.  Also lists the active experts,
-// most tokens first (the work order of the grouped kernels; the order among
-// experts with equal counts is unspecified and affects scheduling only), and
-// their count.
-__device__ __forceinline__ int4 work_item(int row0, int mc, int block, int expert) {
-  return make_int4(row0, mc | (block << 8), expert, 0);
-}
-
-// Writes one work list (see WorkLists): the shared expert's units first, then
-// the routed experts in active[] order.  Thread a < n_act owns routed position a.
-__device__ void build_work_list(int4* __restrict__ list, int32_t* __restrict__ count, int nb, int nb_s, int T,
-                                int TK, int n_act, int a_rows0, int a_rows, int a_expert, int* scan_tmp) {
-  const int tid = threadIdx.x;
-  const bool col = (nb % 8 == 0) && (nb_s % 8 == 0);
-  const int S_T = (T + kSubTokens - 1) / kSubTokens;
-  const int shared_pos = nb_s > 0 ? (col ? S_T * (nb_s / 8) : S_T * nb_s) : 0;
-  const int Sa = (tid < n_act) ? (a_rows + kSubTokens - 1) / kSubTokens : 0;
-  const int wa = col ? Sa * (nb / 8) : Sa * nb;
-  int total = 0;
-  const int Qa = block_incl_scan_1024(wa, scan_tmp, total) - wa;
-  // shared units: items (block b, sub s)
-  for (int k = tid; k < nb_s * S_T; k += 1024) {
-    const int b = k / S_T, sub = k - b * S_T;
-    const int idx = col ? 8 * ((b / 8) * S_T + sub) + (b % 8) : b * S_T + sub;
-    list[idx] = work_item(TK + kSubTokens * sub, min(kSubTokens, T - kSubTokens * sub), b, -1);
-  }
-  if (tid < n_act) {
-    for (int b = 0; b < nb; ++b) {
-      for (int sub = 0; sub < Sa; ++sub) {
-        const int pos = shared_pos + Qa + (col ? (b / 8) * Sa + sub : b * Sa + sub);
-        const int idx = col ? 8 * pos + (b % 8) : pos;
-        list[idx] = work_item(a_rows0 + kSubTokens * sub, min(kSubTokens, a_rows - kSubTokens * sub), b, a_expert);
-      }
-    }
-  }
-  if (tid == 0) count[0] = col ? 8 * (shared_pos + total) : shared_pos + total;
-}
-
+// expert therefore keep their (t, k) order.  With a unit plan it also writes
+// the unit records of the grouped family (see UnitPlan): the unit of a row is
+// ubase[e] + rank / 16, where ubase is a prefix sum of ceil(count / 16).
 __global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ topk_idx, int n, int E,
                                                   int32_t* __restrict__ expert_off, int32_t* __restrict__ perm,
-                                                  int32_t* __restrict__ inv, int32_t* __restrict__ active,
-                                                  int32_t* __restrict__ n_active, WorkLists wl) {
+                                                  int32_t* __restrict__ inv, UnitPlan plan) {
   __shared__ int cnt[kMaxExperts];
   __shared__ int start[kMaxExperts];
   __shared__ int run[kMaxExperts];
+  __shared__ int ubase[kMaxExperts];
   __shared__ unsigned short wcnt[16][kMaxExperts];
-  __shared__ int cbin[1024];
-  __shared__ int lpt[kMaxExperts];
   __shared__ int scan_tmp[16];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -195,38 +158,34 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ to
     cnt[tid] = 0;
     run[tid] = 0;
   }
-  cbin[tid] = 0;
   __syncthreads();
   for (int i = tid; i < n; i += 1024) atomicAdd(&cnt[topk_idx[i]], 1);
   __syncthreads();
   const int c = (tid < E) ? cnt[tid] : 0;
   int total = 0;
   const int incl = block_incl_scan_1024(c, scan_tmp, total);
-  int n_act_total = 0;
-  const int a_incl = block_incl_scan_1024((tid < E && c > 0) ? 1 : 0, scan_tmp, n_act_total);
-  (void)a_incl;
   if (tid < E) {
     start[tid] = incl - c;
     expert_off[tid] = incl - c;
   }
-  if (tid == 0) {
-    expert_off[E] = total;
-    n_active[0] = n_act_total;
-  }
-  // active experts by descending count: bucket by count (clamped), scan the
-  // buckets from the largest count down, place with LDS atomics
-  const int ckey = min(c, 1023);
-  if (tid < E && c > 0) atomicAdd(&cbin[ckey], 1);
-  __syncthreads();
-  const int hv = cbin[1023 - tid];
-  int dummy = 0;
-  const int hincl = block_incl_scan_1024(hv, scan_tmp, dummy);
-  cbin[1023 - tid] = hincl - hv;
-  __syncthreads();
-  if (tid < E && c > 0) {
-    const int ap = atomicAdd(&cbin[ckey], 1);
-    active[ap] = tid;
-    lpt[ap] = tid;
+  if (tid == 0) expert_off[E] = total;
+  const int n_su = (plan.units != nullptr && plan.shared) ? (plan.T + kSubTokens - 1) / kSubTokens : 0;
+  int n_ru = 0;
+  if (plan.units != nullptr) {
+    const int nu = (c + kSubTokens - 1) / kSubTokens;
+    const int uincl = block_incl_scan_1024(nu, scan_tmp, n_ru);
+    if (tid < E) ubase[tid] = n_su + uincl - nu;
+    if (tid == 0) {
+      plan.n_units[0] = n_su;
+      plan.n_units[1] = n_ru;
+    }
+    // the shared expert's units: every token, in order
+    for (int u = tid; u < n_su; u += 1024) {
+      int32_t* rec = plan.units + static_cast<size_t>(u) * kUnitInts;
+      const int mc = min(kSubTokens, plan.T - kSubTokens * u);
+      *reinterpret_cast<int4*>(rec) = make_int4(n + kSubTokens * u, mc, -1, 0);
+      for (int m = 0; m < mc; ++m) rec[4 + m] = kSubTokens * u + m;
+    }
   }
   for (int base = 0; base < n; base += 1024) {
     const int i = base + tid;
@@ -236,7 +195,7 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ to
     unsigned long long todo = __ballot(valid);
     while (todo) {
       const int leader = __ffsll(static_cast<long long>(todo)) - 1;
-      const int le = __shfl(e, leader, kWave);
+      const int le = __builtin_amdgcn_readlane(e, leader);
       const unsigned long long m = __ballot(valid && e == le);
       if (valid && e == le) peers = m;
       todo &= ~m;
@@ -250,28 +209,19 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ to
     if (valid) {
       int before = 0;
       for (int w = 0; w < wave; ++w) before += wcnt[w][e];
-      const int pos = start[e] + run[e] + before + rank;
+      const int r = run[e] + before + rank;   // rank among all rows of expert e
+      const int pos = start[e] + r;
       perm[pos] = i;
       if (inv != nullptr) inv[i] = pos;
-      if (wl.tok_sorted != nullptr) wl.tok_sorted[pos] = i / wl.K;
+      if (plan.units != nullptr) {
+        int32_t* rec = plan.units + static_cast<size_t>(ubase[e] + r / kSubTokens) * kUnitInts;
+        rec[4 + r % kSubTokens] = i / plan.K;
+        if (r % kSubTokens == 0) *reinterpret_cast<int4*>(rec) = make_int4(pos, min(kSubTokens, cnt[e] - r), e, 0);
+      }
     }
     __syncthreads();
     if (first_peer) atomicAdd(&run[e], __popcll(peers));
     __syncthreads();
-  }
-  if (wl.work_gu != nullptr) {
-    // active[] (written above with atomics) -> this thread's routed position
-    __syncthreads();
-    int a_expert = -1, a_rows0 = 0, a_rows = 0;
-    if (tid < n_act_total) {
-      a_expert = lpt[tid];
-      a_rows0 = start[a_expert];
-      a_rows = cnt[a_expert];
-    }
-    build_work_list(wl.work_gu, wl.n_work, wl.nb_gu, wl.nb_gu_s, wl.T, n, n_act_total, a_rows0, a_rows, a_expert,
-                    scan_tmp);
-    build_work_list(wl.work_d, wl.n_work + 1, wl.nb_d, wl.nb_d_s, wl.T, n, n_act_total, a_rows0, a_rows, a_expert,
-                    scan_tmp);
   }
 }
 
@@ -366,10 +316,10 @@ hipError_t launch_topk(const float* logits, int T, int E, int K, int32_t* idx, f
 }
 
 hipError_t launch_permute(const int32_t* idx, int n, int E, int32_t* off, int32_t* perm, int32_t* inv,
-                          int32_t* active, int32_t* n_active, const WorkLists* wl, hipStream_t s) {
-  WorkLists w{};
-  if (wl != nullptr) w = *wl;
-  hipLaunchKernelGGL(k_permute, dim3(1), dim3(1024), 0, s, idx, n, E, off, perm, inv, active, n_active, w);
+                          const UnitPlan* plan, hipStream_t s) {
+  UnitPlan p{};
+  if (plan != nullptr) p = *plan;
+  hipLaunchKernelGGL(k_permute, dim3(1), dim3(1024), 0, s, idx, n, E, off, perm, inv, p);
   return hipGetLastError();
 }
 
