@@ -160,7 +160,9 @@ moe_status moe_route(const moe_layer_desc* desc, const moe_layer_weights* w, con
  * counting sort of the T*K routed rows by expert.  Outputs (device):
  * expert_off [E+1] int32 exclusive prefix sums of per-expert counts;
  * perm [T*K] int32, perm[r] = t*K + k of the r-th row in (expert, t, k)
- * order; inv_or_null [T*K] int32 the inverse permutation. */
+ * order; inv_or_null [T*K] int32 the inverse permutation.  A row whose
+ * expert index lies outside [0, E) is dropped: it is not counted, perm holds
+ * only the expert_off[E] placed rows, and its inv entry is -1. */
 moe_status moe_permute(const moe_layer_desc* desc, const int32_t* topk_idx, int32_t n_tokens,
                        int32_t* expert_off, int32_t* perm, int32_t* inv_or_null,
                        void* ws, size_t ws_bytes, moe_stream stream);

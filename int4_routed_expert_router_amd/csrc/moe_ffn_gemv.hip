@@ -240,10 +240,11 @@ __global__ __launch_bounds__(512) void k_combine(const float* __restrict__ yrow,
         float4 v[kB];
 #pragma unroll
         for (int b = 0; b < kB; ++b)
-          if (k0 + b < ns) v[b] = reinterpret_cast<const float4*>(yrow + static_cast<size_t>(src[k0 + b]) * H)[c4];
+          if (k0 + b < ns && src[k0 + b] >= 0)
+            v[b] = reinterpret_cast<const float4*>(yrow + static_cast<size_t>(src[k0 + b]) * H)[c4];
 #pragma unroll
         for (int b = 0; b < kB; ++b) {
-          if (k0 + b < ns) {
+          if (k0 + b < ns && src[k0 + b] >= 0) {   // a dropped row (src -1) adds nothing
             const float wk = wt[k0 + b];
             acc.x = fmaf(wk, v[b].x, acc.x);
             acc.y = fmaf(wk, v[b].y, acc.y);

@@ -75,7 +75,9 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
   for (int j = 0; j < kJ; ++j) {
     const int e = lane + 64 * j;
     if (e < E) {
-      v[j] = z[e];
+      // NaN orders as -inf, so a selection always exists (indices stay in [0, E))
+      const float zv = z[e];
+      v[j] = zv == zv ? zv : -INFINITY;
       avail |= 1u << j;
     } else {
       v[j] = 0.0f;
@@ -159,7 +161,12 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ to
     run[tid] = 0;
   }
   __syncthreads();
-  for (int i = tid; i < n; i += 1024) atomicAdd(&cnt[topk_idx[i]], 1);
+  // rows whose expert index lies outside [0, E) are dropped: not counted,
+  // not placed (inv = -1), so they contribute nothing
+  for (int i = tid; i < n; i += 1024) {
+    const int e = topk_idx[i];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  }
   __syncthreads();
   const int c = (tid < E) ? cnt[tid] : 0;
   int total = 0;
@@ -189,8 +196,10 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ to
   }
   for (int base = 0; base < n; base += 1024) {
     const int i = base + tid;
-    const bool valid = i < n;
-    const int e = valid ? topk_idx[i] : -1;
+    const int ei = i < n ? topk_idx[i] : -1;
+    const bool valid = ei >= 0 && ei < E;
+    const int e = valid ? ei : -1;
+    if (i < n && !valid && inv != nullptr) inv[i] = -1;
     unsigned long long peers = 0;
     unsigned long long todo = __ballot(valid);
     while (todo) {
