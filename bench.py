@@ -40,7 +40,52 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy three times (scale reference for HBM byte counters)")
     return ap.parse_args()
+
+
+COPY_BYTES = 1 << 30
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gateup_bat80.txt")
+GROUPED_SRC = os.path.join(ROOT, "int4_routed_expert_router_amd", "csrc", "moe_ffn_grouped.hip")
+
+
+def copy_calibration():
+    """A plain device-to-device copy of COPY_BYTES, three times: under
+    rocprofv3 --pmc its FETCH_SIZE / WRITE_SIZE per dispatch give the factor
+    that turns those counters into bytes."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_dispatch": COPY_BYTES, "dispatches": 3}))
+
+
+def measured_traffic():
+    """HBM bytes per gate/up launch from the committed counter summary, or
+    None when the kernel source changed since the counters were taken."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    vals = {}
+    for line in text.splitlines():
+        if line.startswith("- ") and ":" in line:
+            k, v = line[2:].split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    src_hash = hashlib.sha256(open(GROUPED_SRC, "rb").read()).hexdigest()
+    if vals.get("kernel_source_sha256") != src_hash:
+        return None
+    try:
+        fetch = float(vals["fetch_kib_per_launch"]) * 1024 * float(vals["copy_fetch_bytes_per_kib"]) / 1024
+        write = float(vals["write_kib_per_launch"]) * 1024 * float(vals["copy_write_bytes_per_kib"]) / 1024
+    except (KeyError, ValueError):
+        return None
+    return fetch + write
 
 
 class Stack:
@@ -153,6 +198,9 @@ def cpu_baseline(wl, budget_s):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(json.dumps({"error": f"--gpus {args.gpus}: this benchmark runs on exactly one GPU; "
                                    "multi-GPU sharding is designed (DESIGN.md) but not built"}))
@@ -219,11 +267,15 @@ def main():
         gu_bytes = (st.desc.inter * st.desc.hidden + 8 * st.desc.inter * st.desc.hidden // st.desc.group_size)
         per_launch = float(np.mean([(a + 1) * gu_bytes for a in act]))
         achieved = per_launch / (avg_us * 1e-6) / 1e9
+        grouped = args.path == 2 or (args.path == 0 and wl.tokens * wl.top_k > 32)
+        tb = measured_traffic() if (grouped and args.workload == "bat80") else None
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "k_gateup_grouped (int4 gate/up + SwiGLU)" if (args.path == 2 or (
-                    args.path == 0 and wl.tokens * wl.top_k > 32)) else "k_gateup_gemv (int4 gate/up + SwiGLU)",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None if tb is None else round(tb / (avg_us * 1e-6) / 1e9, 1),
+                "kernel": "k_gateup_tiles (int4 gate/up + SwiGLU)" if grouped else
+                          "k_gateup_gemv (int4 gate/up + SwiGLU)",
                 "avg_us": round(avg_us, 2), "bytes_per_launch": int(per_launch),
+                "traffic_bytes_per_launch": None if tb is None else int(tb),
                 "events": "HIP events on the launch stream around each layer's gate/up kernel, eager replay"}
         print(f"[bench] kernel avg us: " + ", ".join(f"{k} {v:.2f}" for k, v in kernel_us.items())
               + f"; gate/up {achieved:.0f} GB/s", file=sys.stderr, flush=True)
@@ -244,7 +296,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 activations, int4 weights, fp32 accumulate",
+        "dtype": "f16" if (args.path == 2 or (args.path == 0 and wl.tokens * wl.top_k > 32)) else wl.act_dtype,
+        "precision": "int4 weights as exact f16 matrix-core operands, activations f16, fp32 accumulate"
+                     if (args.path == 2 or (args.path == 0 and wl.tokens * wl.top_k > 32)) else
+                     "int4 weights, bf16/f16 dot2 products, fp32 accumulate",
         "data": "synthetic (seeded; random-init weights of the stated shapes)",
         "int4_expert_GBps": round(int4_gbs, 1),
         "int4_frac_of_hbm_peak": round(int4_gbs / HBM_PEAK_GBS, 4),
