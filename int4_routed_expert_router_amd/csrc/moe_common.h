@@ -73,6 +73,9 @@ __device__ __forceinline__ float wave_max(float v) {
     return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
   }));
 }
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  return wave_allreduce_u32(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
   return wave_allreduce_u32(v, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
 }

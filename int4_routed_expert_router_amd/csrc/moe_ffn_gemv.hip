@@ -215,16 +215,28 @@ __global__ __launch_bounds__(512) void k_combine(const float* __restrict__ yrow,
   __shared__ int src[kMaxTopK + 1];
   __shared__ float wt[kMaxTopK + 1];
   const int t = blockIdx.x, tid = threadIdx.x;
-  if (tid < K) {
-    src[tid] = inv ? inv[t * K + tid] : t * K + tid;
-    wt[tid] = w[t * K + tid];
-  }
-  if (tid == K && has_shared) {
-    src[K] = T * K + t;
-    wt[K] = gamma[t];
+  __shared__ int n_src;
+  if (tid == 0) {
+    // sources in rank order, then the shared expert; a dropped row (inv -1)
+    // adds nothing and is left out
+    int ns = 0;
+    for (int k = 0; k < K; ++k) {
+      const int sr = inv ? inv[t * K + k] : t * K + k;
+      if (sr >= 0) {
+        src[ns] = sr;
+        wt[ns] = w[t * K + k];
+        ++ns;
+      }
+    }
+    if (has_shared) {
+      src[ns] = T * K + t;
+      wt[ns] = gamma[t];
+      ++ns;
+    }
+    n_src = ns;
   }
   __syncthreads();
-  const int ns = K + (has_shared ? 1 : 0);
+  const int ns = n_src;
   const int H4 = H / 4;
   constexpr int kPer = kMaxH / 4 / 512;
   constexpr int kB = 16;
@@ -240,11 +252,10 @@ __global__ __launch_bounds__(512) void k_combine(const float* __restrict__ yrow,
         float4 v[kB];
 #pragma unroll
         for (int b = 0; b < kB; ++b)
-          if (k0 + b < ns && src[k0 + b] >= 0)
-            v[b] = reinterpret_cast<const float4*>(yrow + static_cast<size_t>(src[k0 + b]) * H)[c4];
+          if (k0 + b < ns) v[b] = reinterpret_cast<const float4*>(yrow + static_cast<size_t>(src[k0 + b]) * H)[c4];
 #pragma unroll
         for (int b = 0; b < kB; ++b) {
-          if (k0 + b < ns && src[k0 + b] >= 0) {   // a dropped row (src -1) adds nothing
+          if (k0 + b < ns) {
             const float wk = wt[k0 + b];
             acc.x = fmaf(wk, v[b].x, acc.x);
             acc.y = fmaf(wk, v[b].y, acc.y);

@@ -330,9 +330,6 @@ __global__ __launch_bounds__(512) void k_gateup_tiles(FfnArgs a) {
   // minimum two LDS cycles.
   constexpr int kRowStride = 80;
   __shared__ float red[2][2][kWaves][2][4][kRowStride];
-  // A operands of the current unit's activations, per wave: chunk j, half,
-  // lane (16 bytes; only this wave reads them)
-  __shared__ uint4 xop[kWaves][kSlot][2][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, kb = lane >> 4;
   const int H = a.H, nc = H / 64, ng = H / G;
@@ -363,6 +360,7 @@ __global__ __launch_bounds__(512) void k_gateup_tiles(FfnArgs a) {
   };
   // ---- activations: raw prefetch (xr) of unit pu, operands (xa) of unit xu
   uint4 xr[kSlot][2];   // raw activations of the prefetched unit
+  uint4 xa[kSlot][2];   // A operands of the current unit (this wave's chunks)
   float csv[kSlot][kHalves][4];   // column sums for the lane's output rows 4kb..4kb+3
   int pu = -1, prow0 = 0, pmc = 0;
   int xu = -1, row0 = 0, mc = 0;
@@ -386,14 +384,14 @@ __global__ __launch_bounds__(512) void k_gateup_tiles(FfnArgs a) {
     prow0 = r0;
     pmc = m_c;
   };
-  // xr -> A operands (this wave's LDS area) and the column sums (32-column
-  // halves) for the C layout rows
+  // xr -> A operands and the column sums (32-column halves) for the C
+  // layout rows
   auto take_x = [&]() {
 #pragma unroll
     for (int j = 0; j < kSlot; ++j) {
       float s0 = 0.0f, s1 = 0.0f;
-      xop[wave][j][0][lane] = act_operand<ACT>(xr[j][0], s0);
-      xop[wave][j][1][lane] = act_operand<ACT>(xr[j][1], s1);
+      xa[j][0] = act_operand<ACT>(xr[j][0], s0);
+      xa[j][1] = act_operand<ACT>(xr[j][1], s1);
       float hs[kHalves];
       if constexpr (G == 32) {
         hs[0] = s0;
@@ -496,10 +494,7 @@ __global__ __launch_bounds__(512) void k_gateup_tiles(FfnArgs a) {
       const Decoded d = decode_slot<G>(s);
       load_slot<G>(s, qnx, snx, min(c, nc - 1));
       Prod p;
-      if (c < nc) {
-        const uint4 a0 = xop[wave][j][0][lane], a1 = xop[wave][j][1][lane];
-        p = chunk_mfma<G, false>(d, a0, a1, a0, a1);
-      }
+      if (c < nc) p = chunk_mfma<G, false>(d, xa[j][0], xa[j][1], xa[j][0], xa[j][1]);
       if (j > 0 && c - kWaves < nc) chunk_scale<G>(pp, pk, csv[j - 1][0], csv[j - 1][kHalves - 1], accA, accB, biasA, biasB);
       pp = p;
       pk = coef_of(d);
@@ -527,7 +522,9 @@ __global__ __launch_bounds__(512) void k_gateup_tiles(FfnArgs a) {
         ga += red[pb][tt][w][0][e][src];
         up += red[pb][tt][w][1][e][src];
       }
-      const float hv = ga / (1.0f + expf(-ga)) * up;
+      // silu(g) * u with the hardware exp2 and reciprocal (relative error a
+      // few ulp, far inside the block's tolerance)
+      const float hv = ga * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * ga)) * up;
       // operand-ready fp16 hi + lo of h * f, f = 1/16 on the columns the down
       // projection's B operand carries as q * 2^-20 (column 16 pt + nn)
       const bool sc = (nn & 2) != 0;

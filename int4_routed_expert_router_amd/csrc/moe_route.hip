@@ -56,11 +56,46 @@ __global__ __launch_bounds__(64) void k_router_logits(const uint16_t* __restrict
   }
 }
 
-// One wave per token: K rounds of a wave-wide arg-max over E/64 values per
-// lane (lane l holds experts l, l+64, ...).  Each round takes the wave maximum
-// of the lanes' best remaining logits, then the lowest expert index among the
-// lanes holding that maximum, so ties resolve to the lower expert index.  Both
-// reductions run on DPP/row-swap permutes (no LDS round trips).
+// Order-preserving map of a float onto uint32 (larger float, larger key).
+// NaN is read as -inf (maxNum drops it), so a selection always exists, and
+// -0 as +0, so the two zeros tie as they do under float comparison.  The key
+// of -inf is 0x007FFFFF; key 0 is left free to mark "no entry".
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(fmaxf(f, -INFINITY) + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Batcher's odd-even merge sorting network over N (a power of two) entries
+// held in registers: cas(a, b) with a < b must leave the pair in order.  All
+// loop bounds are compile-time constants, so the network unrolls into
+// straight-line code on constant register indices.
+template <int N, class Cas>
+__device__ __forceinline__ void oddeven_merge_sort(Cas cas) {
+#pragma unroll
+  for (int p = 1; p < N; p <<= 1) {
+#pragma unroll
+    for (int k = p; k >= 1; k >>= 1) {
+#pragma unroll
+      for (int j = k % p; j + k < N; j += 2 * k) {
+#pragma unroll
+        for (int i = 0; i < k; ++i) {
+          if (i + j + k < N && (i + j) / (2 * p) == (i + j + k) / (2 * p)) cas(i + j, i + j + k);
+        }
+      }
+    }
+  }
+}
+
+// One wave per token; lane l holds experts l, l+64, ... (kJ of them).  Each
+// lane first sorts its own entries by (logit desc, expert index asc), as a
+// 64-bit key (order_key(logit), kJ-1-j).  Then K rounds: the wave maximum of
+// the lanes' head keys picks the logit; among the lanes whose head holds it
+// (one, unless logits tie across lanes) the lowest expert index wins, and
+// the winning lane pops its head.  So ties resolve to the lower expert index.
+template <int kJ>
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int T, int E, int K,
                                               int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
                                               float* __restrict__ gamma) {
@@ -68,72 +103,108 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const float* z = logits + static_cast<size_t>(t) * (E + 1);
-  constexpr int kJ = kMaxExperts / 64;
-  float v[kJ];
-  uint32_t avail = 0;
+  float raw[kJ];
+  // every load is issued before any is used; the index is clamped to E (the
+  // shared-gate column), which is always valid memory
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) raw[j] = z[min(lane + 64 * j, E)];
+  float zg = z[E];
+  asm volatile("" : "+v"(zg));
+  // opaque to the optimiser, so no load is sunk into the validity branch
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) asm volatile("" : "+v"(raw[j]));
+  uint32_t hi[kJ], lo[kJ];
 #pragma unroll
   for (int j = 0; j < kJ; ++j) {
-    const int e = lane + 64 * j;
-    if (e < E) {
-      // NaN orders as -inf, so a selection always exists (indices stay in [0, E))
-      const float zv = z[e];
-      v[j] = zv == zv ? zv : -INFINITY;
-      avail |= 1u << j;
-    } else {
-      v[j] = 0.0f;
-    }
+    hi[j] = (lane + 64 * j < E) ? order_key(raw[j]) : 0u;
+    lo[j] = kJ - 1 - j;
   }
-  float my_v = 0.0f, v0 = 0.0f;
+  oddeven_merge_sort<kJ>([&](int a, int b) {
+    const bool swap = hi[b] > hi[a] || (hi[b] == hi[a] && lo[b] > lo[a]);
+    const uint32_t ha = hi[a], la = lo[a];
+    hi[a] = swap ? hi[b] : ha;
+    lo[a] = swap ? lo[b] : la;
+    hi[b] = swap ? ha : hi[b];
+    lo[b] = swap ? la : lo[b];
+  });
+  uint32_t my_key = 0, key0 = 0;
   int my_i = 0;
   for (int k = 0; k < K; ++k) {
-    float bv = -INFINITY;
-    int bj = -1;
-#pragma unroll
-    for (int j = 0; j < kJ; ++j) {
-      // j ascending = index ascending, so a strict '>' keeps the lower index on ties
-      if (((avail >> j) & 1u) && (bj < 0 || v[j] > bv)) {
-        bv = v[j];
-        bj = j;
-      }
+    // K <= E, so some lane still holds an entry and m > 0
+    const uint32_t m = wave_max_u32(hi[0]);
+    const unsigned long long cand = __ballot(hi[0] == m);
+    int wl;
+    if (__popcll(cand) == 1) {
+      wl = __ffsll(cand) - 1;
+    } else {
+      const uint32_t idx = (hi[0] == m) ? (kJ - 1 - lo[0]) * 64u + static_cast<uint32_t>(lane) : 0xFFFFFFFFu;
+      wl = __builtin_amdgcn_readfirstlane(static_cast<int>(wave_min_u32(idx) & 63u));
     }
-    const float m = wave_max(bv);
-    const uint32_t key = (bj >= 0 && bv == m) ? static_cast<uint32_t>(lane + 64 * bj) : 0xFFFFFFFFu;
-    const int e = static_cast<int>(wave_min_u32(key));
-    if (k == 0) v0 = m;
+    const int e = (kJ - 1 - __builtin_amdgcn_readlane(static_cast<int>(lo[0]), wl)) * 64 + wl;
+    if (k == 0) key0 = m;
     if (lane == k) {
-      my_v = m;
+      my_key = m;
       my_i = e;
     }
-    if ((e & 63) == lane) avail &= ~(1u << (e >> 6));
+    const bool pop = lane == wl;
+#pragma unroll
+    for (int i = 0; i + 1 < kJ; ++i) {
+      hi[i] = pop ? hi[i + 1] : hi[i];
+      lo[i] = pop ? lo[i + 1] : lo[i];
+    }
+    hi[kJ - 1] = pop ? 0u : hi[kJ - 1];
   }
-  const float ex = (lane < K) ? expf(my_v - v0) : 0.0f;
+  const float ex = (lane < K) ? expf(key_value(my_key) - key_value(key0)) : 0.0f;
   const float s = wave_sum(ex);
   if (lane < K) {
     topk_idx[static_cast<size_t>(t) * K + lane] = my_i;
     topk_w[static_cast<size_t>(t) * K + lane] = ex / s;
   }
-  if (lane == 0 && gamma != nullptr) gamma[t] = 1.0f / (1.0f + expf(-z[E]));
+  if (lane == 0 && gamma != nullptr) gamma[t] = 1.0f / (1.0f + expf(-zg));
 }
 
-// Inclusive scan over a 1024-thread block (wave shuffles + one LDS pass).
-__device__ __forceinline__ int block_incl_scan_1024(int v, int* lds16, int& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// Inclusive prefix sums of two values at once over a 1024-thread block.
+// Within a wave: a Hillis-Steele scan inside each row of 16 lanes on DPP
+// row shifts (lanes without a source add 0), then each row adds the totals
+// of the rows before it (read from lanes 15, 31, 47).  Across the 16 waves:
+// one LDS pass over the wave totals.  Integer sums, so the order is moot.
+__device__ __forceinline__ int dpp_row_shr_or0(int v, int shift_ctrl) {
+  switch (shift_ctrl) {   // the control must be a literal
+    case 1: return __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);
+    case 2: return __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);
+    case 4: return __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);
+    default: return __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);
+  }
+}
+__device__ __forceinline__ int wave_incl_scan(int v) {
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(v, off, kWave);
-    if (lane >= off) v += o;
-  }
-  if (lane == 63) lds16[wave] = v;
+  for (int sh = 1; sh < 16; sh <<= 1) v += dpp_row_shr_or0(v, sh);
+  const int lane = threadIdx.x & 63;
+  const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31),
+            r2 = __builtin_amdgcn_readlane(v, 47);
+  return v + (lane >= 16 ? r0 : 0) + (lane >= 32 ? r1 : 0) + (lane >= 48 ? r2 : 0);
+}
+__device__ __forceinline__ void block_incl_scan2_1024(int& a, int& b, int2* lds16, int& total_a, int& total_b) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  a = wave_incl_scan(a);
+  b = wave_incl_scan(b);
+  if (lane == 63) lds16[wave] = make_int2(a, b);
   __syncthreads();
-  int base = 0, tot = 0;
+  int base_a = 0, base_b = 0, tot_a = 0, tot_b = 0;
+#pragma unroll
   for (int w = 0; w < 16; ++w) {
-    const int s = lds16[w];
-    if (w < wave) base += s;
-    tot += s;
+    const int2 s = lds16[w];
+    if (w < wave) {
+      base_a += s.x;
+      base_b += s.y;
+    }
+    tot_a += s.x;
+    tot_b += s.y;
   }
-  __syncthreads();
-  total = tot;
-  return v + base;
+  a += base_a;
+  b += base_b;
+  total_a = tot_a;
+  total_b = tot_b;
 }
 
 // Stable counting sort of the n = T*K routed rows by expert, one 1024-thread
@@ -152,10 +223,10 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ to
   __shared__ int start[kMaxExperts];
   __shared__ int run[kMaxExperts];
   __shared__ int ubase[kMaxExperts];
-  __shared__ unsigned short wcnt[16][kMaxExperts];
-  __shared__ int scan_tmp[16];
+  __shared__ unsigned short wcnt[kMaxExperts][16];   // rows of expert e in wave w of a chunk
+  __shared__ int2 scan_tmp[16];
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   if (tid < E) {
     cnt[tid] = 0;
     run[tid] = 0;
@@ -163,24 +234,25 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ to
   __syncthreads();
   // rows whose expert index lies outside [0, E) are dropped: not counted,
   // not placed (inv = -1), so they contribute nothing
-  for (int i = tid; i < n; i += 1024) {
+  // the first chunk's indices stay in a register for the scatter below
+  const int first_e = tid < n ? topk_idx[tid] : -1;
+  if (first_e >= 0 && first_e < E) atomicAdd(&cnt[first_e], 1);
+  for (int i = tid + 1024; i < n; i += 1024) {
     const int e = topk_idx[i];
     if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
   }
   __syncthreads();
   const int c = (tid < E) ? cnt[tid] : 0;
-  int total = 0;
-  const int incl = block_incl_scan_1024(c, scan_tmp, total);
+  const int nu = (c + kSubTokens - 1) / kSubTokens;   // units of expert tid
+  int incl = c, uincl = nu, total = 0, n_ru = 0;
+  block_incl_scan2_1024(incl, uincl, scan_tmp, total, n_ru);
   if (tid < E) {
     start[tid] = incl - c;
     expert_off[tid] = incl - c;
   }
   if (tid == 0) expert_off[E] = total;
   const int n_su = (plan.units != nullptr && plan.shared) ? (plan.T + kSubTokens - 1) / kSubTokens : 0;
-  int n_ru = 0;
   if (plan.units != nullptr) {
-    const int nu = (c + kSubTokens - 1) / kSubTokens;
-    const int uincl = block_incl_scan_1024(nu, scan_tmp, n_ru);
     if (tid < E) ubase[tid] = n_su + uincl - nu;
     if (tid == 0) {
       plan.n_units[0] = n_su;
@@ -196,28 +268,27 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ to
   }
   for (int base = 0; base < n; base += 1024) {
     const int i = base + tid;
-    const int ei = i < n ? topk_idx[i] : -1;
+    const int ei = base == 0 ? first_e : (i < n ? topk_idx[i] : -1);
     const bool valid = ei >= 0 && ei < E;
-    const int e = valid ? ei : -1;
+    const int e = valid ? ei : 0;
     if (i < n && !valid && inv != nullptr) inv[i] = -1;
-    unsigned long long peers = 0;
-    unsigned long long todo = __ballot(valid);
-    while (todo) {
-      const int leader = __ffsll(static_cast<long long>(todo)) - 1;
-      const int le = __builtin_amdgcn_readlane(e, leader);
-      const unsigned long long m = __ballot(valid && e == le);
-      if (valid && e == le) peers = m;
-      todo &= ~m;
+    // lanes of this wave holding the same expert: intersect, bit by bit of
+    // the expert index, the ballots of lanes that agree with this lane
+    unsigned long long peers = __ballot(valid);
+    for (int b = 0; (1 << b) < E; ++b) {
+      const bool bit = (e >> b) & 1;
+      const unsigned long long on = __ballot(bit);
+      peers &= bit ? on : ~on;
     }
     const int rank = __popcll(peers & ((1ull << lane) - 1ull));
     const bool first_peer = valid && rank == 0;
-    for (int k = tid; k < 16 * E; k += 1024) wcnt[k / E][k % E] = 0;
+    for (int k = tid; k < 8 * E; k += 1024) reinterpret_cast<uint32_t*>(&wcnt[0][0])[k] = 0u;
     __syncthreads();
-    if (first_peer) wcnt[wave][e] = static_cast<unsigned short>(__popcll(peers));
+    if (first_peer) wcnt[e][wave] = static_cast<unsigned short>(__popcll(peers));
     __syncthreads();
     if (valid) {
       int before = 0;
-      for (int w = 0; w < wave; ++w) before += wcnt[w][e];
+      for (int w = 0; w < wave; ++w) before += wcnt[e][w];
       const int r = run[e] + before + rank;   // rank among all rows of expert e
       const int pos = start[e] + r;
       perm[pos] = i;
@@ -247,45 +318,61 @@ __global__ __launch_bounds__(1024) void k_router_mfma(const uint16_t* __restrict
   typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
   typedef float f32x4_t __attribute__((ext_vector_type(4)));
   __shared__ float part[16][16][17];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, kb = lane >> 4;
   const int row = blockIdx.x * 16 + n;      // router row this lane loads (B operand column)
   const int tok = blockIdx.y * 16 + n;      // token this lane loads (A operand row)
   const int nsteps = H / 32;
+  // out-of-range lanes load a clamped (valid) row and zero it, so every load
+  // is unconditional and a wave's loads for up to kBatch steps go out together
+  constexpr int kBatch = 4;
+  const bool tok_ok = tok < T, row_ok = row <= E;
+  const uint16_t* xrow = x + static_cast<size_t>(tok_ok ? tok : T - 1) * H;
+  const uint16_t* wrow = wr + static_cast<size_t>(row_ok ? row : E) * H;
   f32x4_t acc = {0, 0, 0, 0};
-  for (int st = wave; st < nsteps; st += nw) {
-    const int col = 32 * st + 8 * kb;
-    const uint4 av = (tok < T) ? *reinterpret_cast<const uint4*>(x + static_cast<size_t>(tok) * H + col)
-                               : make_uint4(0, 0, 0, 0);
-    const uint4 bv = (row <= E) ? *reinterpret_cast<const uint4*>(wr + static_cast<size_t>(row) * H + col)
-                                : make_uint4(0, 0, 0, 0);
-    if constexpr (ACT == 2) {
-      const uint32_t bw[4] = {bv.x, bv.y, bv.z, bv.w};
-      uint32_t hi[4], lo[4];
+  for (int st0 = wave; st0 < nsteps; st0 += kBatch * nw) {
+    uint4 av[kBatch], bv[kBatch];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float f0 = f16_bits_to_f32(bw[i] & 0xFFFFu), f1 = f16_bits_to_f32(bw[i] >> 16);
-        const uint32_t h0 = __float_as_uint(f0) & 0xFFFF0000u, h1 = __float_as_uint(f1) & 0xFFFF0000u;
-        const uint32_t l0 = f32_to_act<2>(f0 - __uint_as_float(h0)), l1 = f32_to_act<2>(f1 - __uint_as_float(h1));
-        hi[i] = (h0 >> 16) | h1;
-        lo[i] = l0 | (l1 << 16);
+    for (int u = 0; u < kBatch; ++u) {
+      const int col = 32 * min(st0 + u * nw, nsteps - 1) + 8 * kb;
+      av[u] = *reinterpret_cast<const uint4*>(xrow + col);
+      bv[u] = *reinterpret_cast<const uint4*>(wrow + col);
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (st0 + u * nw >= nsteps) break;   // wave-uniform
+      if (!tok_ok) av[u] = make_uint4(0, 0, 0, 0);
+      if (!row_ok) bv[u] = make_uint4(0, 0, 0, 0);
+      if constexpr (ACT == 2) {
+        const uint32_t bw[4] = {bv[u].x, bv[u].y, bv[u].z, bv[u].w};
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float f0 = f16_bits_to_f32(bw[i] & 0xFFFFu), f1 = f16_bits_to_f32(bw[i] >> 16);
+          const uint32_t h0 = __float_as_uint(f0) & 0xFFFF0000u, h1 = __float_as_uint(f1) & 0xFFFF0000u;
+          const uint32_t l0 = f32_to_act<2>(f0 - __uint_as_float(h0)), l1 = f32_to_act<2>(f1 - __uint_as_float(h1));
+          hi[i] = (h0 >> 16) | h1;
+          lo[i] = l0 | (l1 << 16);
+        }
+        const uint4 bh = make_uint4(hi[0], hi[1], hi[2], hi[3]), bl = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[u]),
+                                                      __builtin_bit_cast(bf16x8_t, bh), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[u]),
+                                                      __builtin_bit_cast(bf16x8_t, bl), acc, 0, 0, 0);
+      } else {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, av[u]),
+                                                     __builtin_bit_cast(f16x8_t, bv[u]), acc, 0, 0, 0);
       }
-      const uint4 bh = make_uint4(hi[0], hi[1], hi[2], hi[3]), bl = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, bh),
-                                                    acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, bl),
-                                                    acc, 0, 0, 0);
-    } else {
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, av), __builtin_bit_cast(f16x8_t, bv),
-                                                   acc, 0, 0, 0);
     }
   }
   // lane holds tokens 4kb..4kb+3 (tile rows) of router row n (tile column)
 #pragma unroll
   for (int i = 0; i < 4; ++i) part[wave][4 * kb + i][n] = acc[i];
   __syncthreads();
-  if (threadIdx.x < 256) {
-    const int m = threadIdx.x >> 4, c = threadIdx.x & 15;
+  // 256 outputs per tile; a block may have as few as 2 waves (H = 64)
+  for (int q = threadIdx.x; q < 256; q += blockDim.x) {
+    const int m = q >> 4, c = q & 15;
     const int t = blockIdx.y * 16 + m, r = blockIdx.x * 16 + c;
     float sum = 0.0f;
     for (int w = 0; w < nw; ++w) sum += part[w][m][c];
@@ -320,7 +407,19 @@ hipError_t launch_router_logits(int act, const uint16_t* x, const uint16_t* wr, 
 
 hipError_t launch_topk(const float* logits, int T, int E, int K, int32_t* idx, float* w, float* gamma,
                        hipStream_t s) {
-  hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, K, idx, w, gamma);
+  const dim3 grid((T + 3) / 4), block(256);
+  if (E <= 64) {
+    hipLaunchKernelGGL(k_topk<1>, grid, block, 0, s, logits, T, E, K, idx, w, gamma);
+  } else if (E <= 128) {
+    hipLaunchKernelGGL(k_topk<2>, grid, block, 0, s, logits, T, E, K, idx, w, gamma);
+  } else if (E <= 256) {
+    hipLaunchKernelGGL(k_topk<4>, grid, block, 0, s, logits, T, E, K, idx, w, gamma);
+  } else if (E <= 512) {
+    hipLaunchKernelGGL(k_topk<8>, grid, block, 0, s, logits, T, E, K, idx, w, gamma);
+  } else {
+    static_assert(kMaxExperts == 1024, "top-k dispatch covers up to 16 entries per lane");
+    hipLaunchKernelGGL(k_topk<16>, grid, block, 0, s, logits, T, E, K, idx, w, gamma);
+  }
   return hipGetLastError();
 }
 
