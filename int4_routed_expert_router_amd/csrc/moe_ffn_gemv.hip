@@ -214,48 +214,67 @@ __global__ __launch_bounds__(512) void k_combine(const float* __restrict__ yrow,
   __shared__ float lds16[16];
   __shared__ int src[kMaxTopK + 1];
   __shared__ float wt[kMaxTopK + 1];
-  const int t = blockIdx.x, tid = threadIdx.x;
   __shared__ int n_src;
-  if (tid == 0) {
-    // sources in rank order, then the shared expert; a dropped row (inv -1)
-    // adds nothing and is left out
-    int ns = 0;
-    for (int k = 0; k < K; ++k) {
-      const int sr = inv ? inv[t * K + k] : t * K + k;
-      if (sr >= 0) {
-        src[ns] = sr;
-        wt[ns] = w[t * K + k];
-        ++ns;
-      }
-    }
-    if (has_shared) {
-      src[ns] = T * K + t;
-      wt[ns] = gamma[t];
-      ++ns;
-    }
-    n_src = ns;
-  }
-  __syncthreads();
-  const int ns = n_src;
+  const int t = blockIdx.x, tid = threadIdx.x;
   const int H4 = H / 4;
   constexpr int kPer = kMaxH / 4 / 512;
-  constexpr int kB = 16;
+  // the residual is read first: it does not depend on the source list
   float4 rr[kPer];
+  if constexpr (EPI) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int c4 = tid + 512 * u;
+      rr[u] = c4 < H4 ? reinterpret_cast<const float4*>(r + static_cast<size_t>(t) * H)[c4] : make_float4(0, 0, 0, 0);
+    }
+  }
+  if (tid < 64) {
+    // sources in rank order (lane k holds rank k), then the shared expert; a
+    // dropped row (inv -1) adds nothing and is left out.  The list is
+    // compacted with a ballot: a kept rank goes to the number of kept ranks
+    // before it.
+    const int k = tid;
+    int sr = -1;
+    float wk = 0.0f;
+    if (k < K) {
+      sr = inv ? inv[t * K + k] : t * K + k;
+      wk = w[t * K + k];
+    }
+    const float gm = (k == 0 && has_shared) ? gamma[t] : 0.0f;
+    const unsigned long long kept = __ballot(sr >= 0);
+    const int pos = __popcll(kept & ((1ull << k) - 1ull));
+    if (sr >= 0) {
+      src[pos] = sr;
+      wt[pos] = wk;
+    }
+    if (k == 0) {
+      int ns = __popcll(kept);
+      if (has_shared) {
+        src[ns] = T * K + t;
+        wt[ns] = gm;
+        ++ns;
+      }
+      n_src = ns;
+    }
+  }
+  __syncthreads();
+  const int ns = __builtin_amdgcn_readfirstlane(n_src);   // uniform
+  constexpr int kB = 16;
   float ss = 0.0f;
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
     const int c4 = tid + 512 * u;
-    rr[u] = make_float4(0, 0, 0, 0);
     if (c4 < H4) {
       float4 acc = make_float4(0, 0, 0, 0);
       for (int k0 = 0; k0 < ns; k0 += kB) {
+        // every load of the batch is issued (sources past the list repeat
+        // the last one) before the first is used
         float4 v[kB];
 #pragma unroll
         for (int b = 0; b < kB; ++b)
-          if (k0 + b < ns) v[b] = reinterpret_cast<const float4*>(yrow + static_cast<size_t>(src[k0 + b]) * H)[c4];
+          v[b] = reinterpret_cast<const float4*>(yrow + static_cast<size_t>(src[min(k0 + b, ns - 1)]) * H)[c4];
 #pragma unroll
         for (int b = 0; b < kB; ++b) {
-          if (k0 + b < ns) {
+          if (k0 + b < ns) {   // uniform
             const float wk = wt[k0 + b];
             acc.x = fmaf(wk, v[b].x, acc.x);
             acc.y = fmaf(wk, v[b].y, acc.y);
@@ -266,7 +285,7 @@ __global__ __launch_bounds__(512) void k_combine(const float* __restrict__ yrow,
       }
       if (y) reinterpret_cast<float4*>(y + static_cast<size_t>(t) * H)[c4] = acc;
       if constexpr (EPI) {
-        float4 rv = reinterpret_cast<float4*>(r + static_cast<size_t>(t) * H)[c4];
+        float4 rv = rr[u];
         rv.x += acc.x;
         rv.y += acc.y;
         rv.z += acc.z;

@@ -5,6 +5,8 @@
 // goes to 10 of 512 or 8 of 256 experts).  Selection order is (logit desc,
 // expert index asc); weights are the softmax restricted to the selected set,
 // which equals a softmax over all experts followed by renormalisation.
+#include <utility>
+
 #include "moe_common.h"
 #include "moe_kernels.h"
 
@@ -89,6 +91,15 @@ __device__ __forceinline__ void oddeven_merge_sort(Cas cas) {
   }
 }
 
+// a[i] = a[i + 1] for i < N-1 where take is set.  Written over constant
+// indices (not a loop) so that the list stays in registers as plain values:
+// a select between two neighbouring array loads inside a loop would become
+// one load at a selected index, i.e. a gather over the whole list.
+template <int N, int... I>
+__device__ __forceinline__ void shift_up(uint32_t (&a)[N], bool take, std::integer_sequence<int, I...>) {
+  ((a[I] = take ? a[I + 1] : a[I]), ...);
+}
+
 // One wave per token; lane l holds experts l, l+64, ... (kJ of them).  Each
 // lane first sorts its own entries by (logit desc, expert index asc), as a
 // 64-bit key (order_key(logit), kJ-1-j).  Then K rounds: the wave maximum of
@@ -127,32 +138,44 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
     hi[b] = swap ? ha : hi[b];
     lo[b] = swap ? la : lo[b];
   });
+  // after the sort the lane's indices travel as one word of 4-bit fields
+  // (field i = kJ-1-j of list position i), so a pop is one shift
+  uint32_t lo_packed = 0;
+#pragma unroll
+  for (int i = 0; i < kJ && i < 8; ++i) lo_packed |= lo[i] << (4 * i);
+  uint32_t lo_hi8 = 0;   // positions 8..15 (kJ = 16 only)
+#pragma unroll
+  for (int i = 8; i < kJ; ++i) lo_hi8 |= lo[i] << (4 * (i - 8));
   uint32_t my_key = 0, key0 = 0;
   int my_i = 0;
   for (int k = 0; k < K; ++k) {
     // K <= E, so some lane still holds an entry and m > 0
     const uint32_t m = wave_max_u32(hi[0]);
     const unsigned long long cand = __ballot(hi[0] == m);
+    const uint32_t head_lo = lo_packed & 0xFu;
     int wl;
     if (__popcll(cand) == 1) {
       wl = __ffsll(cand) - 1;
     } else {
-      const uint32_t idx = (hi[0] == m) ? (kJ - 1 - lo[0]) * 64u + static_cast<uint32_t>(lane) : 0xFFFFFFFFu;
+      const uint32_t idx = (hi[0] == m) ? (kJ - 1 - head_lo) * 64u + static_cast<uint32_t>(lane) : 0xFFFFFFFFu;
       wl = __builtin_amdgcn_readfirstlane(static_cast<int>(wave_min_u32(idx) & 63u));
     }
-    const int e = (kJ - 1 - __builtin_amdgcn_readlane(static_cast<int>(lo[0]), wl)) * 64 + wl;
+    const int e = (kJ - 1 - __builtin_amdgcn_readlane(static_cast<int>(head_lo), wl)) * 64 + wl;
     if (k == 0) key0 = m;
     if (lane == k) {
       my_key = m;
       my_i = e;
     }
+    // the winning lane drops its head: its list moves up one position
     const bool pop = lane == wl;
-#pragma unroll
-    for (int i = 0; i + 1 < kJ; ++i) {
-      hi[i] = pop ? hi[i + 1] : hi[i];
-      lo[i] = pop ? lo[i + 1] : lo[i];
-    }
+    shift_up(hi, pop, std::make_integer_sequence<int, kJ - 1>{});
     hi[kJ - 1] = pop ? 0u : hi[kJ - 1];
+    if constexpr (kJ > 8) {
+      lo_packed = pop ? (lo_packed >> 4) | (lo_hi8 << 28) : lo_packed;
+      lo_hi8 = pop ? lo_hi8 >> 4 : lo_hi8;
+    } else {
+      lo_packed = pop ? lo_packed >> 4 : lo_packed;
+    }
   }
   const float ex = (lane < K) ? expf(key_value(my_key) - key_value(key0)) : 0.0f;
   const float s = wave_sum(ex);
