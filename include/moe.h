@@ -151,7 +151,9 @@ moe_status moe_workspace_bytes(const moe_layer_desc* desc, int32_t n_tokens, siz
  * Outputs (device): topk_idx [T][K] int32 in rank order, topk_w [T][K]
  * fp32, shared_gate [T] fp32 (may be NULL when shared_inter == 0),
  * logits_or_null [T][E+1] fp32 (column E = shared-gate logit).  Logits are
- * fp32 sums of exact products; selection and weights use those fp32 values. */
+ * fp32 sums of exact products in a fixed order (for batches of 16+ tokens,
+ * up to 4 hidden-dimension slices added in slice order, then the bias);
+ * selection and weights use those fp32 values. */
 moe_status moe_route(const moe_layer_desc* desc, const moe_layer_weights* w, const void* x,
                      int32_t n_tokens, int32_t* topk_idx, float* topk_w, float* shared_gate,
                      float* logits_or_null, void* ws, size_t ws_bytes, moe_stream stream);

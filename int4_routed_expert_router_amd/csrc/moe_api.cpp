@@ -91,7 +91,7 @@ Ws layout(const moe_layer_desc* d, int T) {
   const size_t rows = T * K + (d->shared_inter ? T : 0);
   Ws s{};
   size_t o = 0;
-  s.logits = o; o += al(T * (E + 1) * 4);
+  s.logits = o; o += al(moe::kRouterMaxParts * T * (E + 1) * 4);   // router partial sums
   s.idx = o; o += al(T * K * 4);
   s.w = o; o += al(T * K * 4);
   s.gamma = o; o += al(T * 4);
@@ -129,14 +129,18 @@ bool use_grouped(const moe_layer_desc* d, int T) {
 }
 
 moe_status do_route(const moe_layer_desc* d, const moe_layer_weights* w, const void* x, int T, int32_t* idx,
-                    float* tw, float* gamma, float* logits, hipStream_t s, int layer = -1) {
+                    float* tw, float* gamma, float* part, float* logits_out, hipStream_t s, int layer = -1) {
   hipError_t e = timer_mark(true, MOE_TIME_ROUTER, layer, s);
+  moe::RouterParts rp{1, false, true};
   if (e == hipSuccess)
-    e = moe::launch_router_logits(d->act_dtype, static_cast<const uint16_t*>(x), w->router_w, w->router_bias, logits,
-                                  T, d->hidden, d->n_experts, s);
+    e = moe::launch_router_logits(d->act_dtype, static_cast<const uint16_t*>(x), w->router_w, w->router_bias, part, T,
+                                  d->hidden, d->n_experts, s, &rp);
   if (e == hipSuccess) e = timer_mark(false, MOE_TIME_ROUTER, layer, s);
   if (e != hipSuccess) return hip_fail(e, "router kernel launch");
-  e = moe::launch_topk(logits, T, d->n_experts, d->top_k, idx, tw, gamma, s);
+  const uint16_t* gate_w = rp.gate ? nullptr : w->router_w + static_cast<size_t>(d->n_experts) * d->hidden;
+  e = moe::launch_topk(d->act_dtype, part, rp.n_part, rp.biased ? nullptr : w->router_bias,
+                       static_cast<const uint16_t*>(x), gate_w, d->hidden, T, d->n_experts, d->top_k, idx, tw, gamma,
+                       logits_out, s);
   if (e != hipSuccess) return hip_fail(e, "top-k kernel launch");
   return MOE_OK;
 }
@@ -327,9 +331,9 @@ moe_status moe_route(const moe_layer_desc* d, const moe_layer_weights* w, const 
   if (!topk_idx || !topk_w) return fail(MOE_EINVAL, "topk_idx and topk_w are required");
   Ws L;
   if ((st = check_ws(d, T, ws, ws_bytes, L))) return st;
-  float* logits = logits_or_null ? logits_or_null : at<float>(ws, L.logits);
   float* gamma = shared_gate ? shared_gate : at<float>(ws, L.gamma);
-  st = do_route(d, w, x, T, topk_idx, topk_w, gamma, logits, reinterpret_cast<hipStream_t>(stream));
+  st = do_route(d, w, x, T, topk_idx, topk_w, gamma, at<float>(ws, L.logits), logits_or_null,
+                reinterpret_cast<hipStream_t>(stream));
   return st ? st : ok();
 }
 
@@ -382,7 +386,7 @@ moe_status moe_layer_forward(const moe_layer_desc* d, const moe_layer_weights* w
   int32_t* idx = idx_out ? idx_out : at<int32_t>(ws, L.idx);
   float* tw = w_out ? w_out : at<float>(ws, L.w);
   float* gamma = gamma_out ? gamma_out : at<float>(ws, L.gamma);
-  if ((st = do_route(d, w, x, T, idx, tw, gamma, at<float>(ws, L.logits), s))) return st;
+  if ((st = do_route(d, w, x, T, idx, tw, gamma, at<float>(ws, L.logits), nullptr, s))) return st;
   if ((st = do_ffn(d, w, x, T, idx, tw, gamma, y, nullptr, nullptr, ws, L, s))) return st;
   return ok();
 }
@@ -425,7 +429,7 @@ static moe_status stack_enqueue(const moe_layer_desc* d, const moe_layer_weights
     float* tw = w_all ? w_all + l * TK : at<float>(ws, L.w);
     float* gamma = gamma_all ? gamma_all + static_cast<size_t>(l) * T : at<float>(ws, L.gamma);
     float* y = y_all ? y_all + l * TH : nullptr;
-    if ((st = do_route(d, &layers[l], xl, T, idx, tw, gamma, at<float>(ws, L.logits), s, l))) return st;
+    if ((st = do_route(d, &layers[l], xl, T, idx, tw, gamma, at<float>(ws, L.logits), nullptr, s, l))) return st;
     if ((st = do_ffn(d, &layers[l], xl, T, idx, tw, gamma, y, r, x_buf, ws, L, s, l))) return st;
   }
   return MOE_OK;

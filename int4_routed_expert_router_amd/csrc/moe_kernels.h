@@ -10,6 +10,9 @@ constexpr int kMaxInter = 4096;    // intermediate size limit (down GEMV stages 
 constexpr int kMaxExperts = 1024;  // top-k holds E/64 logits per lane; bucketing uses one workgroup
 constexpr int kMaxTopK = 64;       // one selected expert per lane
 constexpr int kRouterMfmaMinTokens = 16;  // router GEMM on the matrix cores from this batch size
+constexpr int kRouterMaxParts = 4;        // hidden-dimension slices of the matrix-core router
+constexpr int kRouterWaves = 4;           // waves per matrix-core router workgroup
+constexpr int kRouterBatch = 8;           // 32-column steps whose loads a router wave issues together
 
 // Routed rows of a batch: row j < T*K is (token j/K, rank j%K) in slot order,
 // or the j-th row of the expert-sorted order in the grouped family; rows
@@ -58,10 +61,27 @@ inline int max_units(int T, int K, int E, bool shared) {
   return n_act + rows / kSubTokens + (shared ? (T + kSubTokens - 1) / kSubTokens : 0);
 }
 
-hipError_t launch_router_logits(int act, const uint16_t* x, const uint16_t* wr, const float* bias, float* logits,
-                                int T, int H, int E, hipStream_t s);
-hipError_t launch_topk(const float* logits, int T, int E, int K, int32_t* idx, float* w, float* gamma,
-                       hipStream_t s);
+// Router logits.  The matrix-core path (T >= kRouterMfmaMinTokens) covers
+// the E expert rows only, splits the hidden dimension into n_part slices
+// (n_part <= kRouterMaxParts) and writes unbiased partial sums
+// part[p][t][row]; top-K then computes the shared-gate logit itself.  The
+// per-row path writes finished logits of all E+1 rows (bias included) as a
+// single part.
+struct RouterParts {
+  int n_part;
+  bool biased;   // bias already added
+  bool gate;     // column E holds the shared-gate logit
+};
+hipError_t launch_router_logits(int act, const uint16_t* x, const uint16_t* wr, const float* bias, float* part,
+                                int T, int H, int E, hipStream_t s, RouterParts* out);
+// Top-K over z[t][e] = sum_p part[p][t][e] (p ascending) + bias[e] (bias may
+// be null).  The shared-gate logit is column E of the parts, or x[t] . gate_w
+// when gate_w is non-null.  Writes the selection, the renormalised weights,
+// the shared gate (when gamma is non-null) and, when logits is non-null, the
+// logits themselves.
+hipError_t launch_topk(int act, const float* part, int n_part, const float* bias, const uint16_t* x,
+                       const uint16_t* gate_w, int H, int T, int E, int K, int32_t* idx, float* w, float* gamma,
+                       float* logits, hipStream_t s);
 hipError_t launch_permute(const int32_t* idx, int n, int E, int32_t* off, int32_t* perm, int32_t* inv,
                           const UnitPlan* plan, hipStream_t s);
 

@@ -106,28 +106,96 @@ __device__ __forceinline__ void shift_up(uint32_t (&a)[N], bool take, std::integ
 // the lanes' head keys picks the logit; among the lanes whose head holds it
 // (one, unless logits tie across lanes) the lowest expert index wins, and
 // the winning lane pops its head.  So ties resolve to the lower expert index.
-template <int kJ>
-__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int T, int E, int K,
+//
+// The shared-gate logit comes from column E of the parts, or, when gate_w is
+// given (the matrix-core router leaves that row out, so that its grid is a
+// whole number of 16-row blocks), from a dot product of x[t] with gate_w
+// computed here: lane l takes columns 512 i + 8 l .. +7 in order, then a wave
+// sum.
+template <int kJ, int ACT>
+__global__ __launch_bounds__(64) void k_topk(const float* __restrict__ part, int n_part,
+                                              const float* __restrict__ bias, const uint16_t* __restrict__ x,
+                                              const uint16_t* __restrict__ gate_w, int H, int T, int E, int K,
                                               int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-                                              float* __restrict__ gamma) {
+                                              float* __restrict__ gamma, float* __restrict__ logits) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int t = blockIdx.x;   // one token per workgroup: spreads the loads over the compute units
   if (t >= T) return;
-  const float* z = logits + static_cast<size_t>(t) * (E + 1);
-  float raw[kJ];
-  // every load is issued before any is used; the index is clamped to E (the
-  // shared-gate column), which is always valid memory
+  // gate operands first (columns past H read column 0 and are zeroed below)
+  constexpr int kGI = kMaxH / 512;
+  uint4 gx[kGI], gw[kGI];
+  const int ngi = gate_w != nullptr ? (H + 511) / 512 : 0;
 #pragma unroll
-  for (int j = 0; j < kJ; ++j) raw[j] = z[min(lane + 64 * j, E)];
-  float zg = z[E];
-  asm volatile("" : "+v"(zg));
-  // opaque to the optimiser, so no load is sunk into the validity branch
+  for (int i = 0; i < kGI; ++i) {
+    if (i < ngi) {   // uniform
+      const int c = 512 * i + 8 * lane;
+      const int cc = c < H ? c : 0;
+      gx[i] = *reinterpret_cast<const uint4*>(x + static_cast<size_t>(t) * H + cc);
+      gw[i] = *reinterpret_cast<const uint4*>(gate_w + cc);
+    }
+  }
+  // z = part[0] + part[1] + ... (in order) + bias.  Every load is issued
+  // before any is used: the expert index is clamped to E (the shared-gate
+  // column) and the part index to n_part - 1, both valid memory.
+  const size_t pstride = static_cast<size_t>(T) * (E + 1);
+  const float* z = part + static_cast<size_t>(t) * (E + 1);
+  float raw[kRouterMaxParts][kJ], zgp[kRouterMaxParts], bj[kJ];
 #pragma unroll
-  for (int j = 0; j < kJ; ++j) asm volatile("" : "+v"(raw[j]));
+  for (int p = 0; p < kRouterMaxParts; ++p) {
+    const float* zp = z + min(p, n_part - 1) * pstride;
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) raw[p][j] = zp[min(lane + 64 * j, E)];
+    zgp[p] = zp[E];
+  }
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) bj[j] = bias != nullptr ? bias[min(lane + 64 * j, E - 1)] : 0.0f;
+  // opaque to the optimiser, so no load is sunk into a branch
+#pragma unroll
+  for (int p = 0; p < kRouterMaxParts; ++p) {
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) asm volatile("" : "+v"(raw[p][j]));
+    asm volatile("" : "+v"(zgp[p]));
+  }
+  float zg = zgp[0];
+#pragma unroll
+  for (int p = 1; p < kRouterMaxParts; ++p) {
+    if (p < n_part) {   // uniform
+      zg += zgp[p];
+#pragma unroll
+      for (int j = 0; j < kJ; ++j) raw[0][j] += raw[p][j];
+    }
+  }
+  if (gate_w != nullptr) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kGI; ++i) {
+      if (i < ngi && 512 * i + 8 * lane < H) {
+        const uint32_t xs[4] = {gx[i].x, gx[i].y, gx[i].z, gx[i].w};
+        const uint32_t ws[4] = {gw[i].x, gw[i].y, gw[i].z, gw[i].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc = fmaf(act_to_f32<ACT>(xs[q] & 0xFFFFu), f16_bits_to_f32(ws[q] & 0xFFFFu), acc);
+          acc = fmaf(act_to_f32<ACT>(xs[q] >> 16), f16_bits_to_f32(ws[q] >> 16), acc);
+        }
+      }
+    }
+    zg = wave_sum(acc);
+  }
+  if (bias != nullptr) {
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) raw[0][j] += bj[j];
+  }
+  if (logits != nullptr) {
+    float* lo_out = logits + static_cast<size_t>(t) * (E + 1);
+#pragma unroll
+    for (int j = 0; j < kJ; ++j)
+      if (lane + 64 * j < E) lo_out[lane + 64 * j] = raw[0][j];
+    if (lane == 0) lo_out[E] = zg;
+  }
   uint32_t hi[kJ], lo[kJ];
 #pragma unroll
   for (int j = 0; j < kJ; ++j) {
-    hi[j] = (lane + 64 * j < E) ? order_key(raw[j]) : 0u;
+    hi[j] = (lane + 64 * j < E) ? order_key(raw[0][j]) : 0u;
     lo[j] = kJ - 1 - j;
   }
   oddeven_merge_sort<kJ>([&](int a, int b) {
@@ -329,30 +397,34 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ to
 }
 
 // Router logits on the matrix cores for batches of 16+ tokens.  One workgroup
-// = 16 router rows x 16 tokens; its waves split H into 32-column steps and
-// their fp32 partial tiles are summed in a fixed order.  The fp16 router
-// weights enter bf16 MFMAs as an exact hi + lo pair (fp16 has 11 significant
-// bits); with fp16 activations they enter as they are.
+// = 16 router rows x 16 tokens x one slice of the hidden dimension
+// (blockIdx.z; `steps` 32-column steps per slice); its waves split the slice
+// into 32-column steps and their fp32 partial tiles are summed in a fixed
+// order.  The slice sums go to part[z] (no bias); top-K adds the slices in
+// order and the bias.  Slicing spreads a small batch over all compute units.
+// The fp16 router weights enter bf16 MFMAs as an exact hi + lo pair (fp16 has
+// 11 significant bits); with fp16 activations they enter as they are.
 template <int ACT>
 __global__ __launch_bounds__(1024) void k_router_mfma(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
-                                                      const float* __restrict__ bias, float* __restrict__ logits,
-                                                      int T, int H, int E) {
+                                                      float* __restrict__ part, int T, int H, int E, int steps) {
   typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
   typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
   typedef float f32x4_t __attribute__((ext_vector_type(4)));
-  __shared__ float part[16][16][17];
+  __shared__ float wpart[16][16][17];   // per-wave partial tiles
   const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, kb = lane >> 4;
   const int row = blockIdx.x * 16 + n;      // router row this lane loads (B operand column)
   const int tok = blockIdx.y * 16 + n;      // token this lane loads (A operand row)
-  const int nsteps = H / 32;
+  const int nsteps = steps;
+  const int col0 = blockIdx.z * steps * 32;
+  float* logits = part + static_cast<size_t>(blockIdx.z) * T * (E + 1);
   // out-of-range lanes load a clamped (valid) row and zero it, so every load
   // is unconditional and a wave's loads for up to kBatch steps go out together
-  constexpr int kBatch = 4;
-  const bool tok_ok = tok < T, row_ok = row <= E;
-  const uint16_t* xrow = x + static_cast<size_t>(tok_ok ? tok : T - 1) * H;
-  const uint16_t* wrow = wr + static_cast<size_t>(row_ok ? row : E) * H;
+  constexpr int kBatch = kRouterBatch;
+  const bool tok_ok = tok < T, row_ok = row < E;   // row E (shared gate) is left to top-k
+  const uint16_t* xrow = x + static_cast<size_t>(tok_ok ? tok : T - 1) * H + col0;
+  const uint16_t* wrow = wr + static_cast<size_t>(row_ok ? row : E - 1) * H + col0;
   f32x4_t acc = {0, 0, 0, 0};
   for (int st0 = wave; st0 < nsteps; st0 += kBatch * nw) {
     uint4 av[kBatch], bv[kBatch];
@@ -391,58 +463,77 @@ __global__ __launch_bounds__(1024) void k_router_mfma(const uint16_t* __restrict
   }
   // lane holds tokens 4kb..4kb+3 (tile rows) of router row n (tile column)
 #pragma unroll
-  for (int i = 0; i < 4; ++i) part[wave][4 * kb + i][n] = acc[i];
+  for (int i = 0; i < 4; ++i) wpart[wave][4 * kb + i][n] = acc[i];
   __syncthreads();
   // 256 outputs per tile; a block may have as few as 2 waves (H = 64)
   for (int q = threadIdx.x; q < 256; q += blockDim.x) {
     const int m = q >> 4, c = q & 15;
     const int t = blockIdx.y * 16 + m, r = blockIdx.x * 16 + c;
     float sum = 0.0f;
-    for (int w = 0; w < nw; ++w) sum += part[w][m][c];
-    if (t < T && r <= E) {
-      if (r < E && bias != nullptr) sum += bias[r];
-      logits[static_cast<size_t>(t) * (E + 1) + r] = sum;
-    }
+    for (int w = 0; w < nw; ++w) sum += wpart[w][m][c];
+    if (t < T && r < E) logits[static_cast<size_t>(t) * (E + 1) + r] = sum;
   }
 }
 
 template <int ACT>
-static hipError_t launch_router_t(const uint16_t* x, const uint16_t* wr, const float* bias, float* logits, int T,
-                                  int H, int E, hipStream_t s) {
+static hipError_t launch_router_t(const uint16_t* x, const uint16_t* wr, const float* bias, float* part, int T, int H,
+                                  int E, hipStream_t s, RouterParts* out) {
   if (T >= kRouterMfmaMinTokens) {
-    const int steps = H / 32;
-    const int nw = steps < 16 ? steps : 16;
-    dim3 grid((E + 1 + 15) / 16, (T + 15) / 16);
-    hipLaunchKernelGGL(k_router_mfma<ACT>, grid, dim3(64 * nw), 0, s, x, wr, bias, logits, T, H, E);
+    // slices: double while the grid stays within one workgroup per compute
+    // unit and the slice stays a whole number of 32-column steps
+    const int tiles = ((E + 15) / 16) * ((T + 15) / 16);
+    int S = 1;
+    while (S < kRouterMaxParts && tiles * 2 * S <= kGridTiles && (H / 32) % (2 * S) == 0) S *= 2;
+    const int steps = H / 32 / S;
+    const int nw = steps < kRouterWaves ? steps : kRouterWaves;
+    dim3 grid((E + 15) / 16, (T + 15) / 16, S);
+    hipLaunchKernelGGL(k_router_mfma<ACT>, grid, dim3(64 * nw), 0, s, x, wr, part, T, H, E, steps);
+    out->n_part = S;
+    out->biased = false;
+    out->gate = false;
   } else {
     const int tpb = (T <= 8) ? T : 8;
     dim3 grid(E + 1, (T + tpb - 1) / tpb);
-    hipLaunchKernelGGL(k_router_logits<ACT>, grid, dim3(64), 0, s, x, wr, bias, logits, T, H, E, tpb);
+    hipLaunchKernelGGL(k_router_logits<ACT>, grid, dim3(64), 0, s, x, wr, bias, part, T, H, E, tpb);
+    out->n_part = 1;
+    out->biased = true;
+    out->gate = true;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_router_logits(int act, const uint16_t* x, const uint16_t* wr, const float* bias, float* logits,
-                                int T, int H, int E, hipStream_t s) {
-  return act == 2 ? launch_router_t<2>(x, wr, bias, logits, T, H, E, s)
-                  : launch_router_t<1>(x, wr, bias, logits, T, H, E, s);
+hipError_t launch_router_logits(int act, const uint16_t* x, const uint16_t* wr, const float* bias, float* part,
+                                int T, int H, int E, hipStream_t s, RouterParts* out) {
+  return act == 2 ? launch_router_t<2>(x, wr, bias, part, T, H, E, s, out)
+                  : launch_router_t<1>(x, wr, bias, part, T, H, E, s, out);
 }
 
-hipError_t launch_topk(const float* logits, int T, int E, int K, int32_t* idx, float* w, float* gamma,
-                       hipStream_t s) {
-  const dim3 grid((T + 3) / 4), block(256);
+hipError_t launch_topk(int act, const float* part, int n_part, const float* bias, const uint16_t* x,
+                       const uint16_t* gate_w, int H, int T, int E, int K, int32_t* idx, float* w, float* gamma,
+                       float* logits, hipStream_t s) {
+  const dim3 grid(T), block(64);
+#define TOPK_LAUNCH(J)                                                                                           \
+  do {                                                                                                           \
+    if (act == 2)                                                                                                \
+      hipLaunchKernelGGL((k_topk<J, 2>), grid, block, 0, s, part, n_part, bias, x, gate_w, H, T, E, K, idx, w,   \
+                         gamma, logits);                                                                         \
+    else                                                                                                         \
+      hipLaunchKernelGGL((k_topk<J, 1>), grid, block, 0, s, part, n_part, bias, x, gate_w, H, T, E, K, idx, w,   \
+                         gamma, logits);                                                                         \
+  } while (0)
   if (E <= 64) {
-    hipLaunchKernelGGL(k_topk<1>, grid, block, 0, s, logits, T, E, K, idx, w, gamma);
+    TOPK_LAUNCH(1);
   } else if (E <= 128) {
-    hipLaunchKernelGGL(k_topk<2>, grid, block, 0, s, logits, T, E, K, idx, w, gamma);
+    TOPK_LAUNCH(2);
   } else if (E <= 256) {
-    hipLaunchKernelGGL(k_topk<4>, grid, block, 0, s, logits, T, E, K, idx, w, gamma);
+    TOPK_LAUNCH(4);
   } else if (E <= 512) {
-    hipLaunchKernelGGL(k_topk<8>, grid, block, 0, s, logits, T, E, K, idx, w, gamma);
+    TOPK_LAUNCH(8);
   } else {
     static_assert(kMaxExperts == 1024, "top-k dispatch covers up to 16 entries per lane");
-    hipLaunchKernelGGL(k_topk<16>, grid, block, 0, s, logits, T, E, K, idx, w, gamma);
+    TOPK_LAUNCH(16);
   }
+#undef TOPK_LAUNCH
   return hipGetLastError();
 }
 
