@@ -32,15 +32,36 @@ __device__ __forceinline__ void row_source(const FfnArgs& a, int j, const uint8_
   }
 }
 
+// Sums of G consecutive values of an LDS row (G in {32, 64, 128}): thread u
+// adds `per` consecutive values, then the G/per partials of a group (adjacent
+// lanes of one wave) are combined by a butterfly; a fixed order either way.
+template <class LoadSum>
+__device__ __forceinline__ void group_sums(int n_vals, int G, int per, float* out, LoadSum load_sum) {
+  const int lanes_per_group = G / per;   // 4 .. 32, a power of two dividing 64
+  for (int u0 = 0; u0 < n_vals / per; u0 += blockDim.x) {
+    const int u = u0 + static_cast<int>(threadIdx.x);
+    float v = u < n_vals / per ? load_sum(u * per) : 0.0f;
+    for (int off = 1; off < lanes_per_group; off <<= 1) v += __shfl_xor(v, off, kWave);
+    if (u < n_vals / per && (u & (lanes_per_group - 1)) == 0) out[u / lanes_per_group] = v;
+  }
+}
+
+// Waves per workgroup of the GEMV kernels: at batch 1 the per-wave decode
+// work, not the weight bytes, sets the time, so it is spread thin.
+constexpr int kGemvWaves = 16;
+constexpr int kGemvBatch = 4;   // chunks whose loads a wave issues together
+
 // gate/up + SwiGLU.  Grid (rows, max(I,Is)/16); one workgroup = one row j and
-// one gate/up pair-tile p (16 gate rows + the 16 matching up rows); its four
-// waves split the 64-column chunks of H.  Per lane and chunk: one 16-byte
-// load = 8 gate + 8 up values for each of two 32-column halves.
+// one gate/up pair-tile p (16 gate rows + the 16 matching up rows); its 16
+// waves split the 64-column chunks of H (wave w: chunks w, w + 16, ...).  Per
+// lane and chunk: one 16-byte load = 8 gate + 8 up values for each of two
+// 32-column halves.  The weight and scale loads of a wave's first chunks are
+// issued before the row's activations are staged: they do not depend on them.
 template <int ACT>
-__global__ __launch_bounds__(256) void k_gateup_gemv(FfnArgs a) {
+__global__ __launch_bounds__(64 * kGemvWaves) void k_gateup_gemv(FfnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[kMaxH];
   __shared__ float sx[kMaxH / 32];
-  __shared__ float red[4][2][16];
+  __shared__ float red[kGemvWaves][2][16];
   const uint8_t* blob;
   int t, inter;
   const int j = blockIdx.x;
@@ -52,49 +73,66 @@ __global__ __launch_bounds__(256) void k_gateup_gemv(FfnArgs a) {
     return;
   }
   const int H = a.H, G = a.G;
-  const uint16_t* xr = a.x + static_cast<size_t>(t) * H;
-  for (int c = threadIdx.x * 8; c < H; c += 256 * 8)
-    *reinterpret_cast<uint4*>(xs + c) = *reinterpret_cast<const uint4*>(xr + c);
-  __syncthreads();
   const int ng = H / G;
-  for (int g = threadIdx.x; g < ng; g += 256) {
-    float s = 0.0f;
-    for (int i = 0; i < G; ++i) s += act_to_f32<ACT>(xs[g * G + i]);
-    sx[g] = s;
-  }
-  __syncthreads();
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, kb = lane >> 4;
   const int nc = H / 64;
   const uint4* qblk = reinterpret_cast<const uint4*>(blob) + static_cast<size_t>(p) * nc * 64;
   const uint8_t* ssec = blob + blob_gu_s(H, inter);
-  float accA = 0.0f, accB = 0.0f;
-  constexpr int kBatch = 8;
-  for (int c0 = wave; c0 < nc; c0 += 4 * kBatch) {
-    uint4 q[kBatch];
+  uint4 q[kGemvBatch];
+  uint2 sv[kGemvBatch][2];
+  auto issue = [&](int c0) {
 #pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      const int c = c0 + 4 * b;
-      q[b] = (c < nc) ? qblk[static_cast<size_t>(c) * 64 + lane] : make_uint4(0, 0, 0, 0);
+    for (int b = 0; b < kGemvBatch; ++b) {
+      const int c = c0 + kGemvWaves * b;
+      if (c < nc) {   // uniform
+        q[b] = qblk[static_cast<size_t>(c) * 64 + lane];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int g = (64 * c + 32 * ks) / G;
+          sv[b][ks] = *reinterpret_cast<const uint2*>(ssec + ((static_cast<uint64_t>(p) * ng + g) * 16 + n) * 8);
+        }
+      }
     }
+  };
+  issue(wave);
+  const uint16_t* xr = a.x + static_cast<size_t>(t) * H;
+  for (int c = threadIdx.x * 8; c < H; c += 64 * kGemvWaves * 8)
+    *reinterpret_cast<uint4*>(xs + c) = *reinterpret_cast<const uint4*>(xr + c);
+  __syncthreads();
+  group_sums(H, G, 8, sx, [&](int i) {
+    const uint4 v = *reinterpret_cast<const uint4*>(xs + i);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    float s = 0.0f;
 #pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      const int c = c0 + 4 * b;
-      if (c < nc) {
+    for (int d = 0; d < 4; ++d) s += act_to_f32<ACT>(w[d] & 0xFFFFu) + act_to_f32<ACT>(w[d] >> 16);
+    return s;
+  });
+  __syncthreads();
+
+  float accA = 0.0f, accB = 0.0f;
+  for (int c0 = wave; c0 < nc; c0 += kGemvWaves * kGemvBatch) {
+    if (c0 != wave) issue(c0);
+#pragma unroll
+    for (int b = 0; b < kGemvBatch; ++b) {
+      const int c = c0 + kGemvWaves * b;
+      if (c < nc) {   // uniform
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           const int col = 64 * c + 32 * ks + 8 * kb;
           const int g = (64 * c + 32 * ks) / G;
-          const ScaleBias sb = load_sb(ssec, p, ng, g, n);
+          const uint2 v = sv[b][ks];
+          const float sA = f16_bits_to_f32(v.x & 0xFFFFu), bA = f16_bits_to_f32(v.x >> 16);
+          const float sB = f16_bits_to_f32(v.y & 0xFFFFu), bB = f16_bits_to_f32(v.y >> 16);
           const uint4 xv = *reinterpret_cast<const uint4*>(xs + col);
           const float pA = word_dot_v<ACT>(ks ? q[b].y : q[b].x, xv);
           const float pB = word_dot_v<ACT>(ks ? q[b].w : q[b].z, xv);
-          accA = fmaf(16.0f * sb.sA, pA, accA);
-          accB = fmaf(16.0f * sb.sB, pB, accB);
+          accA = fmaf(16.0f * sA, pA, accA);
+          accB = fmaf(16.0f * sB, pB, accB);
           if (kb == 0 && ((64 * c + 32 * ks) % G) == 0) {
-            accA = fmaf(sb.bA - 16.0f * sb.sA, sx[g], accA);
-            accB = fmaf(sb.bB - 16.0f * sb.sB, sx[g], accB);
+            accA = fmaf(bA - 16.0f * sA, sx[g], accA);
+            accB = fmaf(bB - 16.0f * sB, sx[g], accB);
           }
         }
       }
@@ -111,70 +149,91 @@ __global__ __launch_bounds__(256) void k_gateup_gemv(FfnArgs a) {
   __syncthreads();
   if (threadIdx.x < 16) {
     const int i = threadIdx.x;
-    const float ga = ((red[0][0][i] + red[1][0][i]) + red[2][0][i]) + red[3][0][i];
-    const float up = ((red[0][1][i] + red[1][1][i]) + red[2][1][i]) + red[3][1][i];
+    float ga = 0.0f, up = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kGemvWaves; ++w) {
+      ga += red[w][0][i];
+      up += red[w][1][i];
+    }
     const float hv = ga / (1.0f + expf(-ga)) * up;
     a.h[static_cast<size_t>(j) * a.hstride + 16 * p + i] = hv;
   }
 }
 
-// down projection.  Grid (rows, ceil(H/128)); four waves, each one 32-row
-// down pair-tile; the row's h (fp32) is staged in LDS with its group sums.
-__global__ __launch_bounds__(256) void k_down_gemv(FfnArgs a) {
+// down projection.  Grid (rows, ceil(H/128)); four 32-row down pair-tiles
+// per workgroup, four waves on each (wave w: pair-tile w % 4, chunks
+// w / 4 + 4 i of the inter dimension); the row's h (fp32) is staged in LDS
+// with its group sums after the weight and scale loads are issued.
+__global__ __launch_bounds__(64 * kGemvWaves) void k_down_gemv(FfnArgs a) {
   __shared__ __attribute__((aligned(16))) float hs[kMaxInter];
   __shared__ float sh[kMaxInter / 32];
+  __shared__ float red[4][4][2][16];   // K quarter, pair-tile, A / B, row
   const uint8_t* blob;
   int t, inter;
   const int j = blockIdx.x;
   row_source(a, j, blob, t, inter);
   const int H = a.H, G = a.G;
   if (blob == nullptr) {
-    for (int n = threadIdx.x; n < H; n += 256) a.yrow[static_cast<size_t>(j) * H + n] = 0.0f;
+    for (int n = threadIdx.x; n < H; n += 64 * kGemvWaves) a.yrow[static_cast<size_t>(j) * H + n] = 0.0f;
     return;
   }
-  const float* hr = a.h + static_cast<size_t>(j) * a.hstride;
-  for (int i = threadIdx.x * 4; i < inter; i += 256 * 4)
-    *reinterpret_cast<float4*>(hs + i) = *reinterpret_cast<const float4*>(hr + i);
-  __syncthreads();
   const int ng = inter / G;
-  for (int g = threadIdx.x; g < ng; g += 256) {
-    float s = 0.0f;
-    for (int i = 0; i < G; ++i) s += hs[g * G + i];
-    sh[g] = s;
-  }
-  __syncthreads();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int p = blockIdx.y * 4 + wave;
-  if (p * 32 >= H) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int pt4 = wave & 3, kq = wave >> 2;
+  const int p = blockIdx.y * 4 + pt4;
+  const int pc = min(p, H / 32 - 1);   // loads of a wave past the last pair-tile stay in range
   const int n = lane & 15, kb = lane >> 4;
   const int nc = inter / 64;
-  const uint4* qblk = reinterpret_cast<const uint4*>(blob + blob_d_q(H, inter)) + static_cast<size_t>(p) * nc * 64;
+  const uint4* qblk = reinterpret_cast<const uint4*>(blob + blob_d_q(H, inter)) + static_cast<size_t>(pc) * nc * 64;
   const uint8_t* ssec = blob + blob_d_s(H, inter, G);
-  float accA = 0.0f, accB = 0.0f;
-  constexpr int kBatch = 8;
-  for (int c0 = 0; c0 < nc; c0 += kBatch) {
-    uint4 q[kBatch];
+  uint4 q[kGemvBatch];
+  uint2 sv[kGemvBatch][2];
+  auto issue = [&](int c0) {
 #pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      const int c = c0 + b;
-      q[b] = (c < nc) ? qblk[static_cast<size_t>(c) * 64 + lane] : make_uint4(0, 0, 0, 0);
+    for (int b = 0; b < kGemvBatch; ++b) {
+      const int c = c0 + 4 * b;
+      if (c < nc) {   // uniform
+        q[b] = qblk[static_cast<size_t>(c) * 64 + lane];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int g = (64 * c + 32 * ks) / G;
+          sv[b][ks] = *reinterpret_cast<const uint2*>(ssec + ((static_cast<uint64_t>(pc) * ng + g) * 16 + n) * 8);
+        }
+      }
     }
+  };
+  issue(kq);
+  const float* hr = a.h + static_cast<size_t>(j) * a.hstride;
+  for (int i = threadIdx.x * 4; i < inter; i += 64 * kGemvWaves * 4)
+    *reinterpret_cast<float4*>(hs + i) = *reinterpret_cast<const float4*>(hr + i);
+  __syncthreads();
+  group_sums(inter, G, 4, sh, [&](int i) {
+    const float4 v = *reinterpret_cast<const float4*>(hs + i);
+    return (v.x + v.y) + (v.z + v.w);
+  });
+  __syncthreads();
+  float accA = 0.0f, accB = 0.0f;
+  for (int c0 = kq; c0 < nc; c0 += 4 * kGemvBatch) {
+    if (c0 != kq) issue(c0);
 #pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      const int c = c0 + b;
-      if (c < nc) {
+    for (int b = 0; b < kGemvBatch; ++b) {
+      const int c = c0 + 4 * b;
+      if (c < nc) {   // uniform
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           const int col = 64 * c + 32 * ks + 8 * kb;
           const int g = (64 * c + 32 * ks) / G;
-          const ScaleBias sb = load_sb(ssec, p, ng, g, n);
+          const uint2 v = sv[b][ks];
+          const float sA = f16_bits_to_f32(v.x & 0xFFFFu), bA = f16_bits_to_f32(v.x >> 16);
+          const float sB = f16_bits_to_f32(v.y & 0xFFFFu), bB = f16_bits_to_f32(v.y >> 16);
           const float pA = word_dot_q(ks ? q[b].y : q[b].x, hs + col);
           const float pB = word_dot_q(ks ? q[b].w : q[b].z, hs + col);
-          accA = fmaf(sb.sA, pA, accA);
-          accB = fmaf(sb.sB, pB, accB);
+          accA = fmaf(sA, pA, accA);
+          accB = fmaf(sB, pB, accB);
           if (kb == 0 && ((64 * c + 32 * ks) % G) == 0) {
-            accA = fmaf(sb.bA, sh[g], accA);
-            accB = fmaf(sb.bB, sh[g], accB);
+            accA = fmaf(bA, sh[g], accA);
+            accB = fmaf(bB, sh[g], accB);
           }
         }
       }
@@ -185,9 +244,17 @@ __global__ __launch_bounds__(256) void k_down_gemv(FfnArgs a) {
   accB += __shfl_xor(accB, 16, kWave);
   accB += __shfl_xor(accB, 32, kWave);
   if (kb == 0) {
-    float* yr = a.yrow + static_cast<size_t>(j) * H + 32 * p;
-    yr[n] = accA;
-    yr[16 + n] = accB;
+    red[kq][pt4][0][n] = accA;
+    red[kq][pt4][1][n] = accB;
+  }
+  __syncthreads();
+  if (threadIdx.x < 128) {
+    const int pq = threadIdx.x >> 5, half = (threadIdx.x >> 4) & 1, r = threadIdx.x & 15;
+    const int pp = blockIdx.y * 4 + pq;
+    if (pp * 32 < H) {
+      const float v = ((red[0][pq][half][r] + red[1][pq][half][r]) + red[2][pq][half][r]) + red[3][pq][half][r];
+      a.yrow[static_cast<size_t>(j) * H + 32 * pp + 16 * half + r] = v;
+    }
   }
 }
 
@@ -345,15 +412,15 @@ __global__ __launch_bounds__(256) void k_epilogue(const float* __restrict__ y, f
 hipError_t launch_gateup_gemv(int act, const FfnArgs& a, hipStream_t s) {
   const int rows = a.T * a.K + (a.Is > 0 ? a.T : 0);
   dim3 grid(rows, (a.hstride + 15) / 16);
-  if (act == 2) hipLaunchKernelGGL(k_gateup_gemv<2>, grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(k_gateup_gemv<1>, grid, dim3(256), 0, s, a);
+  if (act == 2) hipLaunchKernelGGL(k_gateup_gemv<2>, grid, dim3(64 * kGemvWaves), 0, s, a);
+  else hipLaunchKernelGGL(k_gateup_gemv<1>, grid, dim3(64 * kGemvWaves), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_down_gemv(const FfnArgs& a, hipStream_t s) {
   const int rows = a.T * a.K + (a.Is > 0 ? a.T : 0);
   dim3 grid(rows, (a.H + 127) / 128);
-  hipLaunchKernelGGL(k_down_gemv, grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_down_gemv, grid, dim3(64 * kGemvWaves), 0, s, a);
   return hipGetLastError();
 }
 
