@@ -275,7 +275,7 @@ def run_pool(args):
            "h2d_GBps": round(st["bytes_h2d"] / elapsed / 1e9, 2),
            "config": {"workload": f"pool80: {L} layers x {E} experts as pinned host blobs of {stride} B, "
                                   f"{S} HBM slots per layer, batch 1, {steps} steps, router bias re-drawn every "
-                                  f"{wl.drift_period} steps, router weights x2"},
+                                  f"{wl.drift_period} steps, router weights x3"},
            "data": "synthetic (seeded)"}
     pool.close()
     print(json.dumps(out))

@@ -13,7 +13,7 @@ Workloads (shapes from the pages' two model sizes: 8 of 256 experts for the
   bat80    dec80 weights, T=64, Zipf exponent 1.3
   pool80   dec80 weights as pinned host blobs, 128 HBM slots per layer,
            T=1 for 256 steps, bias permutation redrawn every 32 steps,
-           router weights x2 (logit noise sigma 2)
+           router weights x3 (logit noise sigma 3; measured hit rate 66%)
 
 Expert weights (the bulk: 43.5 GB at the 80B shape) come from Philox4x32-10
 so that any single expert can be regenerated alone, here or on the GPU:
@@ -84,7 +84,7 @@ DEC80 = Workload("dec80", 2048, 512, 10, 512, 512, 64, 1, 48, "bf16", 2, 102, 0.
                  1.0 / math.sqrt(2048), 1.1)
 BAT80 = dataclasses.replace(DEC80, name="bat80", tokens=64, token_seed=103, zipf_s=1.3)
 POOL80 = dataclasses.replace(DEC80, name="pool80", token_seed=104, slots_per_layer=128, steps=256,
-                             drift_period=32, drift_seed=105, router_sigma=2.0 / math.sqrt(2048))
+                             drift_period=32, drift_seed=105, router_sigma=3.0 / math.sqrt(2048))
 WORKLOADS = {w.name: w for w in (TINY, DEC35, DEC80, BAT80, POOL80)}
 
 
