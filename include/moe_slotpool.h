@@ -7,7 +7,11 @@
  * how-it-works list and prior-art paragraph; creativeainews explainer, "How
  * Expert Streaming Works"), one read per fixed-stride expert blob.  Here the
  * backing store is pinned host memory and a miss is one host-to-device copy
- * on a side stream.  The pages give no formula; this pool's policy:
+ * on a side stream: by default one kernel per acquire that reads the missed
+ * blobs straight from the pinned host memory over the host link (many
+ * compute units keep more reads in flight than one copy engine does), or,
+ * with MOE_POOL_DMA_COPY or when the host memory has no device mapping, one
+ * hipMemcpyAsync per miss.  The pages give no formula; this pool's policy:
  *
  *  - per layer, slots_per_layer slots of blob_stride bytes in device_slab;
  *  - every resident expert carries (count, last_use); counts are halved
@@ -39,6 +43,7 @@ extern "C" {
 typedef struct moe_slotpool moe_slotpool;
 
 #define MOE_POOL_HOST_ONLY 1u /* policy only: no copies, no events, no device writes */
+#define MOE_POOL_DMA_COPY 2u  /* copy misses with hipMemcpyAsync (a copy engine) instead of the copy kernel */
 
 typedef struct {
   int32_t n_layers, n_experts, slots_per_layer, aging_period;

@@ -14,6 +14,7 @@ MOE_F16, MOE_BF16 = 1, 2
 MOE_PATH_AUTO, MOE_PATH_GEMV, MOE_PATH_GROUPED = 0, 1, 2
 MOE_GEMV_MAX_ROWS = 32
 MOE_POOL_HOST_ONLY = 1
+MOE_POOL_DMA_COPY = 2
 MOE_TIME_GATEUP, MOE_TIME_DOWN, MOE_TIME_ROUTER = 0, 1, 2
 
 STATUS_NAMES = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_ESHAPE", -3: "MOE_EWORKSPACE", -4: "MOE_EHIP",

@@ -13,8 +13,8 @@ import dataclasses
 import numpy as np
 import torch
 
-from ._lib import (MOE_BF16, MOE_F16, MOE_PATH_AUTO, MOE_POOL_HOST_ONLY, LayerDesc, LayerWeights,  # noqa: F401
-                   SlotPoolConfig, SlotPoolStats, check, lib)
+from ._lib import (MOE_BF16, MOE_F16, MOE_PATH_AUTO, MOE_POOL_DMA_COPY, MOE_POOL_HOST_ONLY, LayerDesc,  # noqa: F401
+                   LayerWeights, SlotPoolConfig, SlotPoolStats, check, lib)
 
 __all__ = ["Desc", "Layer", "blob_bytes", "pack_expert", "workspace_bytes", "workspace", "route", "permute",
            "expert_ffn", "layer_forward", "stack_epilogue", "stack_forward", "StackGraph", "synth_fill_experts",
@@ -200,11 +200,11 @@ class SlotPool:
     """Bounded HBM slot pool (include/moe_slotpool.h)."""
 
     def __init__(self, n_layers, n_experts, slots, aging_period, blob_stride=0, blob_bytes_=0, host_blobs=None,
-                 device_slab=None, device_offsets=None, copy_stream=None, host_only=False):
+                 device_slab=None, device_offsets=None, copy_stream=None, host_only=False, dma_copy=False):
         cfg = SlotPoolConfig(n_layers, n_experts, slots, aging_period, blob_stride, blob_bytes_, _ptr(host_blobs),
                              _ptr(device_slab), _ptr(device_offsets),
                              None if copy_stream is None else _stream(copy_stream),
-                             MOE_POOL_HOST_ONLY if host_only else 0)
+                             (MOE_POOL_HOST_ONLY if host_only else 0) | (MOE_POOL_DMA_COPY if dma_copy else 0))
         h = C.c_void_p()
         check(lib().slotpool_create(C.byref(cfg), C.byref(h)))
         self._h = h

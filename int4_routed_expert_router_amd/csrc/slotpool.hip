@@ -30,6 +30,40 @@ __global__ void k_set_offsets(uint64_t* table, OffsetBatch b) {
   if (i < b.n) table[b.expert[i]] = b.offset[i];
 }
 
+// Copy of up to kOffsetBatch missed blobs from mapped pinned host memory into
+// their slots: blockIdx.y = miss, blockIdx.x = contiguous slice of the blob.
+// Each thread keeps kCopyDepth 16-byte host reads in flight.
+constexpr int kCopySlices = 64;
+constexpr int kCopyDepth = 4;
+struct CopyBatch {
+  int32_t n;
+  uint64_t src[kOffsetBatch];   // byte offsets from the host base
+  uint64_t dst[kOffsetBatch];   // byte offsets from the device slab base
+};
+__global__ __launch_bounds__(256) void k_copy_blobs(const uint8_t* __restrict__ host, uint8_t* __restrict__ dev,
+                                                    uint64_t bytes, CopyBatch b) {
+  const int i = blockIdx.y;
+  if (i >= b.n) return;
+  const uint4* src = reinterpret_cast<const uint4*>(host + b.src[i]);
+  uint4* dst = reinterpret_cast<uint4*>(dev + b.dst[i]);
+  const uint64_t n16 = bytes / 16;
+  const uint64_t per = (n16 + kCopySlices - 1) / kCopySlices;
+  const uint64_t k0 = blockIdx.x * per;
+  const uint64_t k1 = k0 + per < n16 ? k0 + per : n16;
+  for (uint64_t k = k0 + threadIdx.x; k < k1; k += kCopyDepth * 256) {
+    uint4 v[kCopyDepth];
+#pragma unroll
+    for (int d = 0; d < kCopyDepth; ++d)
+      if (k + d * 256 < k1) v[d] = src[k + d * 256];
+#pragma unroll
+    for (int d = 0; d < kCopyDepth; ++d)
+      if (k + d * 256 < k1) dst[k + d * 256] = v[d];
+  }
+  // a tail of fewer than 16 bytes, by one thread
+  if (blockIdx.x == 0 && threadIdx.x == 0)
+    for (uint64_t t = n16 * 16; t < bytes; ++t) (dev + b.dst[i])[t] = (host + b.src[i])[t];
+}
+
 }  // namespace
 
 struct moe_slotpool {
@@ -39,6 +73,7 @@ struct moe_slotpool {
   std::vector<uint8_t> released_recorded;
   uint64_t bytes_h2d = 0;
   std::vector<moe::PoolEvent> events;
+  const uint8_t* host_dev = nullptr;   // device mapping of host_blobs (copy kernel), or null (copy engine)
   moe_slotpool(const moe_slotpool_config& c)
       : cfg(c), core(c.n_layers, c.n_experts, c.slots_per_layer, c.aging_period) {}
   bool host_only() const { return (cfg.flags & MOE_POOL_HOST_ONLY) != 0; }
@@ -56,7 +91,7 @@ moe_status slotpool_create(const moe_slotpool_config* c, moe_slotpool** out) {
                      c->n_experts, c->slots_per_layer, c->aging_period);
   if (c->slots_per_layer > c->n_experts)
     return set_error(MOE_ESHAPE, "slots_per_layer=%d exceeds n_experts=%d", c->slots_per_layer, c->n_experts);
-  if (c->flags & ~MOE_POOL_HOST_ONLY) return set_error(MOE_EINVAL, "unknown flags 0x%x", c->flags);
+  if (c->flags & ~(MOE_POOL_HOST_ONLY | MOE_POOL_DMA_COPY)) return set_error(MOE_EINVAL, "unknown flags 0x%x", c->flags);
   const bool host_only = (c->flags & MOE_POOL_HOST_ONLY) != 0;
   if (!host_only) {
     if (c->blob_stride == 0 || c->blob_stride % 256 || c->blob_bytes == 0 || c->blob_bytes > c->blob_stride)
@@ -72,6 +107,13 @@ moe_status slotpool_create(const moe_slotpool_config* c, moe_slotpool** out) {
     p->ready.assign(c->n_layers, nullptr);
     p->released.assign(c->n_layers, nullptr);
     p->released_recorded.assign(c->n_layers, 0);
+    if (!(c->flags & MOE_POOL_DMA_COPY)) {
+      void* dev = nullptr;
+      if (hipHostGetDevicePointer(&dev, const_cast<uint8_t*>(c->host_blobs), 0) == hipSuccess && dev != nullptr)
+        p->host_dev = static_cast<const uint8_t*>(dev);
+      else
+        (void)hipGetLastError();   // not mapped: the copy engine path is used
+    }
     for (int l = 0; l < c->n_layers; ++l) {
       hipError_t e1 = hipEventCreateWithFlags(&p->ready[l], hipEventDisableTiming);
       hipError_t e2 = hipEventCreateWithFlags(&p->released[l], hipEventDisableTiming);
@@ -113,13 +155,28 @@ moe_status slotpool_acquire(moe_slotpool* p, int32_t layer, const int32_t* exper
   hipError_t e = hipSuccess;
   if (p->released_recorded[layer]) e = hipStreamWaitEvent(cs, p->released[layer], 0);  // WAR
   uint8_t* slab = p->cfg.device_slab + static_cast<uint64_t>(layer) * S * stride;
-  const uint8_t* host = p->cfg.host_blobs + static_cast<uint64_t>(layer) * E * stride;
+  const uint64_t host_off = static_cast<uint64_t>(layer) * E * stride;
+  const uint8_t* host = p->cfg.host_blobs + host_off;
   OffsetBatch batch{};
+  CopyBatch copies{};
+  auto flush_copies = [&]() {
+    if (copies.n == 0) return;
+    hipLaunchKernelGGL(k_copy_blobs, dim3(kCopySlices, copies.n), dim3(256), 0, cs, p->host_dev + host_off, slab,
+                       p->cfg.blob_bytes, copies);
+    copies.n = 0;
+    if (e == hipSuccess) e = hipGetLastError();
+  };
   for (int i = 0; i < n && e == hipSuccess; ++i) {
     const moe::PoolEvent& ev = p->events[i];
     if (ev.hit) continue;
-    e = hipMemcpyAsync(slab + static_cast<uint64_t>(ev.slot) * stride, host + static_cast<uint64_t>(ev.expert) * stride,
-                       p->cfg.blob_bytes, hipMemcpyHostToDevice, cs);
+    if (p->host_dev) {
+      copies.src[copies.n] = static_cast<uint64_t>(ev.expert) * stride;
+      copies.dst[copies.n] = static_cast<uint64_t>(ev.slot) * stride;
+      if (++copies.n == kOffsetBatch) flush_copies();
+    } else {
+      e = hipMemcpyAsync(slab + static_cast<uint64_t>(ev.slot) * stride, host + static_cast<uint64_t>(ev.expert) * stride,
+                         p->cfg.blob_bytes, hipMemcpyHostToDevice, cs);
+    }
     p->bytes_h2d += p->cfg.blob_bytes;
     batch.expert[batch.n] = ev.expert;
     batch.offset[batch.n] = static_cast<uint64_t>(ev.slot) * stride;
@@ -130,6 +187,7 @@ moe_status slotpool_acquire(moe_slotpool* p, int32_t layer, const int32_t* exper
       if (e == hipSuccess) e = hipGetLastError();
     }
   }
+  if (e == hipSuccess) flush_copies();
   if (e == hipSuccess && batch.n > 0) {
     hipLaunchKernelGGL(k_set_offsets, dim3(1), dim3(kOffsetBatch), 0, ks,
                        p->cfg.device_offsets + static_cast<uint64_t>(layer) * E, batch);

@@ -17,7 +17,8 @@ POOLED = dataclasses.replace(synth.TINY, name="pooled", n_experts=16, top_k=3, t
                              weight_seed=41, token_seed=141, router_sigma=0.05, zipf_s=1.1)
 
 
-def test_streamed_layers_equal_resident_and_trace_matches_simulator():
+@pytest.mark.parametrize("dma_copy", [False, True], ids=["copy_kernel", "copy_engine"])
+def test_streamed_layers_equal_resident_and_trace_matches_simulator(dma_copy):
     import torch
     from int4_routed_expert_router_amd import api
     wl = POOLED
@@ -33,7 +34,7 @@ def test_streamed_layers_equal_resident_and_trace_matches_simulator():
     offsets = torch.zeros(L * E, dtype=torch.int64, device="cuda")
     copy_stream = torch.cuda.Stream()
     compute = torch.cuda.current_stream()
-    pool = api.SlotPool(L, E, slots, period, stride, blob, host, slab, offsets, copy_stream)
+    pool = api.SlotPool(L, E, slots, period, stride, blob, host, slab, offsets, copy_stream, dma_copy=dma_copy)
     sim = PoolSim(L, E, slots, period, blob_bytes=blob)
     desc = desc_for(wl, path=1)
     ws = api.workspace(desc, 1)
