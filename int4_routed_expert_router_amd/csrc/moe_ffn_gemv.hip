@@ -50,26 +50,36 @@ __device__ __forceinline__ void group_sums(int n_vals, int G, int per, float* ou
 // work, not the weight bytes, sets the time, so it is spread thin.
 constexpr int kGemvWaves = 16;
 constexpr int kGemvBatch = 4;   // chunks whose loads a wave issues together
+// gate/up splits the hidden dimension over kGemvSplit workgroups per
+// pair-tile (more, smaller workgroups even out the bytes per compute unit);
+// each writes its partial gate and up sums to h as
+// [kGemvSplit][rows][hstride][2], and the down kernel adds the splits in
+// order and applies SwiGLU while it stages h.
+constexpr int kGemvGateUpWaves = 8;
 
-// gate/up + SwiGLU.  Grid (rows, max(I,Is)/16); one workgroup = one row j and
-// one gate/up pair-tile p (16 gate rows + the 16 matching up rows); its 16
-// waves split the 64-column chunks of H (wave w: chunks w, w + 16, ...).  Per
-// lane and chunk: one 16-byte load = 8 gate + 8 up values for each of two
-// 32-column halves.  The weight and scale loads of a wave's first chunks are
-// issued before the row's activations are staged: they do not depend on them.
+// gate/up partial sums.  Grid (rows, max(I,Is)/16, kGemvSplit); one
+// workgroup = one row j, one gate/up pair-tile p (16 gate rows + the 16
+// matching up rows) and one split z of the 64-column chunks of H (chunks
+// z, z + S, ...); its 8 waves take every 8th chunk of the split.  Per lane and
+// chunk: one 16-byte load = 8 gate + 8 up values for each of two 32-column
+// halves.  The weight and scale loads of a wave's first chunks are issued
+// before the row's activations are staged: they do not depend on them.
 template <int ACT>
-__global__ __launch_bounds__(64 * kGemvWaves) void k_gateup_gemv(FfnArgs a) {
+__global__ __launch_bounds__(64 * kGemvGateUpWaves) void k_gateup_gemv(FfnArgs a) {
+  constexpr int NW = kGemvGateUpWaves;
   __shared__ __attribute__((aligned(16))) uint16_t xs[kMaxH];
   __shared__ float sx[kMaxH / 32];
-  __shared__ float red[kGemvWaves][2][16];
+  __shared__ float red[NW][2][16];
   const uint8_t* blob;
   int t, inter;
   const int j = blockIdx.x;
   row_source(a, j, blob, t, inter);
-  const int p = blockIdx.y;
+  const int p = blockIdx.y, z = blockIdx.z;
   if (p * 16 >= inter) return;
+  const int rows = gridDim.x;
+  float* part = a.h + ((static_cast<size_t>(z) * rows + j) * a.hstride + 16 * p) * 2;
   if (blob == nullptr) {
-    if (threadIdx.x < 16) a.h[static_cast<size_t>(j) * a.hstride + 16 * p + threadIdx.x] = 0.0f;
+    if (threadIdx.x < 32) part[threadIdx.x] = 0.0f;
     return;
   }
   const int H = a.H, G = a.G;
@@ -82,10 +92,12 @@ __global__ __launch_bounds__(64 * kGemvWaves) void k_gateup_gemv(FfnArgs a) {
   const uint8_t* ssec = blob + blob_gu_s(H, inter);
   uint4 q[kGemvBatch];
   uint2 sv[kGemvBatch][2];
-  auto issue = [&](int c0) {
+  // chunk of the wave's i-th step: z + S (wave + NW i)
+  auto chunk = [&](int i) { return z + kGemvSplit * (wave + NW * i); };
+  auto issue = [&](int i0) {
 #pragma unroll
     for (int b = 0; b < kGemvBatch; ++b) {
-      const int c = c0 + kGemvWaves * b;
+      const int c = chunk(i0 + b);
       if (c < nc) {   // uniform
         q[b] = qblk[static_cast<size_t>(c) * 64 + lane];
 #pragma unroll
@@ -96,9 +108,9 @@ __global__ __launch_bounds__(64 * kGemvWaves) void k_gateup_gemv(FfnArgs a) {
       }
     }
   };
-  issue(wave);
+  issue(0);
   const uint16_t* xr = a.x + static_cast<size_t>(t) * H;
-  for (int c = threadIdx.x * 8; c < H; c += 64 * kGemvWaves * 8)
+  for (int c = threadIdx.x * 8; c < H; c += 64 * NW * 8)
     *reinterpret_cast<uint4*>(xs + c) = *reinterpret_cast<const uint4*>(xr + c);
   __syncthreads();
   group_sums(H, G, 8, sx, [&](int i) {
@@ -112,11 +124,11 @@ __global__ __launch_bounds__(64 * kGemvWaves) void k_gateup_gemv(FfnArgs a) {
   __syncthreads();
 
   float accA = 0.0f, accB = 0.0f;
-  for (int c0 = wave; c0 < nc; c0 += kGemvWaves * kGemvBatch) {
-    if (c0 != wave) issue(c0);
+  for (int i0 = 0; chunk(i0) < nc; i0 += kGemvBatch) {
+    if (i0 != 0) issue(i0);
 #pragma unroll
     for (int b = 0; b < kGemvBatch; ++b) {
-      const int c = c0 + kGemvWaves * b;
+      const int c = chunk(i0 + b);
       if (c < nc) {   // uniform
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -147,23 +159,20 @@ __global__ __launch_bounds__(64 * kGemvWaves) void k_gateup_gemv(FfnArgs a) {
     red[wave][1][n] = accB;
   }
   __syncthreads();
-  if (threadIdx.x < 16) {
-    const int i = threadIdx.x;
-    float ga = 0.0f, up = 0.0f;
+  if (threadIdx.x < 32) {
+    const int i = threadIdx.x & 15, gu = threadIdx.x >> 4;
+    float v = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kGemvWaves; ++w) {
-      ga += red[w][0][i];
-      up += red[w][1][i];
-    }
-    const float hv = ga / (1.0f + expf(-ga)) * up;
-    a.h[static_cast<size_t>(j) * a.hstride + 16 * p + i] = hv;
+    for (int w = 0; w < NW; ++w) v += red[w][gu][i];
+    part[2 * i + gu] = v;
   }
 }
 
 // down projection.  Grid (rows, ceil(H/128)); four 32-row down pair-tiles
 // per workgroup, four waves on each (wave w: pair-tile w % 4, chunks
-// w / 4 + 4 i of the inter dimension); the row's h (fp32) is staged in LDS
-// with its group sums after the weight and scale loads are issued.
+// w / 4 + 4 i of the inter dimension).  After the weight and scale loads are
+// issued, the row's h = silu(gate) * up is formed in LDS from the gate/up
+// splits (added in split order), with its group sums.
 __global__ __launch_bounds__(64 * kGemvWaves) void k_down_gemv(FfnArgs a) {
   __shared__ __attribute__((aligned(16))) float hs[kMaxInter];
   __shared__ float sh[kMaxInter / 32];
@@ -204,9 +213,17 @@ __global__ __launch_bounds__(64 * kGemvWaves) void k_down_gemv(FfnArgs a) {
     }
   };
   issue(kq);
-  const float* hr = a.h + static_cast<size_t>(j) * a.hstride;
-  for (int i = threadIdx.x * 4; i < inter; i += 64 * kGemvWaves * 4)
-    *reinterpret_cast<float4*>(hs + i) = *reinterpret_cast<const float4*>(hr + i);
+  const int rows = gridDim.x;
+  for (int i = threadIdx.x; i < inter; i += 64 * kGemvWaves) {
+    float ga = 0.0f, up = 0.0f;
+#pragma unroll
+    for (int z = 0; z < kGemvSplit; ++z) {
+      const float2 v = *reinterpret_cast<const float2*>(a.h + ((static_cast<size_t>(z) * rows + j) * a.hstride + i) * 2);
+      ga += v.x;
+      up += v.y;
+    }
+    hs[i] = ga / (1.0f + expf(-ga)) * up;
+  }
   __syncthreads();
   group_sums(inter, G, 4, sh, [&](int i) {
     const float4 v = *reinterpret_cast<const float4*>(hs + i);
@@ -411,9 +428,9 @@ __global__ __launch_bounds__(256) void k_epilogue(const float* __restrict__ y, f
 
 hipError_t launch_gateup_gemv(int act, const FfnArgs& a, hipStream_t s) {
   const int rows = a.T * a.K + (a.Is > 0 ? a.T : 0);
-  dim3 grid(rows, (a.hstride + 15) / 16);
-  if (act == 2) hipLaunchKernelGGL(k_gateup_gemv<2>, grid, dim3(64 * kGemvWaves), 0, s, a);
-  else hipLaunchKernelGGL(k_gateup_gemv<1>, grid, dim3(64 * kGemvWaves), 0, s, a);
+  dim3 grid(rows, (a.hstride + 15) / 16, kGemvSplit);
+  if (act == 2) hipLaunchKernelGGL(k_gateup_gemv<2>, grid, dim3(64 * kGemvGateUpWaves), 0, s, a);
+  else hipLaunchKernelGGL(k_gateup_gemv<1>, grid, dim3(64 * kGemvGateUpWaves), 0, s, a);
   return hipGetLastError();
 }
 

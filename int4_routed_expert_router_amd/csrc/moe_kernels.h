@@ -24,7 +24,8 @@ struct FfnArgs {
   uint64_t stride;            // blob stride when offsets == nullptr
   const uint64_t* offsets;    // [E] byte offsets or nullptr
   const uint8_t* shared;      // shared blob or nullptr
-  float* h;                   // [rows][hstride] SwiGLU activations (grouped: hi, lo bf16 planes)
+  float* h;                   // grouped: h as fp16 hi, lo planes [2][rows][hstride];
+                              // GEMV: partial (gate, up) sums [kGemvSplit][rows][hstride][2] fp32
   float* yrow;                // [rows][H] per-row expert outputs (unweighted)
   // grouped family
   const int32_t* units;       // [n_units][kUnitInts] unit records (see UnitPlan)
@@ -50,6 +51,7 @@ struct UnitPlan {
 // Logical workgroup w takes the contiguous part [w L / W, (w+1) L / W) of the
 // list of all L tiles (W = kGridTiles, a power of two).
 constexpr int kGridTiles = 256;
+constexpr int kGemvSplit = 2;   // GEMV gate/up: hidden-dimension splits per pair-tile
 constexpr int kGridTilesLog2 = 8;
 constexpr int kSubTokens = 16;
 // limits of the grouped family (larger shapes use the GEMV family)

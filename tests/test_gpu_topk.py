@@ -15,8 +15,11 @@ from oracle import moe_oracle as mo
 pytestmark = pytest.mark.gpu
 
 # (E, K, T, H): per-lane depths 1, 2, 4, 8 and 16; E = 100 leaves the last
-# lane entries partly empty; T = 70 spans several top-k workgroups
-CASES = [(20, 20, 7, 64), (100, 10, 9, 128), (256, 8, 70, 64), (512, 10, 64, 128), (1000, 64, 5, 64)]
+# lane entries partly empty; T = 70 spans several top-k workgroups.  From 16
+# tokens the router runs on the matrix cores over hidden-dimension slices:
+# 2 slices at (256, 70, 64) and (512, 64, 128), 4 at (512, 16, 256).
+CASES = [(20, 20, 7, 64), (100, 10, 9, 128), (256, 8, 70, 64), (512, 10, 64, 128), (512, 10, 16, 256),
+         (1000, 64, 5, 64)]
 
 F16_BITS = {-1: 0xBC00, 0: 0x0000, 1: 0x3C00}
 BF16_BITS = {-1: 0xBF80, 0: 0x0000, 1: 0x3F80}
