@@ -361,7 +361,24 @@ __global__ __launch_bounds__(512) void k_gateup_tiles(FfnArgs a) {
   // ---- activations: raw prefetch (xr) of unit pu, operands (xa) of unit xu
   uint4 xr[kSlot][2];   // raw activations of the prefetched unit
   uint4 xa[kSlot][2];   // A operands of the current unit (this wave's chunks)
-  float csv[kSlot][kHalves][4];   // column sums for the lane's output rows 4kb..4kb+3
+  // column sums for the lane's output rows 4kb..4kb+3: in registers, or for
+  // group 32 (two groups per chunk, the register-heaviest case) in this
+  // wave's part of LDS, read back per chunk
+  constexpr bool kSumsInLds = G == 32;
+  float csv[kSumsInLds ? 1 : kSlot][kHalves][4];
+  __shared__ __attribute__((aligned(16))) float csl[kSumsInLds ? kWaves : 1][kSlot][kHalves][kSub];
+  auto sums_of = [&](int j, int hh, float* out) {
+    if constexpr (kSumsInLds) {
+      const float4 v = *reinterpret_cast<const float4*>(&csl[wave][j][hh][4 * kb]);
+      out[0] = v.x;
+      out[1] = v.y;
+      out[2] = v.z;
+      out[3] = v.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) out[i] = csv[j][hh][i];
+    }
+  };
   int pu = -1, prow0 = 0, pmc = 0;
   int xu = -1, row0 = 0, mc = 0;
   // issue the activation loads of unit u (record rec) into xr
@@ -408,9 +425,13 @@ __global__ __launch_bounds__(512) void k_gateup_tiles(FfnArgs a) {
         v = __float_as_uint(__uint_as_float(static_cast<uint32_t>(p16[0])) + __uint_as_float(static_cast<uint32_t>(p16[1])));
         const auto p32 = __builtin_amdgcn_permlane32_swap(static_cast<int>(v), static_cast<int>(v), false, false);
         v = __float_as_uint(__uint_as_float(static_cast<uint32_t>(p32[0])) + __uint_as_float(static_cast<uint32_t>(p32[1])));
+        if constexpr (kSumsInLds) {
+          if (kb == 0) csl[wave][j][hh][n] = __uint_as_float(v);   // token n (lanes kb > 0 hold the same)
+        } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          csv[j][hh][i] = __uint_as_float(static_cast<uint32_t>(__shfl(static_cast<int>(v), 4 * kb + i, kWave)));
+          for (int i = 0; i < 4; ++i)
+            csv[j][hh][i] = __uint_as_float(static_cast<uint32_t>(__shfl(static_cast<int>(v), 4 * kb + i, kWave)));
+        }
       }
     }
     xu = pu;
@@ -495,12 +516,21 @@ __global__ __launch_bounds__(512) void k_gateup_tiles(FfnArgs a) {
       load_slot<G>(s, qnx, snx, min(c, nc - 1));
       Prod p;
       if (c < nc) p = chunk_mfma<G, false>(d, xa[j][0], xa[j][1], xa[j][0], xa[j][1]);
-      if (j > 0 && c - kWaves < nc) chunk_scale<G>(pp, pk, csv[j - 1][0], csv[j - 1][kHalves - 1], accA, accB, biasA, biasB);
+      if (j > 0 && c - kWaves < nc) {
+        float s0[4], s1[4];
+        sums_of(j - 1, 0, s0);
+        sums_of(j - 1, kHalves - 1, s1);
+        chunk_scale<G>(pp, pk, s0, s1, accA, accB, biasA, biasB);
+      }
       pp = p;
       pk = coef_of(d);
     }
-    if (wave + kWaves * (kSlot - 1) < nc)
-      chunk_scale<G>(pp, pk, csv[kSlot - 1][0], csv[kSlot - 1][kHalves - 1], accA, accB, biasA, biasB);
+    if (wave + kWaves * (kSlot - 1) < nc) {
+      float s0[4], s1[4];
+      sums_of(kSlot - 1, 0, s0);
+      sums_of(kSlot - 1, kHalves - 1, s1);
+      chunk_scale<G>(pp, pk, s0, s1, accA, accB, biasA, biasB);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       red[pb][hf][wave][0][i][lane] = fmaf(kQScale, accA[i], biasA[i]);
