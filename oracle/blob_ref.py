@@ -31,6 +31,12 @@ starts lane l's four little-endian 32-bit words (n = l % 16, kb = l // 16):
 
 and value j of a word sits in bits [4p, 4p+4) with p = (j >> 1) + 4*(j & 1).
 
+int8 experts (bits = 8) double the value sections: GU_Q is 2*I*H bytes and
+D_Q is I*H; the scale sections follow at 3*I*H and 3*I*H + 8*I*H/G.  A chunk
+is then a 2048-byte block, lane l owns bytes 32*l..32*l+31 = eight words:
+words 2m, 2m+1 hold what word m holds above (m = 0..3), value j as byte j of
+the 8 bytes in natural order.
+
 The scale/bias sections hold, for pair-tile p, group g (G columns of the
 input dimension) and n < 16, eight bytes at ((p * n_groups + g) * 16 + n) * 8:
 four fp16 values [s_A, b_A, s_B, b_B] for row n of tiles A and B.
@@ -50,18 +56,20 @@ def check_shape(hidden: int, inter: int, group: int) -> None:
         raise ValueError("group must be 32, 64 or 128 and divide hidden and inter")
 
 
-def section_offsets(hidden: int, inter: int, group: int):
+def section_offsets(hidden: int, inter: int, group: int, bits: int = 4):
     check_shape(hidden, inter, group)
+    if bits not in (4, 8):
+        raise ValueError("bits must be 4 or 8")
     gu_q = 0
-    d_q = inter * hidden
-    gu_s = d_q + hidden * inter // 2
+    d_q = inter * hidden * bits // 4
+    gu_s = d_q + hidden * inter * bits // 8
     d_s = gu_s + 8 * inter * hidden // group
     end = d_s + 4 * hidden * inter // group
     return dict(gu_q=gu_q, d_q=d_q, gu_s=gu_s, d_s=d_s, end=end)
 
 
-def blob_bytes(hidden: int, inter: int, group: int) -> int:
-    return section_offsets(hidden, inter, group)["end"]
+def blob_bytes(hidden: int, inter: int, group: int, bits: int = 4) -> int:
+    return section_offsets(hidden, inter, group, bits)["end"]
 
 
 def _words_to_values(words: np.ndarray) -> np.ndarray:
@@ -76,22 +84,27 @@ def _values_to_words(vals: np.ndarray) -> np.ndarray:
     return np.bitwise_or.reduce(vals.astype(np.uint32) << shifts, axis=-1).astype(np.uint32)
 
 
-def _parse_pair_tiles(raw: np.ndarray, n_pairs: int, in_dim: int):
-    """Nibble section -> (tile-A values, tile-B values), each [n_pairs*16, in_dim]."""
+def _parse_pair_tiles(raw: np.ndarray, n_pairs: int, in_dim: int, bits: int = 4):
+    """Value section -> (tile-A values, tile-B values), each [n_pairs*16, in_dim]."""
     n_chunks = in_dim // 64
-    words = raw.view("<u4").reshape(n_pairs, n_chunks, 4, 16, 4)  # p, c, kb, n, word
-    vals = _words_to_values(words)                                   # p, c, kb, n, word, j
+    if bits == 8:
+        vals = raw.reshape(n_pairs, n_chunks, 4, 16, 4, 8)            # p, c, kb, n, word pair, j
+    else:
+        words = raw.view("<u4").reshape(n_pairs, n_chunks, 4, 16, 4)  # p, c, kb, n, word
+        vals = _words_to_values(words)                                # p, c, kb, n, word, j
     vals = vals.reshape(n_pairs, n_chunks, 4, 16, 2, 2, 8)           # p, c, kb, n, tile, ks, j
     # row = (p, tile, n); column = 64c + 32ks + 8kb + j
     arr = vals.transpose(0, 4, 3, 1, 5, 2, 6)                        # p, tile, n, c, ks, kb, j
     return arr.reshape(n_pairs, 2, 16, in_dim)
 
 
-def _pack_pair_tiles(tile_a: np.ndarray, tile_b: np.ndarray, n_pairs: int, in_dim: int) -> np.ndarray:
+def _pack_pair_tiles(tile_a: np.ndarray, tile_b: np.ndarray, n_pairs: int, in_dim: int, bits: int = 4) -> np.ndarray:
     n_chunks = in_dim // 64
     both = np.stack([tile_a.reshape(n_pairs, 16, in_dim), tile_b.reshape(n_pairs, 16, in_dim)], axis=1)
     arr = both.reshape(n_pairs, 2, 16, n_chunks, 2, 4, 8)            # p, tile, n, c, ks, kb, j
     vals = arr.transpose(0, 3, 5, 2, 1, 4, 6)                        # p, c, kb, n, tile, ks, j
+    if bits == 8:
+        return np.ascontiguousarray(vals).astype(np.uint8).reshape(-1)
     words = _values_to_words(vals.reshape(n_pairs, n_chunks, 4, 16, 4, 8))
     return words.astype("<u4").view(np.uint8).reshape(-1)
 
@@ -109,17 +122,17 @@ def _pack_scales(s: np.ndarray, b: np.ndarray, n_pairs: int, n_groups: int) -> n
     return arr.view(np.uint8).reshape(-1)
 
 
-def parse_blob(buf, hidden: int, inter: int, group: int):
+def parse_blob(buf, hidden: int, inter: int, group: int, bits: int = 4):
     """Blob bytes -> dict(gate=(q,s,b), up=(q,s,b), down=(q,s,b)).
 
     gate/up q: [I, H] uint8, s/b: [I, H/G] fp16 bits; down q: [H, I], s/b: [H, I/G].
     """
-    off = section_offsets(hidden, inter, group)
+    off = section_offsets(hidden, inter, group, bits)
     raw = np.frombuffer(bytes(buf) if not isinstance(buf, np.ndarray) else buf.tobytes(), dtype=np.uint8)
     if raw.size < off["end"]:
         raise ValueError("blob too short")
-    gu = _parse_pair_tiles(raw[off["gu_q"]:off["d_q"]].copy(), inter // 16, hidden)
-    dn = _parse_pair_tiles(raw[off["d_q"]:off["gu_s"]].copy(), hidden // 32, inter)
+    gu = _parse_pair_tiles(raw[off["gu_q"]:off["d_q"]].copy(), inter // 16, hidden, bits)
+    dn = _parse_pair_tiles(raw[off["d_q"]:off["gu_s"]].copy(), hidden // 32, inter, bits)
     gs, gb = _parse_scales(raw[off["gu_s"]:off["d_s"]].copy(), inter // 16, hidden // group)
     ds, db = _parse_scales(raw[off["d_s"]:off["end"]].copy(), hidden // 32, inter // group)
     gate = (gu[:, 0].reshape(inter, hidden), gs[:, 0].reshape(inter, -1), gb[:, 0].reshape(inter, -1))
@@ -128,13 +141,13 @@ def parse_blob(buf, hidden: int, inter: int, group: int):
     return dict(gate=gate, up=up, down=down)
 
 
-def pack_blob(gate, up, down, hidden: int, inter: int, group: int) -> np.ndarray:
+def pack_blob(gate, up, down, hidden: int, inter: int, group: int, bits: int = 4) -> np.ndarray:
     """Inverse of parse_blob (used to pin the reader by round trips)."""
-    off = section_offsets(hidden, inter, group)
+    off = section_offsets(hidden, inter, group, bits)
     out = np.zeros(off["end"], dtype=np.uint8)
-    out[off["gu_q"]:off["d_q"]] = _pack_pair_tiles(np.asarray(gate[0]), np.asarray(up[0]), inter // 16, hidden)
+    out[off["gu_q"]:off["d_q"]] = _pack_pair_tiles(np.asarray(gate[0]), np.asarray(up[0]), inter // 16, hidden, bits)
     dq = np.asarray(down[0]).reshape(hidden // 32, 2, 16, inter)
-    out[off["d_q"]:off["gu_s"]] = _pack_pair_tiles(dq[:, 0], dq[:, 1], hidden // 32, inter)
+    out[off["d_q"]:off["gu_s"]] = _pack_pair_tiles(dq[:, 0], dq[:, 1], hidden // 32, inter, bits)
     ng = hidden // group
     s_gu = np.stack([np.asarray(gate[1]).reshape(inter // 16, 16, ng), np.asarray(up[1]).reshape(inter // 16, 16, ng)], 1)
     b_gu = np.stack([np.asarray(gate[2]).reshape(inter // 16, 16, ng), np.asarray(up[2]).reshape(inter // 16, 16, ng)], 1)

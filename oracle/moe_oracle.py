@@ -79,18 +79,21 @@ def f64_to_bf16_bits_rne(v) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 
-def dequant(q, s_bits, b_bits, group: int) -> np.ndarray:
+def dequant(q, s_bits, b_bits, group: int, bits: int = 4) -> np.ndarray:
     """W[r, c] = s[r, c // G] * q[r, c] + b[r, c // G] in float64.
 
-    q: [rows, cols] integers 0..15; s_bits, b_bits: [rows, cols // G] fp16
+    q: [rows, cols] integers 0..2**bits - 1 (bits 4 or 8: the pages' affine
+    int4 and int8 group quantisation); s_bits, b_bits: [rows, cols // G] fp16
     bit patterns.  Groups are G contiguous columns along the input dimension.
     """
     q = np.asarray(q)
     rows, cols = q.shape
+    if bits not in (4, 8):
+        raise ValueError("bits must be 4 or 8")
     if cols % group:
         raise ValueError("cols must be a multiple of the group size")
-    if q.min(initial=0) < 0 or q.max(initial=0) > 15:
-        raise ValueError("q must lie in 0..15")
+    if q.min(initial=0) < 0 or q.max(initial=0) > (1 << bits) - 1:
+        raise ValueError(f"q must lie in 0..{(1 << bits) - 1}")
     s = f16_bits_to_f64(s_bits)
     b = f16_bits_to_f64(b_bits)
     if s.shape != (rows, cols // group) or b.shape != s.shape:
@@ -222,9 +225,9 @@ class ExpertWeights:
         self.wd = np.asarray(wd, np.float64)
 
     @classmethod
-    def from_quant(cls, gate, up, down, group: int):
+    def from_quant(cls, gate, up, down, group: int, bits: int = 4):
         """Each of gate/up/down is a (q, s_bits, b_bits) triple."""
-        return cls(dequant(*gate, group), dequant(*up, group), dequant(*down, group))
+        return cls(dequant(*gate, group, bits), dequant(*up, group, bits), dequant(*down, group, bits))
 
 
 def combine(w_row, expert_outputs, gamma, shared_output):

@@ -14,6 +14,8 @@ Workloads (shapes from the pages' two model sizes: 8 of 256 experts for the
   pool80   dec80 weights as pinned host blobs, 128 HBM slots per layer,
            T=1 for 256 steps, bias permutation redrawn every 32 steps,
            router weights x3 (logit noise sigma 3; measured hit rate 66%)
+  dec80i8  dec80 shapes with int8 experts (the pages' other affine variant),
+           scales U(1e-4, 1e-3) so that weights span the int4 range
 
 Expert weights (the bulk: 43.5 GB at the 80B shape) come from Philox4x32-10
 so that any single expert can be regenerated alone, here or on the GPU:
@@ -23,9 +25,12 @@ so that any single expert can be regenerated alone, here or on the GPU:
             tensor 0/1/2 = gate/up/down nibbles, 3/4/5 = gate/up/down scales
   nibbles : value j = r*cols + c of a [rows, cols] matrix is bits
             [4*(j%8), 4*(j%8)+4) of word (j%32)//8 of block j//32
+  bytes   : (int8 experts) value j is bits [8*(j%4), 8*(j%4)+8) of word
+            (j%16)//4 of block j//16
   scales  : value j = r*ngroups + g takes word j%4 of block j//4,
             u = (word >> 8) * 2**-24, s = fp16_rne(fl32(fl32(u*span) + lo))
-            with fp32 constants lo and span = fl32(hi - lo); b = -8*s (exact)
+            with fp32 constants lo and span = fl32(hi - lo); b = -8*s, or
+            -128*s for int8 (exact either way)
 
 Router weights, shared-gate vectors, router bias and tokens are small and are
 drawn on the host with numpy's SeedSequence/PCG64 streams keyed by
@@ -65,16 +70,17 @@ class Workload:
     steps: int = 1
     drift_period: int = 0
     drift_seed: int = 0
+    bits: int = 4             # expert weight width: 4 or 8
 
     @property
     def blob_bytes(self) -> int:
         h, i, g = self.hidden, self.inter, self.group
-        return 3 * i * h // 2 + 12 * i * h // g
+        return 3 * i * h * self.bits // 8 + 12 * i * h // g
 
     @property
     def shared_blob_bytes(self) -> int:
         h, i, g = self.hidden, self.shared_inter, self.group
-        return 3 * i * h // 2 + 12 * i * h // g
+        return 3 * i * h * self.bits // 8 + 12 * i * h // g
 
 
 TINY = Workload("tiny", 256, 16, 2, 64, 64, 32, 4, 1, "f16", 0, 100, 0.002, 0.01, 0.02, 0.0)
@@ -85,7 +91,8 @@ DEC80 = Workload("dec80", 2048, 512, 10, 512, 512, 64, 1, 48, "bf16", 2, 102, 0.
 BAT80 = dataclasses.replace(DEC80, name="bat80", tokens=64, token_seed=103, zipf_s=1.3)
 POOL80 = dataclasses.replace(DEC80, name="pool80", token_seed=104, slots_per_layer=128, steps=256,
                              drift_period=32, drift_seed=105, router_sigma=3.0 / math.sqrt(2048))
-WORKLOADS = {w.name: w for w in (TINY, DEC35, DEC80, BAT80, POOL80)}
+DEC80I8 = dataclasses.replace(DEC80, name="dec80i8", bits=8, scale_lo=1e-4, scale_hi=1e-3)
+WORKLOADS = {w.name: w for w in (TINY, DEC35, DEC80, BAT80, POOL80, DEC80I8)}
 
 
 # ---------------------------------------------------------------------------
@@ -122,8 +129,20 @@ def _nibbles(seed: int, layer: int, expert: int, tensor: int, rows: int, cols: i
     return vals.reshape(rows, cols).astype(np.uint8)
 
 
+def _bytes(seed: int, layer: int, expert: int, tensor: int, rows: int, cols: int) -> np.ndarray:
+    n = rows * cols
+    if n % 16:
+        raise ValueError("rows*cols must be a multiple of 16")
+    blocks = np.arange(n // 16, dtype=np.uint32)
+    words = philox4x32_10(blocks, expert, tensor, 0, seed & 0xFFFFFFFF, layer)
+    w = np.stack(words, axis=1)                                   # [blocks, 4]
+    shifts = (8 * np.arange(4)).astype(np.uint32)
+    vals = (w[:, :, None] >> shifts) & np.uint32(0xFF)            # [blocks, 4, 4]
+    return vals.reshape(rows, cols).astype(np.uint8)
+
+
 def _scales(seed: int, layer: int, expert: int, tensor: int, rows: int, ngroups: int,
-            lo: float, hi: float):
+            lo: float, hi: float, bits: int = 4):
     n = rows * ngroups
     nblocks = (n + 3) // 4
     blocks = np.arange(nblocks, dtype=np.uint32)
@@ -133,15 +152,16 @@ def _scales(seed: int, layer: int, expert: int, tensor: int, rows: int, ngroups:
     span32 = np.float32(hi - lo)
     s32 = (u * span32).astype(np.float32) + lo32
     s16 = s32.astype(np.float32).astype(np.float16)
-    b16 = (s16 * np.float16(-8.0)).astype(np.float16)            # exact: power-of-two multiple
+    b16 = (s16 * np.float16(-float(1 << (bits - 1)))).astype(np.float16)   # exact: power-of-two multiple
     return s16.view(np.uint16).reshape(rows, ngroups), b16.view(np.uint16).reshape(rows, ngroups)
 
 
 def expert_raw(wl: Workload, layer: int, expert: int, shared: bool = False, seed: int | None = None):
     """Raw quantised tensors of one expert: dict(gate=(q,s,b), up=..., down=...).
 
-    gate/up q: [I, H] uint8 in 0..15; down q: [H, I]; s, b: fp16 bit patterns
-    [rows, cols // G].  ``expert`` is ignored for the shared expert (id E).
+    gate/up q: [I, H] uint8 in 0..2**bits - 1; down q: [H, I]; s, b: fp16 bit
+    patterns [rows, cols // G].  ``expert`` is ignored for the shared expert
+    (id E).
     """
     seed = wl.weight_seed if seed is None else seed
     h = wl.hidden
@@ -152,8 +172,8 @@ def expert_raw(wl: Workload, layer: int, expert: int, shared: bool = False, seed
     for name, tq, ts, rows, cols in (("gate", T_GATE_Q, T_GATE_S, i, h),
                                      ("up", T_UP_Q, T_UP_S, i, h),
                                      ("down", T_DOWN_Q, T_DOWN_S, h, i)):
-        q = _nibbles(seed, layer, eid, tq, rows, cols)
-        s, b = _scales(seed, layer, eid, ts, rows, cols // g, wl.scale_lo, wl.scale_hi)
+        q = (_bytes if wl.bits == 8 else _nibbles)(seed, layer, eid, tq, rows, cols)
+        s, b = _scales(seed, layer, eid, ts, rows, cols // g, wl.scale_lo, wl.scale_hi, wl.bits)
         out[name] = (q, s, b)
     return out
 

@@ -96,3 +96,51 @@ def test_value_order_in_word():
     assert blob_ref.NIBBLE_OF_VALUE.tolist() == [0, 4, 1, 5, 2, 6, 3, 7]
     words = np.array([0x76543210], np.uint32)
     assert blob_ref._words_to_values(words)[0].tolist() == [0, 4, 1, 5, 2, 6, 3, 7]
+
+
+# ---- int8 experts: value sections twice as wide, bytes in natural order ----
+
+def test_int8_sizes_closed_form():
+    # 3*I*H value bytes + the same scale sections as int4
+    assert blob_ref.blob_bytes(2048, 512, 64, bits=8) == 3 * 512 * 2048 + 12 * 512 * 2048 // 64 == 3_342_336
+    off = blob_ref.section_offsets(2048, 512, 64, bits=8)
+    assert off == dict(gu_q=0, d_q=2_097_152, gu_s=3_145_728, d_s=3_276_800, end=3_342_336)
+    with pytest.raises(ValueError):
+        blob_ref.section_offsets(256, 64, 32, bits=6)
+
+
+def test_int8_hand_placed_bytes():
+    h, i, g = 128, 64, 32
+    buf = np.zeros(blob_ref.blob_bytes(h, i, g, bits=8), np.uint8)
+    # gate q[5, 115] = 0xAB: pair-tile p = 0, row n = 5, chunk c = 1 (cols 64..127),
+    # 115 = 64 + 32 + 8*2 + 3 -> ks = 1, kb = 2, j = 3; lane l = 16*2 + 5 = 37;
+    # word pair m = 2*tile + ks = 1.  Block p*2 + c = 1 of 2048 bytes.
+    # byte = 1*2048 + 37*32 + 8*1 + 3 = 3243.
+    buf[3243] = 0xAB
+    # up q[20, 7] = 0x5C: p = 1, n = 4, c = 0, 7 = 0 + 8*0 + 7 -> ks 0, kb 0, j 7; lane 4;
+    # m = 2*1 + 0 = 2; block 1*2 + 0 = 2 -> byte 2*2048 + 4*32 + 16 + 7 = 4247.
+    buf[4247] = 0x5C
+    # down q[40, 33] = 0xFF: pair-tile p = 1 (rows 32..63), tile A = rows 32..47 -> n = 8;
+    # in_dim = 64: c = 0, 33 = 32 + 0*8 + 1 -> ks 1, kb 0, j 1; lane 8; m = 1;
+    # D_Q starts at 2*I*H = 16384; block p*1 + c = 1 -> 16384 + 2048 + 8*32 + 8 + 1 = 18697.
+    buf[18697] = 0xFF
+    r = blob_ref.parse_blob(buf, h, i, g, bits=8)
+    gate, up, down = r["gate"][0], r["up"][0], r["down"][0]
+    assert gate[5, 115] == 0xAB and int(gate.sum()) == 0xAB
+    assert up[20, 7] == 0x5C and int(up.sum()) == 0x5C
+    assert down[40, 33] == 0xFF and int(down.sum()) == 0xFF
+
+
+@pytest.mark.parametrize("shape", [(128, 64, 32), (256, 128, 64), (320, 192, 64), (256, 128, 128)])
+def test_int8_round_trip(shape):
+    h, i, g = shape
+    rng = np.random.default_rng(h + i + g)
+    q = lambda r, c: rng.integers(0, 256, (r, c)).astype(np.uint8)  # noqa: E731
+    sb = lambda r, c: rng.integers(0, 65536, (r, c // g)).astype(np.uint16)  # noqa: E731
+    raw = dict(gate=(q(i, h), sb(i, h), sb(i, h)), up=(q(i, h), sb(i, h), sb(i, h)), down=(q(h, i), sb(h, i), sb(h, i)))
+    buf = blob_ref.pack_blob(raw["gate"], raw["up"], raw["down"], h, i, g, bits=8)
+    assert buf.size == blob_ref.blob_bytes(h, i, g, bits=8)
+    back = blob_ref.parse_blob(buf, h, i, g, bits=8)
+    for k in raw:
+        for a, b in zip(raw[k], back[k]):
+            assert np.array_equal(a, b)

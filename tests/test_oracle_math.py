@@ -92,6 +92,20 @@ def _brute_topk(z, k):
     return sorted(range(len(z)), key=lambda e: (-z[e], e))[:k]
 
 
+def test_dequant_int8_closed_forms():
+    # int8 affine: W = s*q + b with q in 0..255; b = -128 s centres the range.
+    # s = 2^-8: q = 255 -> 127/256, q = 0 -> -1/2, q = 128 -> 0 (all exact in fp16 and fp64)
+    s = np.full((1, 1), 0x1C00, np.uint16)      # fp16 2^-8
+    b = np.full((1, 1), 0xB800, np.uint16)      # fp16 -0.5
+    q = np.array([[255, 0, 128, 1] * 8], np.uint8)
+    w = mo.dequant(q, s, b, 32, bits=8)
+    assert w[0, 0] == 127 / 256 and w[0, 1] == -0.5 and w[0, 2] == 0.0 and w[0, 3] == -127 / 256
+    with pytest.raises(ValueError):
+        mo.dequant(q, s, b, 32)               # bits = 4 rejects values above 15
+    with pytest.raises(ValueError):
+        mo.dequant(q, s, b, 32, bits=6)
+
+
 def test_topk_brute_force_with_ties():
     rng = np.random.default_rng(2)
     for _ in range(400):

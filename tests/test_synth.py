@@ -53,6 +53,23 @@ def test_value_ranges_and_bias():
     assert counts.min() > 0.9 * q.size / 16
 
 
+def test_int8_values_bytes_and_bias():
+    wl = synth.DEC80I8
+    raw = synth.expert_raw(wl, 3, 77)
+    q, s, b = raw["gate"]
+    assert q.shape == (512, 2048) and q.min() == 0 and q.max() == 255
+    sv = s.view(np.float16).astype(np.float64)
+    assert sv.min() >= 1e-4 - 1e-7 and sv.max() <= 1e-3 + 1e-6
+    assert np.array_equal(b.view(np.float16).astype(np.float64), -128 * sv)
+    # value j is byte j % 4 of word (j % 16) // 4 of Philox block j // 16
+    from synth.philox import philox4x32_10
+    from synth.recipes import T_GATE_Q
+    words = philox4x32_10(np.uint32(2), 77, T_GATE_Q, 0, wl.weight_seed, 3)
+    flat = q.reshape(-1)
+    for j in range(32, 48):
+        assert flat[j] == (int(words[(j % 16) // 4]) >> (8 * (j % 4))) & 0xFF
+
+
 def test_router_bias_is_zipf():
     wl = synth.DEC80
     beta = synth.router_bias(wl, 0).astype(np.float64)
