@@ -33,9 +33,10 @@ and value j of a word sits in bits [4p, 4p+4) with p = (j >> 1) + 4*(j & 1).
 
 int8 experts (bits = 8) double the value sections: GU_Q is 2*I*H bytes and
 D_Q is I*H; the scale sections follow at 3*I*H and 3*I*H + 8*I*H/G.  A chunk
-is then a 2048-byte block, lane l owns bytes 32*l..32*l+31 = eight words:
-words 2m, 2m+1 hold what word m holds above (m = 0..3), value j as byte j of
-the 8 bytes in natural order.
+is then a 2048-byte block of two 1024-byte planes, tile A first.  In plane
+`tile`, lane l owns the 16 bytes at 16*l: the 8 values of half ks = 0, then
+the 8 of half ks = 1 (columns 64c + 32ks + 8kb + j as above), value j as byte
+j of its 8 in natural order.  So byte 1024*tile + 16*l + 8*ks + j of the block.
 
 The scale/bias sections hold, for pair-tile p, group g (G columns of the
 input dimension) and n < 16, eight bytes at ((p * n_groups + g) * 16 + n) * 8:
@@ -88,11 +89,12 @@ def _parse_pair_tiles(raw: np.ndarray, n_pairs: int, in_dim: int, bits: int = 4)
     """Value section -> (tile-A values, tile-B values), each [n_pairs*16, in_dim]."""
     n_chunks = in_dim // 64
     if bits == 8:
-        vals = raw.reshape(n_pairs, n_chunks, 4, 16, 4, 8)            # p, c, kb, n, word pair, j
+        vals = raw.reshape(n_pairs, n_chunks, 2, 4, 16, 2, 8)         # p, c, tile, kb, n, ks, j
+        vals = vals.transpose(0, 1, 3, 4, 2, 5, 6)                    # p, c, kb, n, tile, ks, j
     else:
         words = raw.view("<u4").reshape(n_pairs, n_chunks, 4, 16, 4)  # p, c, kb, n, word
         vals = _words_to_values(words)                                # p, c, kb, n, word, j
-    vals = vals.reshape(n_pairs, n_chunks, 4, 16, 2, 2, 8)           # p, c, kb, n, tile, ks, j
+        vals = vals.reshape(n_pairs, n_chunks, 4, 16, 2, 2, 8)       # p, c, kb, n, tile, ks, j
     # row = (p, tile, n); column = 64c + 32ks + 8kb + j
     arr = vals.transpose(0, 4, 3, 1, 5, 2, 6)                        # p, tile, n, c, ks, kb, j
     return arr.reshape(n_pairs, 2, 16, in_dim)
@@ -102,9 +104,10 @@ def _pack_pair_tiles(tile_a: np.ndarray, tile_b: np.ndarray, n_pairs: int, in_di
     n_chunks = in_dim // 64
     both = np.stack([tile_a.reshape(n_pairs, 16, in_dim), tile_b.reshape(n_pairs, 16, in_dim)], axis=1)
     arr = both.reshape(n_pairs, 2, 16, n_chunks, 2, 4, 8)            # p, tile, n, c, ks, kb, j
-    vals = arr.transpose(0, 3, 5, 2, 1, 4, 6)                        # p, c, kb, n, tile, ks, j
     if bits == 8:
-        return np.ascontiguousarray(vals).astype(np.uint8).reshape(-1)
+        planes = arr.transpose(0, 3, 1, 5, 2, 4, 6)                  # p, c, tile, kb, n, ks, j
+        return np.ascontiguousarray(planes).astype(np.uint8).reshape(-1)
+    vals = arr.transpose(0, 3, 5, 2, 1, 4, 6)                        # p, c, kb, n, tile, ks, j
     words = _values_to_words(vals.reshape(n_pairs, n_chunks, 4, 16, 4, 8))
     return words.astype("<u4").view(np.uint8).reshape(-1)
 

@@ -112,18 +112,18 @@ def test_int8_sizes_closed_form():
 def test_int8_hand_placed_bytes():
     h, i, g = 128, 64, 32
     buf = np.zeros(blob_ref.blob_bytes(h, i, g, bits=8), np.uint8)
-    # gate q[5, 115] = 0xAB: pair-tile p = 0, row n = 5, chunk c = 1 (cols 64..127),
-    # 115 = 64 + 32 + 8*2 + 3 -> ks = 1, kb = 2, j = 3; lane l = 16*2 + 5 = 37;
-    # word pair m = 2*tile + ks = 1.  Block p*2 + c = 1 of 2048 bytes.
-    # byte = 1*2048 + 37*32 + 8*1 + 3 = 3243.
-    buf[3243] = 0xAB
-    # up q[20, 7] = 0x5C: p = 1, n = 4, c = 0, 7 = 0 + 8*0 + 7 -> ks 0, kb 0, j 7; lane 4;
-    # m = 2*1 + 0 = 2; block 1*2 + 0 = 2 -> byte 2*2048 + 4*32 + 16 + 7 = 4247.
-    buf[4247] = 0x5C
+    # byte of (tile, lane l, ks, j) in a 2048-byte chunk block: 1024*tile + 16*l + 8*ks + j
+    # gate q[5, 115] = 0xAB: pair-tile p = 0, tile A, row n = 5, chunk c = 1 (cols 64..127),
+    # 115 = 64 + 32 + 8*2 + 3 -> ks = 1, kb = 2, j = 3; lane l = 16*2 + 5 = 37.
+    # Block p*2 + c = 1 -> byte 1*2048 + 0 + 37*16 + 8 + 3 = 2651.
+    buf[2651] = 0xAB
+    # up q[20, 7] = 0x5C: p = 1, tile B, n = 4, c = 0, 7 = 0 + 8*0 + 7 -> ks 0, kb 0, j 7;
+    # lane 4; block 1*2 + 0 = 2 -> byte 2*2048 + 1024 + 4*16 + 0 + 7 = 5191.
+    buf[5191] = 0x5C
     # down q[40, 33] = 0xFF: pair-tile p = 1 (rows 32..63), tile A = rows 32..47 -> n = 8;
-    # in_dim = 64: c = 0, 33 = 32 + 0*8 + 1 -> ks 1, kb 0, j 1; lane 8; m = 1;
-    # D_Q starts at 2*I*H = 16384; block p*1 + c = 1 -> 16384 + 2048 + 8*32 + 8 + 1 = 18697.
-    buf[18697] = 0xFF
+    # in_dim = 64: c = 0, 33 = 32 + 0*8 + 1 -> ks 1, kb 0, j 1; lane 8.
+    # D_Q starts at 2*I*H = 16384; block p*1 + c = 1 -> 16384 + 2048 + 0 + 8*16 + 8 + 1 = 18569.
+    buf[18569] = 0xFF
     r = blob_ref.parse_blob(buf, h, i, g, bits=8)
     gate, up, down = r["gate"][0], r["up"][0], r["down"][0]
     assert gate[5, 115] == 0xAB and int(gate.sum()) == 0xAB
