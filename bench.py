@@ -33,7 +33,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="bat80", choices=["bat80", "dec80", "dec35", "pool80"])
+    ap.add_argument("--workload", default="bat80", choices=["bat80", "dec80", "dec35", "pool80", "dec80i8"])
     ap.add_argument("--layers", type=int, default=0, help="override the number of layers (0 = workload's)")
     ap.add_argument("--path", type=int, default=0, help="0 auto, 1 GEMV family, 2 grouped family")
     ap.add_argument("--eager", action="store_true", help="launch kernels one by one instead of a HIP graph")
@@ -97,9 +97,9 @@ class Stack:
         from int4_routed_expert_router_amd import api
         self.wl, self.L = wl, n_layers
         self.desc = api.Desc(wl.hidden, wl.n_experts, wl.top_k, wl.inter, wl.shared_inter, wl.group, wl.act_dtype,
-                             path)
-        self.stride = api.blob_bytes(wl.hidden, wl.inter, wl.group)
-        self.sstride = api.blob_bytes(wl.hidden, wl.shared_inter, wl.group)
+                             path, wl.bits)
+        self.stride = api.blob_bytes(wl.hidden, wl.inter, wl.group, wl.bits)
+        self.sstride = api.blob_bytes(wl.hidden, wl.shared_inter, wl.group, wl.bits)
         E = wl.n_experts
         self.slab = torch.empty(n_layers * E * self.stride, dtype=torch.uint8, device="cuda")
         self.shared = torch.empty(n_layers * self.sstride, dtype=torch.uint8, device="cuda")
@@ -108,9 +108,9 @@ class Stack:
             ex = self.slab[l * E * self.stride:(l + 1) * E * self.stride]
             sh = self.shared[l * self.sstride:(l + 1) * self.sstride]
             api.synth_fill_experts(wl.weight_seed, l, 0, E, wl.hidden, wl.inter, wl.group, wl.scale_lo, wl.scale_hi,
-                                   ex, self.stride)
+                                   ex, self.stride, bits=wl.bits)
             api.synth_fill_experts(wl.weight_seed, l, E, 1, wl.hidden, wl.shared_inter, wl.group, wl.scale_lo,
-                                   wl.scale_hi, sh, self.sstride)
+                                   wl.scale_hi, sh, self.sstride, bits=wl.bits)
             wr = torch.from_numpy(synth.router_weights(wl, l).view(np.int16).copy()).cuda()
             b = synth.router_bias(wl, l)
             bt = None if b is None else torch.from_numpy(b).cuda()
@@ -180,7 +180,7 @@ def cpu_baseline(wl, budget_s):
 
         def expert(e, shared=False, l=l):
             r = synth.expert_raw(wl, l, e, shared=shared)
-            return mo.ExpertWeights.from_quant(r["gate"], r["up"], r["down"], wl.group)
+            return mo.ExpertWeights.from_quant(r["gate"], r["up"], r["down"], wl.group, wl.bits)
 
         wr = mo.f16_bits_to_f64(synth.router_weights(wl, l))
         b = synth.router_bias(wl, l)
@@ -327,9 +327,11 @@ def main():
     tokens_s = wl.tokens * args.steps / elapsed
     act = st.active_experts()
     B = st.stride  # routed and shared blobs have the same size in these workloads
-    int4_bytes = sum((a + 1) * B for a in act)
-    int4_gbs = int4_bytes / (ms_per_step * 1e-3) / 1e9
-    print(f"[bench] {ms_per_step:.3f} ms/step, {tokens_s:.0f} tok/s, int4 {int4_gbs:.0f} GB/s, "
+    wname = f"int{wl.bits}"
+    expert_bytes = sum((a + 1) * B for a in act)
+    expert_gbs = expert_bytes / (ms_per_step * 1e-3) / 1e9
+    grouped = wl.bits == 4 and (args.path == 2 or (args.path == 0 and wl.tokens * wl.top_k > 32))
+    print(f"[bench] {ms_per_step:.3f} ms/step, {tokens_s:.0f} tok/s, {wname} {expert_gbs:.0f} GB/s, "
           f"active experts/layer mean {np.mean(act):.1f}", file=sys.stderr, flush=True)
 
     roof = None
@@ -352,16 +354,17 @@ def main():
                     durs.append([begin[l].elapsed_time(end[l]) for l in range(L)])
             kernel_us[name] = float(np.mean(durs)) * 1e3
         avg_us = kernel_us["gateup"]
-        gu_bytes = (st.desc.inter * st.desc.hidden + 8 * st.desc.inter * st.desc.hidden // st.desc.group_size)
+        # gate and up values (2 I H of bits/8 bytes) plus their fp16 scale and bias
+        gu_bytes = (st.desc.inter * st.desc.hidden * wl.bits // 4
+                    + 8 * st.desc.inter * st.desc.hidden // st.desc.group_size)
         per_launch = float(np.mean([(a + 1) * gu_bytes for a in act]))
         achieved = per_launch / (avg_us * 1e-6) / 1e9
-        grouped = args.path == 2 or (args.path == 0 and wl.tokens * wl.top_k > 32)
         tb = measured_traffic() if (grouped and args.workload == "bat80") else None
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": None if tb is None else round(tb / (avg_us * 1e-6) / 1e9, 1),
                 "kernel": "k_gateup_tiles (int4 gate/up + SwiGLU)" if grouped else
-                          "k_gateup_gemv (int4 gate/up + SwiGLU)",
+                          f"k_gateup_gemv ({wname} gate/up partial sums)",
                 "avg_us": round(avg_us, 2), "bytes_per_launch": int(per_launch),
                 "traffic_bytes_per_launch": None if tb is None else int(tb),
                 "events": "HIP events on the launch stream around each layer's gate/up kernel, eager replay"}
@@ -374,7 +377,7 @@ def main():
         cpu = cpu_baseline(wl, args.cpu_seconds)
 
     out = {
-        "metric": "MoE-layer tokens/sec + achieved HBM GB/s on int4 expert bytes (80B-shaped)",
+        "metric": f"MoE-layer tokens/sec + achieved HBM GB/s on {wname} expert bytes (80B-shaped)",
         "value": round(tokens_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -384,16 +387,17 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16" if (args.path == 2 or (args.path == 0 and wl.tokens * wl.top_k > 32)) else wl.act_dtype,
+        "dtype": "f16" if grouped else ("f32" if wl.bits == 8 else wl.act_dtype),
         "precision": "int4 weights as exact f16 matrix-core operands, activations f16, fp32 accumulate"
-                     if (args.path == 2 or (args.path == 0 and wl.tokens * wl.top_k > 32)) else
-                     "int4 weights, bf16/f16 dot2 products, fp32 accumulate",
+                     if grouped else
+                     ("int8 weights times activations widened to fp32, fp32 accumulate" if wl.bits == 8 else
+                      "int4 weights, bf16/f16 dot2 products, fp32 accumulate"),
         "data": "synthetic (seeded; random-init weights of the stated shapes)",
-        "int4_expert_GBps": round(int4_gbs, 1),
-        "int4_frac_of_hbm_peak": round(int4_gbs / HBM_PEAK_GBS, 4),
+        f"{wname}_expert_GBps": round(expert_gbs, 1),
+        f"{wname}_frac_of_hbm_peak": round(expert_gbs / HBM_PEAK_GBS, 4),
         "active_experts_per_layer": round(float(np.mean(act)), 2),
         "config": {"workload": f"{wl.name}: {L} layers, hidden {wl.hidden}, {wl.n_experts} experts top-{wl.top_k}, "
-                               f"inter {wl.inter}, shared {wl.shared_inter}, int4 group {wl.group}, "
+                               f"inter {wl.inter}, shared {wl.shared_inter}, {wname} group {wl.group}, "
                                f"{wl.tokens} tokens/step, Zipf {wl.zipf_s}",
                    "global_batch": wl.tokens, "layers": L, "path": ["auto", "gemv", "grouped"][args.path],
                    "graph": not args.eager, "parallelism": "single GPU"},

@@ -17,8 +17,9 @@
  *   FFN_e(x) = Wd_e (silu(Wg_e x) * (Wu_e x)),  silu(a) = a / (1 + exp(-a))
  *   y[t]     = sum_k w[t,k] FFN_{S_tk}(x[t]) + gamma[t] FFN_shared(x[t])
  *
- * with W[r,c] = s[r, c/G] * q[r,c] + b[r, c/G], q in 0..15, fp16 s and b,
- * groups of G columns along each matrix's input dimension.
+ * with W[r,c] = s[r, c/G] * q[r,c] + b[r, c/G], q in 0..15 (or 0..255 for
+ * int8 experts, the pages' other affine width: same what-was-built list),
+ * fp16 s and b, groups of G columns along each matrix's input dimension.
  *
  * Conventions (all functions):
  *  - Every buffer is caller-owned.  Pointers named "device" are device
@@ -73,11 +74,16 @@ enum { MOE_PATH_AUTO = 0, MOE_PATH_GEMV = 1, MOE_PATH_GROUPED = 2 };
  *   shared_inter:    0 (no shared expert) or a multiple of 64, 64..4096
  *   group_size G:    32, 64 or 128, dividing H, I and shared_inter
  *   act_dtype:       MOE_F16 or MOE_BF16 (dtype of x); y is always fp32
- *   path:            MOE_PATH_* */
+ *   path:            MOE_PATH_*
+ *   weight_bits:     4 (or 0, the same) for int4 experts, 8 for int8 experts
+ *                    (routed and shared alike).  int8 experts run on the GEMV
+ *                    family at every batch size: AUTO picks it, GROUPED is
+ *                    MOE_ESHAPE. */
 typedef struct {
   int32_t hidden, n_experts, top_k, inter, shared_inter, group_size;
   int32_t act_dtype;
   int32_t path;
+  int32_t weight_bits;
 } moe_layer_desc;
 
 /* Weights of one layer (device addresses, caller-owned, read-only).
@@ -88,7 +94,7 @@ typedef struct {
  *                  experts + (expert_offset ? expert_offset[e] : e*expert_stride).
  *                  Blob starts must be 256-byte aligned.
  *   expert_stride: bytes between consecutive blobs when expert_offset is NULL
- *                  (>= moe_blob_bytes(H, I, G), multiple of 256).
+ *                  (>= moe_blob_bytes_q(H, I, G, weight_bits), multiple of 256).
  *   expert_offset: [E] uint64 byte offsets (device) or NULL.  Only entries of
  *                  selected experts are read (the slot pool keeps them valid).
  *   shared:        blob of the shared expert (inter = shared_inter), or NULL
@@ -127,14 +133,31 @@ typedef struct {
  * and value j of a word occupies bits [4p, 4p+4), p = (j>>1) + 4*(j&1).
  * Scale sections: for pair-tile p, group g (< in_dim/G), n < 16, the eight
  * bytes at ((p*(in_dim/G) + g)*16 + n)*8 hold fp16 [s_A, b_A, s_B, b_B] of
- * row n of tiles A and B. */
+ * row n of tiles A and B.
+ *
+ * int8 experts double the value sections (GU_Q 2*I*H bytes at 0, D_Q I*H
+ * bytes at 2*I*H) and move the scale sections to 3*I*H and 3*I*H + 8*I*H/G
+ * (same contents).  A chunk is then a 2048-byte block of two 1024-byte
+ * planes, tile A first; in each plane lane l owns the 16 bytes at 16l: the 8
+ * values of columns 64c + 8kb + j, then the 8 of columns 64c + 32 + 8kb + j,
+ * one byte per value in order j = 0..7.
+ *
+ * moe_blob_bytes: size of an int4 blob; moe_blob_bytes_q: of a blob of
+ * weight_bits 4 or 8.  Both return 0 for unsupported sizes. */
 uint64_t moe_blob_bytes(int32_t hidden, int32_t inter, int32_t group_size);
+uint64_t moe_blob_bytes_q(int32_t hidden, int32_t inter, int32_t group_size, int32_t weight_bits);
 
 /* Host-side packer: raw tensors -> one blob (host buffer of
- * moe_blob_bytes() bytes).  q arrays hold one value 0..15 per byte,
- * row-major: gate_q, up_q [I][H], down_q [H][I]; scale and bias arrays are
- * fp16 bits, row-major [rows][in_dim/G].  Returns MOE_ESHAPE for bad sizes,
- * MOE_EINVAL for NULL pointers or q values above 15. */
+ * moe_blob_bytes_q() bytes).  q arrays hold one value per byte (0..15 for
+ * weight_bits 4, 0..255 for 8), row-major: gate_q, up_q [I][H], down_q
+ * [H][I]; scale and bias arrays are fp16 bits, row-major [rows][in_dim/G].
+ * Returns MOE_ESHAPE for bad sizes or widths, MOE_EINVAL for NULL pointers
+ * or int4 q values above 15.  moe_pack_expert is the int4 packer. */
+moe_status moe_pack_expert_q(int32_t hidden, int32_t inter, int32_t group_size, int32_t weight_bits,
+                             const uint8_t* gate_q, const uint16_t* gate_s, const uint16_t* gate_b,
+                             const uint8_t* up_q, const uint16_t* up_s, const uint16_t* up_b,
+                             const uint8_t* down_q, const uint16_t* down_s, const uint16_t* down_b,
+                             uint8_t* blob_out);
 moe_status moe_pack_expert(int32_t hidden, int32_t inter, int32_t group_size,
                            const uint8_t* gate_q, const uint16_t* gate_s, const uint16_t* gate_b,
                            const uint8_t* up_q, const uint16_t* up_s, const uint16_t* up_b,

@@ -24,7 +24,7 @@ STATUS_NAMES = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_ESHAPE", -3: "MOE_EWORKS
 class LayerDesc(C.Structure):
     _fields_ = [("hidden", C.c_int32), ("n_experts", C.c_int32), ("top_k", C.c_int32), ("inter", C.c_int32),
                 ("shared_inter", C.c_int32), ("group_size", C.c_int32), ("act_dtype", C.c_int32),
-                ("path", C.c_int32)]
+                ("path", C.c_int32), ("weight_bits", C.c_int32)]
 
 
 class LayerWeights(C.Structure):
@@ -57,6 +57,8 @@ PROTOS = {
     "moe_version": (C.c_char_p, []),
     "moe_blob_bytes": (u64, [i32, i32, i32]),
     "moe_pack_expert": (i32, [i32, i32, i32] + [vp] * 10),
+    "moe_blob_bytes_q": (u64, [i32, i32, i32, i32]),
+    "moe_pack_expert_q": (i32, [i32, i32, i32, i32] + [vp] * 10),
     "moe_workspace_bytes": (i32, [vp, i32, C.POINTER(C.c_size_t)]),
     "moe_route": (i32, [vp, vp, vp, i32, vp, vp, vp, vp, vp, C.c_size_t, vp]),
     "moe_permute": (i32, [vp, vp, i32, vp, vp, vp, vp, C.c_size_t, vp]),
@@ -69,7 +71,7 @@ PROTOS = {
     "moe_graph_launch": (i32, [vp, vp]),
     "moe_stack_set_kernel_events": (i32, [vp, vp, i32, i32]),
     "moe_graph_destroy": (None, [vp]),
-    "moe_synth_fill_experts": (i32, [u64, i32, i32, i32, i32, i32, i32, f32, f32, vp, u64, vp]),
+    "moe_synth_fill_experts": (i32, [u64, i32, i32, i32, i32, i32, i32, i32, f32, f32, vp, u64, vp]),
     "moe_synth_philox": (i32, [vp, vp, vp, i32, vp]),
     "slotpool_create": (i32, [C.POINTER(SlotPoolConfig), C.POINTER(vp)]),
     "slotpool_acquire": (i32, [vp, i32, vp, i32, u64, vp, vp, vp, vp]),

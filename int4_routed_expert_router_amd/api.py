@@ -45,18 +45,19 @@ class Desc:
     group_size: int
     act_dtype: str = "bf16"          # "f16" | "bf16"
     path: int = MOE_PATH_AUTO
+    weight_bits: int = 4             # 4 | 8
 
     def c(self) -> LayerDesc:
         return LayerDesc(self.hidden, self.n_experts, self.top_k, self.inter, self.shared_inter, self.group_size,
-                         {"bf16": MOE_BF16, "f16": MOE_F16}.get(self.act_dtype, 0), self.path)
+                         {"bf16": MOE_BF16, "f16": MOE_F16}.get(self.act_dtype, 0), self.path, self.weight_bits)
 
     @property
     def blob_bytes(self) -> int:
-        return blob_bytes(self.hidden, self.inter, self.group_size)
+        return blob_bytes(self.hidden, self.inter, self.group_size, self.weight_bits)
 
     @property
     def shared_blob_bytes(self) -> int:
-        return blob_bytes(self.hidden, self.shared_inter, self.group_size) if self.shared_inter else 0
+        return blob_bytes(self.hidden, self.shared_inter, self.group_size, self.weight_bits) if self.shared_inter else 0
 
 
 class Layer:
@@ -77,19 +78,19 @@ class Layer:
                             _ptr(self.expert_offset), _ptr(self.shared))
 
 
-def blob_bytes(hidden: int, inter: int, group: int) -> int:
-    return int(lib().moe_blob_bytes(hidden, inter, group))
+def blob_bytes(hidden: int, inter: int, group: int, bits: int = 4) -> int:
+    return int(lib().moe_blob_bytes_q(hidden, inter, group, bits))
 
 
-def pack_expert(raw, hidden: int, inter: int, group: int) -> np.ndarray:
+def pack_expert(raw, hidden: int, inter: int, group: int, bits: int = 4) -> np.ndarray:
     """Host packer: raw dict(gate=(q,s,b), up=..., down=...) -> blob bytes (np.uint8)."""
-    out = np.zeros(blob_bytes(hidden, inter, group), np.uint8)
+    out = np.zeros(blob_bytes(hidden, inter, group, bits), np.uint8)
     arrs = []
     for name in ("gate", "up", "down"):
         q, s, b = raw[name]
         arrs += [np.ascontiguousarray(q, np.uint8), np.ascontiguousarray(s, np.uint16),
                  np.ascontiguousarray(b, np.uint16)]
-    check(lib().moe_pack_expert(hidden, inter, group, *[a.ctypes.data for a in arrs], out.ctypes.data))
+    check(lib().moe_pack_expert_q(hidden, inter, group, bits, *[a.ctypes.data for a in arrs], out.ctypes.data))
     return out
 
 
@@ -185,10 +186,10 @@ class StackGraph:
 
 
 def synth_fill_experts(seed, layer, expert_first, n_experts, hidden, inter, group, scale_lo, scale_hi, dst, stride,
-                       stream=None):
+                       stream=None, bits: int = 4):
     """Fill blobs on the GPU with the seeded synthetic weights (see include/moe_synth.h)."""
     span = float(np.float32(scale_hi - scale_lo))
-    check(lib().moe_synth_fill_experts(seed, layer, expert_first, n_experts, hidden, inter, group,
+    check(lib().moe_synth_fill_experts(seed, layer, expert_first, n_experts, hidden, inter, group, bits,
                                        float(np.float32(scale_lo)), span, _ptr(dst), stride, _stream(stream)))
 
 

@@ -41,7 +41,9 @@ hipError_t timer_mark(bool at_begin, int kind, int layer, hipStream_t s) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-uint64_t blob_size(int H, int I, int G) { return 3ull * I * H / 2 + 12ull * I * H / G; }
+// weight_bits 0 means 4 (a zero-initialised descriptor describes int4 experts)
+int wbits(const moe_layer_desc* d) { return d->weight_bits == 8 ? 8 : 4; }
+uint64_t blob_size(int H, int I, int G, int bits) { return 3ull * I * H * bits / 8 + 12ull * I * H / G; }
 
 bool grouped_fits(const moe_layer_desc* d);
 
@@ -58,6 +60,9 @@ moe_status check_desc(const moe_layer_desc* d) {
   if (H % G || I % G || (Is && Is % G)) return fail(MOE_ESHAPE, "group_size=%d must divide hidden, inter and shared_inter", G);
   if (d->act_dtype != MOE_F16 && d->act_dtype != MOE_BF16) return fail(MOE_EINVAL, "act_dtype=%d is not MOE_F16/MOE_BF16", d->act_dtype);
   if (d->path < MOE_PATH_AUTO || d->path > MOE_PATH_GROUPED) return fail(MOE_EINVAL, "path=%d is not a MOE_PATH_*", d->path);
+  if (d->weight_bits != 0 && d->weight_bits != 4 && d->weight_bits != 8)
+    return fail(MOE_ESHAPE, "weight_bits=%d must be 4 (or 0) or 8", d->weight_bits);
+  if (d->path == MOE_PATH_GROUPED && wbits(d) == 8) return fail(MOE_ESHAPE, "int8 experts run on the GEMV family only");
   if (d->path == MOE_PATH_GROUPED && !grouped_fits(d))
     return fail(MOE_ESHAPE, "the grouped family needs hidden <= %d and inter, shared_inter <= %d", moe::kGroupedMaxH,
                 moe::kGroupedMaxInter);
@@ -69,10 +74,10 @@ moe_status check_weights(const moe_layer_desc* d, const moe_layer_weights* w) {
   if (!w->router_w || !aligned(w->router_w, 16)) return fail(MOE_EINVAL, "router_w must be a 16-byte aligned device pointer");
   if (!w->experts || !aligned(w->experts, 256)) return fail(MOE_EINVAL, "experts must be a 256-byte aligned device pointer");
   if (!w->expert_offset) {
-    if (w->expert_stride % 256 || w->expert_stride < blob_size(d->hidden, d->inter, d->group_size))
+    if (w->expert_stride % 256 || w->expert_stride < blob_size(d->hidden, d->inter, d->group_size, wbits(d)))
       return fail(MOE_EINVAL, "expert_stride=%llu must be a multiple of 256 and >= %llu",
                   (unsigned long long)w->expert_stride,
-                  (unsigned long long)blob_size(d->hidden, d->inter, d->group_size));
+                  (unsigned long long)blob_size(d->hidden, d->inter, d->group_size, wbits(d)));
   }
   if (d->shared_inter > 0 && (!w->shared || !aligned(w->shared, 256)))
     return fail(MOE_EINVAL, "shared blob must be a 256-byte aligned device pointer when shared_inter > 0");
@@ -124,7 +129,7 @@ bool grouped_fits(const moe_layer_desc* d) {
 }
 
 bool use_grouped(const moe_layer_desc* d, int T) {
-  if (d->path == MOE_PATH_GEMV) return false;
+  if (d->path == MOE_PATH_GEMV || wbits(d) == 8) return false;
   if (d->path == MOE_PATH_GROUPED) return true;
   return static_cast<long long>(T) * d->top_k > MOE_GEMV_MAX_ROWS && grouped_fits(d);
 }
@@ -166,6 +171,7 @@ moe_status do_ffn(const moe_layer_desc* d, const moe_layer_weights* w, const voi
   a.G = d->group_size;
   a.E = d->n_experts;
   a.hstride = d->inter > d->shared_inter ? d->inter : d->shared_inter;
+  a.bits = wbits(d);
   const int32_t* inv = nullptr;
   hipError_t e;
   if (use_grouped(d, T)) {
@@ -229,26 +235,36 @@ const char* moe_last_error(void) { return g_err; }
 
 const char* moe_version(void) { return "int4_routed_expert_router_amd 0.1 (gfx950)"; }
 
-uint64_t moe_blob_bytes(int32_t hidden, int32_t inter, int32_t group_size) {
+uint64_t moe_blob_bytes_q(int32_t hidden, int32_t inter, int32_t group_size, int32_t bits) {
   if (hidden <= 0 || inter <= 0 || hidden % 64 || inter % 64) return 0;
   if ((group_size != 32 && group_size != 64 && group_size != 128) || hidden % group_size || inter % group_size)
     return 0;
-  return blob_size(hidden, inter, group_size);
+  if (bits != 4 && bits != 8) return 0;
+  return blob_size(hidden, inter, group_size, bits);
 }
 
-moe_status moe_pack_expert(int32_t H, int32_t I, int32_t G, const uint8_t* gate_q, const uint16_t* gate_s,
-                           const uint16_t* gate_b, const uint8_t* up_q, const uint16_t* up_s, const uint16_t* up_b,
-                           const uint8_t* down_q, const uint16_t* down_s, const uint16_t* down_b,
-                           uint8_t* blob_out) {
-  if (moe_blob_bytes(H, I, G) == 0) return fail(MOE_ESHAPE, "bad blob shape H=%d I=%d G=%d", H, I, G);
+uint64_t moe_blob_bytes(int32_t hidden, int32_t inter, int32_t group_size) {
+  return moe_blob_bytes_q(hidden, inter, group_size, 4);
+}
+
+moe_status moe_pack_expert_q(int32_t H, int32_t I, int32_t G, int32_t bits, const uint8_t* gate_q,
+                             const uint16_t* gate_s, const uint16_t* gate_b, const uint8_t* up_q,
+                             const uint16_t* up_s, const uint16_t* up_b, const uint8_t* down_q,
+                             const uint16_t* down_s, const uint16_t* down_b, uint8_t* blob_out) {
+  if (moe_blob_bytes_q(H, I, G, bits) == 0)
+    return fail(MOE_ESHAPE, "bad blob shape H=%d I=%d G=%d bits=%d", H, I, G, bits);
   if (!gate_q || !gate_s || !gate_b || !up_q || !up_s || !up_b || !down_q || !down_s || !down_b || !blob_out)
     return fail(MOE_EINVAL, "NULL pointer");
   const size_t nq = static_cast<size_t>(I) * H;
-  for (size_t i = 0; i < nq; ++i)
-    if ((gate_q[i] | up_q[i] | down_q[i]) > 15) return fail(MOE_EINVAL, "q value above 15 at element %zu", i);
-  memset(blob_out, 0, blob_size(H, I, G));
-  // nibble sections: for pair-tile p, chunk c, lane l = 16 kb + n, word wd:
-  // tile (wd >> 1), half ks = (wd & 1), value j -> column 64c + 32ks + 8kb + j
+  if (bits == 4)
+    for (size_t i = 0; i < nq; ++i)
+      if ((gate_q[i] | up_q[i] | down_q[i]) > 15) return fail(MOE_EINVAL, "q value above 15 at element %zu", i);
+  memset(blob_out, 0, blob_size(H, I, G, bits));
+  // value sections, for pair-tile p, chunk c, lane l = 16 kb + n, tile, half ks
+  // and value j (column 64c + 32ks + 8kb + j): int4 puts it in nibble
+  // (j>>1) + 4(j&1) of word 2 tile + ks of the lane's 16 bytes in a 1 KiB
+  // block; int8 puts it in byte 8 ks + j of the lane's 16 bytes in plane
+  // `tile` of a 2 KiB block
   auto pack_section = [&](uint8_t* sec, int n_pairs, int in_dim, const uint8_t* qa, int row_a0_stride,
                           const uint8_t* qb, bool gu) {
     const int nc = in_dim / 64;
@@ -267,12 +283,13 @@ moe_status moe_pack_expert(int32_t H, int32_t I, int32_t G, const uint8_t* gate_
               row = 32 * p + 16 * tile + n;
               q = qa;
             }
-            uint32_t word = 0;
-            for (int j = 0; j < 8; ++j) {
-              const int col = 64 * c + 32 * ks + 8 * kb + j;
-              const uint32_t v = q[static_cast<size_t>(row) * in_dim + col];
-              word |= v << (4 * ((j >> 1) + 4 * (j & 1)));
+            const uint8_t* src = q + static_cast<size_t>(row) * in_dim + 64 * c + 32 * ks + 8 * kb;
+            if (bits == 8) {
+              memcpy(sec + (static_cast<size_t>(p) * nc + c) * 2048 + 1024 * tile + 16 * l + 8 * ks, src, 8);
+              continue;
             }
+            uint32_t word = 0;
+            for (int j = 0; j < 8; ++j) word |= static_cast<uint32_t>(src[j]) << (4 * ((j >> 1) + 4 * (j & 1)));
             uint8_t* dst = sec + (static_cast<size_t>(p) * nc + c) * 1024 + 16 * l + 4 * wd;
             memcpy(dst, &word, 4);
           }
@@ -280,7 +297,7 @@ moe_status moe_pack_expert(int32_t H, int32_t I, int32_t G, const uint8_t* gate_
     (void)row_a0_stride;
   };
   pack_section(blob_out, I / 16, H, gate_q, 0, up_q, true);
-  pack_section(blob_out + static_cast<size_t>(I) * H, H / 32, I, down_q, 0, nullptr, false);
+  pack_section(blob_out + static_cast<size_t>(I) * H * bits / 4, H / 32, I, down_q, 0, nullptr, false);
   auto pack_scales = [&](uint8_t* sec, int n_pairs, int in_dim, const uint16_t* sa, const uint16_t* ba,
                          const uint16_t* sb_, const uint16_t* bb, bool gu) {
     const int ng = in_dim / G;
@@ -305,10 +322,17 @@ moe_status moe_pack_expert(int32_t H, int32_t I, int32_t G, const uint8_t* gate_
           memcpy(sec + ((static_cast<size_t>(p) * ng + g) * 16 + n) * 8, v, 8);
         }
   };
-  const size_t gu_s = 3ull * I * H / 2, d_s = gu_s + 8ull * I * H / G;
+  const size_t gu_s = 3ull * I * H * bits / 8, d_s = gu_s + 8ull * I * H / G;
   pack_scales(blob_out + gu_s, I / 16, H, gate_s, gate_b, up_s, up_b, true);
   pack_scales(blob_out + d_s, H / 32, I, down_s, down_b, nullptr, nullptr, false);
   return ok();
+}
+
+moe_status moe_pack_expert(int32_t H, int32_t I, int32_t G, const uint8_t* gate_q, const uint16_t* gate_s,
+                           const uint16_t* gate_b, const uint8_t* up_q, const uint16_t* up_s, const uint16_t* up_b,
+                           const uint8_t* down_q, const uint16_t* down_s, const uint16_t* down_b,
+                           uint8_t* blob_out) {
+  return moe_pack_expert_q(H, I, G, 4, gate_q, gate_s, gate_b, up_q, up_s, up_b, down_q, down_s, down_b, blob_out);
 }
 
 moe_status moe_workspace_bytes(const moe_layer_desc* d, int32_t n_tokens, size_t* bytes) {

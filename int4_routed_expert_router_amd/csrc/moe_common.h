@@ -135,13 +135,31 @@ __device__ __forceinline__ float word_dot_q(uint32_t w, const float* h) {
   return p;
 }
 
+// sum_j q_j * x_j over 8 int8 values (bytes 0..3 of lo, then of hi) with fp32
+// x[0..7]; every product is exact in fp32.
+__device__ __forceinline__ float bytes8_dot(uint32_t lo, uint32_t hi, const float* x) {
+  float p = static_cast<float>(lo & 0xFFu) * x[0];
+  p = fmaf(static_cast<float>((lo >> 8) & 0xFFu), x[1], p);
+  p = fmaf(static_cast<float>((lo >> 16) & 0xFFu), x[2], p);
+  p = fmaf(static_cast<float>(lo >> 24), x[3], p);
+  p = fmaf(static_cast<float>(hi & 0xFFu), x[4], p);
+  p = fmaf(static_cast<float>((hi >> 8) & 0xFFu), x[5], p);
+  p = fmaf(static_cast<float>((hi >> 16) & 0xFFu), x[6], p);
+  p = fmaf(static_cast<float>(hi >> 24), x[7], p);
+  return p;
+}
+
 // ---- blob geometry (see the public header for the byte layout) -------------
+// bits = 4 or 8: the value sections scale with the weight width, the scale
+// sections do not.
 __host__ __device__ __forceinline__ uint64_t blob_gu_q(int, int) { return 0; }
-__host__ __device__ __forceinline__ uint64_t blob_d_q(int H, int I) { return (uint64_t)I * H; }
-__host__ __device__ __forceinline__ uint64_t blob_gu_s(int H, int I) { return 3ull * I * H / 2; }
-__host__ __device__ __forceinline__ uint64_t blob_d_s(int H, int I, int G) { return 3ull * I * H / 2 + 8ull * I * H / G; }
-__host__ __device__ __forceinline__ uint64_t blob_size(int H, int I, int G) {
-  return 3ull * I * H / 2 + 12ull * I * H / G;
+__host__ __device__ __forceinline__ uint64_t blob_d_q(int H, int I, int bits = 4) { return (uint64_t)I * H * bits / 4; }
+__host__ __device__ __forceinline__ uint64_t blob_gu_s(int H, int I, int bits = 4) { return 3ull * I * H * bits / 8; }
+__host__ __device__ __forceinline__ uint64_t blob_d_s(int H, int I, int G, int bits = 4) {
+  return 3ull * I * H * bits / 8 + 8ull * I * H / G;
+}
+__host__ __device__ __forceinline__ uint64_t blob_size(int H, int I, int G, int bits = 4) {
+  return 3ull * I * H * bits / 8 + 12ull * I * H / G;
 }
 
 // fp16 scale/bias entry [s_A, b_A, s_B, b_B] of (pair-tile p, group g, row n)

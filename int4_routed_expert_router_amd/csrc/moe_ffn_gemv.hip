@@ -1,11 +1,12 @@
-// Per-row int4 expert GEMVs (decode-sized batches) and the combine.
+// Per-row int4 / int8 expert GEMVs (decode-sized batches) and the combine.
 //
 // The pages run a cooperative GEMV fast path over MLX-style affine int4/int8
 // group-quantised weights (what-was-built list of the page "Show HN: Run an
 // 80B Qwen in 4.3 GB of RAM on a Mac and a 35B on an iPhone").  Here a
-// 64-lane wavefront reads one 1 KiB block of packed nibbles per 16-byte load,
-// so every weight byte moves in fully coalesced 128-bit loads, and the
-// activations are staged once per workgroup in LDS.
+// 64-lane wavefront reads one 1 KiB block of packed values per 16-byte load
+// (int4: one block per 64-column chunk; int8: two, one per tile of the
+// pair-tile), so every weight byte moves in fully coalesced 128-bit loads,
+// and the activations are staged once per workgroup in LDS.
 //
 // Affine group identity used by every kernel: for a group of G input columns
 // with scale s and bias b,  sum_c (s q_c + b) x_c = s sum_c q_c x_c + b sum_c x_c,
@@ -61,14 +62,20 @@ constexpr int kGemvGateUpWaves = 8;
 // workgroup = one row j, one gate/up pair-tile p (16 gate rows + the 16
 // matching up rows) and one split z of the 64-column chunks of H (chunks
 // z, z + S, ...); its 8 waves take every 8th chunk of the split.  Per lane and
-// chunk: one 16-byte load = 8 gate + 8 up values for each of two 32-column
-// halves.  The weight and scale loads of a wave's first chunks are issued
-// before the row's activations are staged: they do not depend on them.
-template <int ACT>
+// chunk: 8 gate + 8 up values for each of two 32-column halves, in one
+// 16-byte load (int4) or two (int8: the gate plane, then the up plane).  The
+// weight and scale loads of a wave's first chunks are issued before the row's
+// activations are staged: they do not depend on them.  int4 products run as
+// packed 16-bit dot products of re-based nibbles with the raw activations;
+// int8 bytes multiply activations staged as fp32.
+template <int ACT, int BITS>
 __global__ __launch_bounds__(64 * kGemvGateUpWaves) void k_gateup_gemv(FfnArgs a) {
   constexpr int NW = kGemvGateUpWaves;
-  __shared__ __attribute__((aligned(16))) uint16_t xs[kMaxH];
+  constexpr int NQ = BITS / 4;   // 16-byte loads per lane and chunk
+  __shared__ __attribute__((aligned(16))) uint8_t xraw[(BITS == 8 ? 4 : 2) * kMaxH];
   __shared__ float sx[kMaxH / 32];
+  uint16_t* xs = reinterpret_cast<uint16_t*>(xraw);   // int4: activations as given
+  float* xf = reinterpret_cast<float*>(xraw);          // int8: activations as fp32
   __shared__ float red[NW][2][16];
   const uint8_t* blob;
   int t, inter;
@@ -88,9 +95,9 @@ __global__ __launch_bounds__(64 * kGemvGateUpWaves) void k_gateup_gemv(FfnArgs a
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, kb = lane >> 4;
   const int nc = H / 64;
-  const uint4* qblk = reinterpret_cast<const uint4*>(blob) + static_cast<size_t>(p) * nc * 64;
-  const uint8_t* ssec = blob + blob_gu_s(H, inter);
-  uint4 q[kGemvBatch];
+  const uint4* qblk = reinterpret_cast<const uint4*>(blob) + static_cast<size_t>(p) * nc * 64 * NQ;
+  const uint8_t* ssec = blob + blob_gu_s(H, inter, BITS);
+  uint4 q[kGemvBatch][NQ];
   uint2 sv[kGemvBatch][2];
   // chunk of the wave's i-th step: z + S (wave + NW i)
   auto chunk = [&](int i) { return z + kGemvSplit * (wave + NW * i); };
@@ -99,7 +106,8 @@ __global__ __launch_bounds__(64 * kGemvGateUpWaves) void k_gateup_gemv(FfnArgs a
     for (int b = 0; b < kGemvBatch; ++b) {
       const int c = chunk(i0 + b);
       if (c < nc) {   // uniform
-        q[b] = qblk[static_cast<size_t>(c) * 64 + lane];
+#pragma unroll
+        for (int h = 0; h < NQ; ++h) q[b][h] = qblk[(static_cast<size_t>(c) * NQ + h) * 64 + lane];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           const int g = (64 * c + 32 * ks) / G;
@@ -110,15 +118,35 @@ __global__ __launch_bounds__(64 * kGemvGateUpWaves) void k_gateup_gemv(FfnArgs a
   };
   issue(0);
   const uint16_t* xr = a.x + static_cast<size_t>(t) * H;
-  for (int c = threadIdx.x * 8; c < H; c += 64 * NW * 8)
-    *reinterpret_cast<uint4*>(xs + c) = *reinterpret_cast<const uint4*>(xr + c);
+  for (int c = threadIdx.x * 8; c < H; c += 64 * NW * 8) {
+    const uint4 v = *reinterpret_cast<const uint4*>(xr + c);
+    if constexpr (BITS == 8) {
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      float f[8];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        f[2 * d] = act_to_f32<ACT>(w[d] & 0xFFFFu);
+        f[2 * d + 1] = act_to_f32<ACT>(w[d] >> 16);
+      }
+      *reinterpret_cast<float4*>(xf + c) = make_float4(f[0], f[1], f[2], f[3]);
+      *reinterpret_cast<float4*>(xf + c + 4) = make_float4(f[4], f[5], f[6], f[7]);
+    } else {
+      *reinterpret_cast<uint4*>(xs + c) = v;
+    }
+  }
   __syncthreads();
   group_sums(H, G, 8, sx, [&](int i) {
-    const uint4 v = *reinterpret_cast<const uint4*>(xs + i);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     float s = 0.0f;
+    if constexpr (BITS == 8) {
+      const float4 u = *reinterpret_cast<const float4*>(xf + i);
+      const float4 v = *reinterpret_cast<const float4*>(xf + i + 4);
+      s = ((u.x + u.y) + (u.z + u.w)) + ((v.x + v.y) + (v.z + v.w));
+    } else {
+      const uint4 v = *reinterpret_cast<const uint4*>(xs + i);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int d = 0; d < 4; ++d) s += act_to_f32<ACT>(w[d] & 0xFFFFu) + act_to_f32<ACT>(w[d] >> 16);
+      for (int d = 0; d < 4; ++d) s += act_to_f32<ACT>(w[d] & 0xFFFFu) + act_to_f32<ACT>(w[d] >> 16);
+    }
     return s;
   });
   __syncthreads();
@@ -137,14 +165,26 @@ __global__ __launch_bounds__(64 * kGemvGateUpWaves) void k_gateup_gemv(FfnArgs a
           const uint2 v = sv[b][ks];
           const float sA = f16_bits_to_f32(v.x & 0xFFFFu), bA = f16_bits_to_f32(v.x >> 16);
           const float sB = f16_bits_to_f32(v.y & 0xFFFFu), bB = f16_bits_to_f32(v.y >> 16);
-          const uint4 xv = *reinterpret_cast<const uint4*>(xs + col);
-          const float pA = word_dot_v<ACT>(ks ? q[b].y : q[b].x, xv);
-          const float pB = word_dot_v<ACT>(ks ? q[b].w : q[b].z, xv);
-          accA = fmaf(16.0f * sA, pA, accA);
-          accB = fmaf(16.0f * sB, pB, accB);
-          if (kb == 0 && ((64 * c + 32 * ks) % G) == 0) {
-            accA = fmaf(bA - 16.0f * sA, sx[g], accA);
-            accB = fmaf(bB - 16.0f * sB, sx[g], accB);
+          if constexpr (BITS == 8) {
+            // plane 0 = gate, plane 1 = up; words 0, 1 = half 0, words 2, 3 = half 1
+            const float pA = ks ? bytes8_dot(q[b][0].z, q[b][0].w, xf + col) : bytes8_dot(q[b][0].x, q[b][0].y, xf + col);
+            const float pB = ks ? bytes8_dot(q[b][1].z, q[b][1].w, xf + col) : bytes8_dot(q[b][1].x, q[b][1].y, xf + col);
+            accA = fmaf(sA, pA, accA);
+            accB = fmaf(sB, pB, accB);
+            if (kb == 0 && ((64 * c + 32 * ks) % G) == 0) {
+              accA = fmaf(bA, sx[g], accA);
+              accB = fmaf(bB, sx[g], accB);
+            }
+          } else {
+            const uint4 xv = *reinterpret_cast<const uint4*>(xs + col);
+            const float pA = word_dot_v<ACT>(ks ? q[b][0].y : q[b][0].x, xv);
+            const float pB = word_dot_v<ACT>(ks ? q[b][0].w : q[b][0].z, xv);
+            accA = fmaf(16.0f * sA, pA, accA);
+            accB = fmaf(16.0f * sB, pB, accB);
+            if (kb == 0 && ((64 * c + 32 * ks) % G) == 0) {
+              accA = fmaf(bA - 16.0f * sA, sx[g], accA);
+              accB = fmaf(bB - 16.0f * sB, sx[g], accB);
+            }
           }
         }
       }
@@ -173,7 +213,9 @@ __global__ __launch_bounds__(64 * kGemvGateUpWaves) void k_gateup_gemv(FfnArgs a
 // w / 4 + 4 i of the inter dimension).  After the weight and scale loads are
 // issued, the row's h = silu(gate) * up is formed in LDS from the gate/up
 // splits (added in split order), with its group sums.
+template <int BITS>
 __global__ __launch_bounds__(64 * kGemvWaves) void k_down_gemv(FfnArgs a) {
+  constexpr int NQ = BITS / 4;
   __shared__ __attribute__((aligned(16))) float hs[kMaxInter];
   __shared__ float sh[kMaxInter / 32];
   __shared__ float red[4][4][2][16];   // K quarter, pair-tile, A / B, row
@@ -194,16 +236,18 @@ __global__ __launch_bounds__(64 * kGemvWaves) void k_down_gemv(FfnArgs a) {
   const int pc = min(p, H / 32 - 1);   // loads of a wave past the last pair-tile stay in range
   const int n = lane & 15, kb = lane >> 4;
   const int nc = inter / 64;
-  const uint4* qblk = reinterpret_cast<const uint4*>(blob + blob_d_q(H, inter)) + static_cast<size_t>(pc) * nc * 64;
-  const uint8_t* ssec = blob + blob_d_s(H, inter, G);
-  uint4 q[kGemvBatch];
+  const uint4* qblk =
+      reinterpret_cast<const uint4*>(blob + blob_d_q(H, inter, BITS)) + static_cast<size_t>(pc) * nc * 64 * NQ;
+  const uint8_t* ssec = blob + blob_d_s(H, inter, G, BITS);
+  uint4 q[kGemvBatch][NQ];
   uint2 sv[kGemvBatch][2];
   auto issue = [&](int c0) {
 #pragma unroll
     for (int b = 0; b < kGemvBatch; ++b) {
       const int c = c0 + 4 * b;
       if (c < nc) {   // uniform
-        q[b] = qblk[static_cast<size_t>(c) * 64 + lane];
+#pragma unroll
+        for (int h = 0; h < NQ; ++h) q[b][h] = qblk[(static_cast<size_t>(c) * NQ + h) * 64 + lane];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           const int g = (64 * c + 32 * ks) / G;
@@ -244,8 +288,14 @@ __global__ __launch_bounds__(64 * kGemvWaves) void k_down_gemv(FfnArgs a) {
           const uint2 v = sv[b][ks];
           const float sA = f16_bits_to_f32(v.x & 0xFFFFu), bA = f16_bits_to_f32(v.x >> 16);
           const float sB = f16_bits_to_f32(v.y & 0xFFFFu), bB = f16_bits_to_f32(v.y >> 16);
-          const float pA = word_dot_q(ks ? q[b].y : q[b].x, hs + col);
-          const float pB = word_dot_q(ks ? q[b].w : q[b].z, hs + col);
+          float pA, pB;
+          if constexpr (BITS == 8) {
+            pA = ks ? bytes8_dot(q[b][0].z, q[b][0].w, hs + col) : bytes8_dot(q[b][0].x, q[b][0].y, hs + col);
+            pB = ks ? bytes8_dot(q[b][1].z, q[b][1].w, hs + col) : bytes8_dot(q[b][1].x, q[b][1].y, hs + col);
+          } else {
+            pA = word_dot_q(ks ? q[b][0].y : q[b][0].x, hs + col);
+            pB = word_dot_q(ks ? q[b][0].w : q[b][0].z, hs + col);
+          }
           accA = fmaf(sA, pA, accA);
           accB = fmaf(sB, pB, accB);
           if (kb == 0 && ((64 * c + 32 * ks) % G) == 0) {
@@ -429,15 +479,22 @@ __global__ __launch_bounds__(256) void k_epilogue(const float* __restrict__ y, f
 hipError_t launch_gateup_gemv(int act, const FfnArgs& a, hipStream_t s) {
   const int rows = a.T * a.K + (a.Is > 0 ? a.T : 0);
   dim3 grid(rows, (a.hstride + 15) / 16, kGemvSplit);
-  if (act == 2) hipLaunchKernelGGL(k_gateup_gemv<2>, grid, dim3(64 * kGemvGateUpWaves), 0, s, a);
-  else hipLaunchKernelGGL(k_gateup_gemv<1>, grid, dim3(64 * kGemvGateUpWaves), 0, s, a);
+  const dim3 block(64 * kGemvGateUpWaves);
+  if (a.bits == 8) {
+    if (act == 2) hipLaunchKernelGGL((k_gateup_gemv<2, 8>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_gateup_gemv<1, 8>), grid, block, 0, s, a);
+  } else {
+    if (act == 2) hipLaunchKernelGGL((k_gateup_gemv<2, 4>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_gateup_gemv<1, 4>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_down_gemv(const FfnArgs& a, hipStream_t s) {
   const int rows = a.T * a.K + (a.Is > 0 ? a.T : 0);
   dim3 grid(rows, (a.H + 127) / 128);
-  hipLaunchKernelGGL(k_down_gemv, grid, dim3(64 * kGemvWaves), 0, s, a);
+  if (a.bits == 8) hipLaunchKernelGGL(k_down_gemv<8>, grid, dim3(64 * kGemvWaves), 0, s, a);
+  else hipLaunchKernelGGL(k_down_gemv<4>, grid, dim3(64 * kGemvWaves), 0, s, a);
   return hipGetLastError();
 }
 

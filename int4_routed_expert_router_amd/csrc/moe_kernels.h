@@ -33,6 +33,7 @@ struct FfnArgs {
   float* hsum;                // [rows][hstride/16] sums of h over 16-column blocks
   int T, H, K, I, Is, G, E;
   int hstride;                // max(I, Is)
+  int bits;                   // expert weight width, 4 or 8 (8: GEMV family only)
 };
 
 // Units of the grouped family, written by the bucketing kernel.  A unit is up

@@ -45,25 +45,38 @@ __device__ __forceinline__ uint32_t gen_word8(uint32_t key0, uint32_t layer, uin
   return r.v[(j & 31) >> 3];
 }
 
+// int8: values j .. j+7 (j a multiple of 8) = the bytes of words (j%16)/4 and
+// (j%16)/4 + 1 of block j/16, in natural order
+__device__ __forceinline__ uint2 gen_bytes8(uint32_t key0, uint32_t layer, uint32_t eid, uint32_t tensor, uint64_t j) {
+  const P4 r = philox(static_cast<uint32_t>(j >> 4), eid, tensor, 0, key0, layer);
+  return (j & 8) ? make_uint2(r.v[2], r.v[3]) : make_uint2(r.v[0], r.v[1]);
+}
+
+// bias_mul = -2^(bits-1): b = -8 s for int4, -128 s for int8 (exact)
 __device__ __forceinline__ uint32_t gen_scale_bias(uint32_t key0, uint32_t layer, uint32_t eid, uint32_t tensor,
-                                                   uint64_t j, float lo, float span) {
+                                                   uint64_t j, float lo, float span, float bias_mul) {
 #pragma clang fp contract(off)
   const P4 r = philox(static_cast<uint32_t>(j >> 2), eid, tensor, 0, key0, layer);
   const float u = static_cast<float>(r.v[j & 3] >> 8) * 5.9604644775390625e-8f;  // 2^-24, exact
   const float prod = u * span;
   const float s32 = prod + lo;
   const _Float16 s = static_cast<_Float16>(s32);
-  const _Float16 b = static_cast<_Float16>(-8.0f * static_cast<float>(s));
+  const _Float16 b = static_cast<_Float16>(bias_mul * static_cast<float>(s));
   return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, s)) |
          (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
 }
 
+// One work unit writes one 16-byte lane record of a value block (int4: the
+// lane's four words of a 1 KiB chunk block; int8: the lane's 16 bytes in one
+// tile plane of a 2 KiB chunk block) or one 8-byte scale entry.
+template <int BITS>
 __global__ __launch_bounds__(256) void k_fill(uint32_t key0, uint32_t layer, int expert_first, int H, int I, int G,
                                               float lo, float span, uint8_t* dst, uint64_t stride) {
+  constexpr int NQ = BITS / 4;
   const uint32_t eid = static_cast<uint32_t>(expert_first + static_cast<int>(blockIdx.y));
   uint8_t* blob = dst + blockIdx.y * stride;
-  const uint64_t u_gu = static_cast<uint64_t>(I / 16) * (H / 64) * 64;
-  const uint64_t u_d = static_cast<uint64_t>(H / 32) * (I / 64) * 64;
+  const uint64_t u_gu = static_cast<uint64_t>(I / 16) * (H / 64) * 64 * NQ;
+  const uint64_t u_d = static_cast<uint64_t>(H / 32) * (I / 64) * 64 * NQ;
   const uint64_t u_gus = static_cast<uint64_t>(I / 16) * (H / G) * 16;
   const uint64_t u_ds = static_cast<uint64_t>(H / 32) * (I / G) * 16;
   const uint64_t total = u_gu + u_d + u_gus + u_ds;
@@ -74,10 +87,28 @@ __global__ __launch_bounds__(256) void k_fill(uint32_t key0, uint32_t layer, int
       const int in_dim = gu ? H : I;
       const int nc = in_dim / 64;
       const int l = static_cast<int>(v & 63);
+      const int n = l & 15, kb = l >> 4;
+      uint8_t* sec = blob + (gu ? 0 : static_cast<uint64_t>(I) * H * BITS / 4);
+      if constexpr (BITS == 8) {
+        const int tile = static_cast<int>((v >> 6) & 1);
+        const uint64_t blk = v >> 7;
+        const int c = static_cast<int>(blk % nc);
+        const int p = static_cast<int>(blk / nc);
+        const int row = gu ? 16 * p + n : 32 * p + 16 * tile + n;
+        const uint32_t tensor = gu ? static_cast<uint32_t>(tile) : 2u;
+        uint2 half[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int col = 64 * c + 32 * ks + 8 * kb;
+          half[ks] = gen_bytes8(key0, layer, eid, tensor, static_cast<uint64_t>(row) * in_dim + col);
+        }
+        *reinterpret_cast<uint4*>(sec + blk * 2048 + 1024 * tile + 16 * l) =
+            make_uint4(half[0].x, half[0].y, half[1].x, half[1].y);
+        continue;
+      }
       const uint64_t blk = v >> 6;
       const int c = static_cast<int>(blk % nc);
       const int p = static_cast<int>(blk / nc);
-      const int n = l & 15, kb = l >> 4;
       uint32_t words[4];
 #pragma unroll
       for (int wd = 0; wd < 4; ++wd) {
@@ -88,7 +119,6 @@ __global__ __launch_bounds__(256) void k_fill(uint32_t key0, uint32_t layer, int
         const uint64_t j = static_cast<uint64_t>(row) * in_dim + col;
         words[wd] = to_blob_word(gen_word8(key0, layer, eid, tensor, j));
       }
-      uint8_t* sec = blob + (gu ? 0 : static_cast<uint64_t>(I) * H);
       *reinterpret_cast<uint4*>(sec + blk * 1024 + 16 * l) = make_uint4(words[0], words[1], words[2], words[3]);
     } else {
       const bool gu = u < u_gu + u_d + u_gus;
@@ -105,9 +135,9 @@ __global__ __launch_bounds__(256) void k_fill(uint32_t key0, uint32_t layer, int
         const int row = gu ? 16 * p + n : 32 * p + 16 * tile + n;
         const uint32_t tensor = gu ? 3u + tile : 5u;
         const uint64_t j = static_cast<uint64_t>(row) * ng + g;
-        ab[tile] = gen_scale_bias(key0, layer, eid, tensor, j, lo, span);
+        ab[tile] = gen_scale_bias(key0, layer, eid, tensor, j, lo, span, -static_cast<float>(1 << (BITS - 1)));
       }
-      const uint64_t sec = 3ull * I * H / 2 + (gu ? 0 : 8ull * I * H / G);
+      const uint64_t sec = 3ull * I * H * BITS / 8 + (gu ? 0 : 8ull * I * H / G);
       *reinterpret_cast<uint2*>(blob + sec + v * 8) = make_uint2(ab[0], ab[1]);
     }
   }
@@ -125,17 +155,22 @@ thread_local char g_err[256] = "";
 }  // namespace
 
 extern "C" moe_status moe_synth_fill_experts(uint64_t seed, int32_t layer, int32_t expert_first, int32_t n_experts,
-                                             int32_t H, int32_t I, int32_t G, float lo, float span, uint8_t* dst,
-                                             uint64_t stride, moe_stream stream) {
-  const uint64_t bytes = moe_blob_bytes(H, I, G);
+                                             int32_t H, int32_t I, int32_t G, int32_t bits, float lo, float span,
+                                             uint8_t* dst, uint64_t stride, moe_stream stream) {
+  const uint64_t bytes = moe_blob_bytes_q(H, I, G, bits);
   if (bytes == 0 || n_experts < 0 || layer < 0 || expert_first < 0) return MOE_ESHAPE;
   if (n_experts == 0) return MOE_OK;
   if (!dst || (reinterpret_cast<uintptr_t>(dst) % 256) || stride % 256 || stride < bytes) return MOE_EINVAL;
   const uint64_t units = bytes / 16;  // at least this many work units per expert
   const unsigned gx = static_cast<unsigned>(units / 256 / 4 + 1);
-  hipLaunchKernelGGL(k_fill, dim3(gx, n_experts), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
-                     static_cast<uint32_t>(seed & 0xFFFFFFFFu), static_cast<uint32_t>(layer), expert_first, H, I, G,
-                     lo, span, dst, stride);
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const uint32_t k0 = static_cast<uint32_t>(seed & 0xFFFFFFFFu), ly = static_cast<uint32_t>(layer);
+  if (bits == 8)
+    hipLaunchKernelGGL(k_fill<8>, dim3(gx, n_experts), dim3(256), 0, s, k0, ly, expert_first, H, I, G, lo, span, dst,
+                       stride);
+  else
+    hipLaunchKernelGGL(k_fill<4>, dim3(gx, n_experts), dim3(256), 0, s, k0, ly, expert_first, H, I, G, lo, span, dst,
+                       stride);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 

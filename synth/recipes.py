@@ -178,16 +178,17 @@ def expert_raw(wl: Workload, layer: int, expert: int, shared: bool = False, seed
     return out
 
 
-def random_affine_bias(raw, seed: int):
-    """Replace b = -8*s with general affine biases b = fp16(-s * U(0, 15)).
+def random_affine_bias(raw, seed: int, bits: int = 4):
+    """Replace b = -2**(bits-1)*s with general affine biases b = fp16(-s * U(0, 2**bits - 1)).
 
     Used by tests to exercise arbitrary per-group biases.
     """
     rng = np.random.default_rng([seed, 0xB1A5])
+    top = float((1 << bits) - 1)
     out = {}
     for name, (q, s, _) in raw.items():
         sv = s.view(np.float16).astype(np.float32)
-        b = (-sv * rng.uniform(0.0, 15.0, size=s.shape).astype(np.float32)).astype(np.float16)
+        b = (-sv * rng.uniform(0.0, top, size=s.shape).astype(np.float32)).astype(np.float16)
         out[name] = (q, s, b.view(np.uint16))
     return out
 

@@ -18,7 +18,7 @@ def torch_mod():
 def desc_for(wl, path=0, act=None, shared_inter=None):
     from int4_routed_expert_router_amd.api import Desc
     return Desc(wl.hidden, wl.n_experts, wl.top_k, wl.inter, wl.shared_inter if shared_inter is None else shared_inter,
-                wl.group, act or wl.act_dtype, path)
+                wl.group, act or wl.act_dtype, path, wl.bits)
 
 
 class DeviceLayer:
@@ -31,7 +31,7 @@ class DeviceLayer:
         self.wl, self.layer = wl, layer
         self.general_bias_seed = general_bias_seed
         h = wl.hidden
-        self.stride = api.blob_bytes(h, wl.inter, wl.group)
+        self.stride = api.blob_bytes(h, wl.inter, wl.group, wl.bits)
         wr = synth.router_weights(wl, layer)
         if router_scale != 1.0:
             wr = synth.f32_to_f16_bits(wr.view(np.float16).astype(np.float32) * np.float32(router_scale))
@@ -45,29 +45,31 @@ class DeviceLayer:
         self.experts = torch.empty(wl.n_experts * self.stride, dtype=torch.uint8, device="cuda")
         if use_gpu_fill and general_bias_seed is None:
             api.synth_fill_experts(wl.weight_seed, layer, 0, wl.n_experts, h, wl.inter, wl.group, wl.scale_lo,
-                                   wl.scale_hi, self.experts, self.stride)
+                                   wl.scale_hi, self.experts, self.stride, bits=wl.bits)
         else:
             host = np.zeros(wl.n_experts * self.stride, np.uint8)
             for e in range(wl.n_experts):
-                host[e * self.stride:(e + 1) * self.stride] = api.pack_expert(self.raw(e), h, wl.inter, wl.group)
+                host[e * self.stride:(e + 1) * self.stride] = api.pack_expert(self.raw(e), h, wl.inter, wl.group,
+                                                                              wl.bits)
             self.experts.copy_(torch.from_numpy(host))
         self.has_shared = shared and wl.shared_inter > 0
         self.shared = None
         if self.has_shared:
-            sb = api.blob_bytes(h, wl.shared_inter, wl.group)
+            sb = api.blob_bytes(h, wl.shared_inter, wl.group, wl.bits)
             self.shared = torch.empty(sb, dtype=torch.uint8, device="cuda")
             if use_gpu_fill and general_bias_seed is None:
                 api.synth_fill_experts(wl.weight_seed, layer, wl.n_experts, 1, h, wl.shared_inter, wl.group,
-                                       wl.scale_lo, wl.scale_hi, self.shared, sb)
+                                       wl.scale_lo, wl.scale_hi, self.shared, sb, bits=wl.bits)
             else:
                 self.shared.copy_(torch.from_numpy(api.pack_expert(self.raw(0, shared=True), h, wl.shared_inter,
-                                                                   wl.group)))
+                                                                   wl.group, wl.bits)))
         self._cache = {}
 
     def raw(self, e, shared=False):
         r = synth.expert_raw(self.wl, self.layer, e, shared=shared)
         if self.general_bias_seed is not None:
-            r = synth.random_affine_bias(r, self.general_bias_seed + 7919 * e + (104729 if shared else 0))
+            r = synth.random_affine_bias(r, self.general_bias_seed + 7919 * e + (104729 if shared else 0),
+                                         bits=self.wl.bits)
         return r
 
     def api_layer(self):
@@ -77,7 +79,7 @@ class DeviceLayer:
     def oracle_expert(self, e):
         if e not in self._cache:
             r = self.raw(e)
-            self._cache[e] = mo.ExpertWeights.from_quant(r["gate"], r["up"], r["down"], self.wl.group)
+            self._cache[e] = mo.ExpertWeights.from_quant(r["gate"], r["up"], r["down"], self.wl.group, self.wl.bits)
         return self._cache[e]
 
     def oracle_shared(self):
@@ -85,7 +87,8 @@ class DeviceLayer:
             return None
         if "s" not in self._cache:
             r = self.raw(0, shared=True)
-            self._cache["s"] = mo.ExpertWeights.from_quant(r["gate"], r["up"], r["down"], self.wl.group)
+            self._cache["s"] = mo.ExpertWeights.from_quant(r["gate"], r["up"], r["down"], self.wl.group,
+                                                           self.wl.bits)
         return self._cache["s"]
 
     def router_f64(self):

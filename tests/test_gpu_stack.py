@@ -73,9 +73,14 @@ def oracle_sets(x64, wr64, b64, gpu_idx, k):
     return np.stack(sets), flagged
 
 
-@pytest.mark.parametrize("path,n_tokens", [(1, 3), (2, 40)], ids=["gemv", "grouped"])
-def test_stack_teacher_forced_parity(path, n_tokens):
-    wl = STACK
+# int8 experts: 12 tokens x 4 rows are past the GEMV row limit, and AUTO still
+# keeps int8 on the GEMV family
+STACK8 = dataclasses.replace(STACK, name="stack_i8", bits=8, scale_lo=1e-4, scale_hi=1e-3, weight_seed=32)
+
+
+@pytest.mark.parametrize("path,n_tokens,wl", [(1, 3, STACK), (2, 40, STACK), (0, 12, STACK8)],
+                         ids=["gemv", "grouped", "auto_int8"])
+def test_stack_teacher_forced_parity(path, n_tokens, wl):
     st = Stack(wl, n_tokens, path)
     st.run_eager()
     got = st.snapshot()

@@ -2,6 +2,7 @@
 declare, the host packer and the pool policy match the oracle, and argument
 validation rejects bad calls before touching the GPU."""
 import ctypes as C
+import dataclasses
 import os
 import re
 
@@ -52,6 +53,37 @@ def test_blob_bytes_and_packer_match_oracle():
         for name in raw:
             for a, b in zip(raw[name], back[name]):
                 assert np.array_equal(a, b)
+
+
+def test_int8_blob_bytes_and_packer_match_oracle():
+    from int4_routed_expert_router_amd import api
+    assert api.blob_bytes(2048, 512, 64, 8) == 3_342_336 == blob_ref.blob_bytes(2048, 512, 64, bits=8)
+    assert api.blob_bytes(256, 64, 32, 6) == 0
+    for wl in (synth.TINY, synth.DEC80I8):
+        wl8 = wl if wl.bits == 8 else dataclasses.replace(wl, bits=8)
+        raw = synth.expert_raw(wl8, 1, 2)
+        got = api.pack_expert(raw, wl8.hidden, wl8.inter, wl8.group, 8)
+        assert got.size == blob_ref.blob_bytes(wl8.hidden, wl8.inter, wl8.group, bits=8)
+        back = blob_ref.parse_blob(got, wl8.hidden, wl8.inter, wl8.group, bits=8)
+        for name in raw:
+            for a, b in zip(raw[name], back[name]):
+                assert np.array_equal(a, b)
+        # the oracle's own writer gives the same bytes
+        want = blob_ref.pack_blob(raw["gate"], raw["up"], raw["down"], wl8.hidden, wl8.inter, wl8.group, bits=8)
+        assert np.array_equal(got, want)
+
+
+def test_int8_desc_validation():
+    from int4_routed_expert_router_amd import api, MoeError
+    from int4_routed_expert_router_amd._lib import MOE_PATH_GEMV
+    n8 = api.workspace_bytes(api.Desc(2048, 512, 10, 512, 512, 64, weight_bits=8), 64)
+    assert n8 == api.workspace_bytes(api.Desc(2048, 512, 10, 512, 512, 64), 64)
+    api.workspace_bytes(api.Desc(256, 16, 2, 64, 64, 32, path=MOE_PATH_GEMV, weight_bits=8), 4)
+    api.workspace_bytes(api.Desc(256, 16, 2, 64, 64, 32, weight_bits=0), 4)   # 0 reads as int4
+    with pytest.raises(MoeError, match="MOE_ESHAPE"):
+        api.workspace_bytes(api.Desc(256, 16, 2, 64, 64, 32, weight_bits=6), 4)
+    with pytest.raises(MoeError, match="MOE_ESHAPE"):   # int8 has no grouped kernels
+        api.workspace_bytes(api.Desc(256, 16, 2, 64, 64, 32, path=2, weight_bits=8), 4)
 
 
 def test_packer_rejects_bad_nibbles():
