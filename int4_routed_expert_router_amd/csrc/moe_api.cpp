@@ -137,16 +137,14 @@ bool use_grouped(const moe_layer_desc* d, int T) {
 moe_status do_route(const moe_layer_desc* d, const moe_layer_weights* w, const void* x, int T, int32_t* idx,
                     float* tw, float* gamma, float* part, float* logits_out, hipStream_t s, int layer = -1) {
   hipError_t e = timer_mark(true, MOE_TIME_ROUTER, layer, s);
-  moe::RouterParts rp{1, false, true};
+  moe::RouterParts rp{1, true};
   if (e == hipSuccess)
     e = moe::launch_router_logits(d->act_dtype, static_cast<const uint16_t*>(x), w->router_w, w->router_bias, part, T,
                                   d->hidden, d->n_experts, s, &rp);
   if (e == hipSuccess) e = timer_mark(false, MOE_TIME_ROUTER, layer, s);
   if (e != hipSuccess) return hip_fail(e, "router kernel launch");
-  const uint16_t* gate_w = rp.gate ? nullptr : w->router_w + static_cast<size_t>(d->n_experts) * d->hidden;
-  e = moe::launch_topk(d->act_dtype, part, rp.n_part, rp.biased ? nullptr : w->router_bias,
-                       static_cast<const uint16_t*>(x), gate_w, d->hidden, T, d->n_experts, d->top_k, idx, tw, gamma,
-                       logits_out, s);
+  e = moe::launch_topk(part, rp.n_part, rp.biased ? nullptr : w->router_bias, T, d->n_experts, d->top_k, idx, tw,
+                       gamma, logits_out, s);
   if (e != hipSuccess) return hip_fail(e, "top-k kernel launch");
   return MOE_OK;
 }

@@ -64,27 +64,23 @@ inline int max_units(int T, int K, int E, bool shared) {
   return n_act + rows / kSubTokens + (shared ? (T + kSubTokens - 1) / kSubTokens : 0);
 }
 
-// Router logits.  The matrix-core path (T >= kRouterMfmaMinTokens) covers
-// the E expert rows only, splits the hidden dimension into n_part slices
-// (n_part <= kRouterMaxParts) and writes unbiased partial sums
-// part[p][t][row]; top-K then computes the shared-gate logit itself.  The
-// per-row path writes finished logits of all E+1 rows (bias included) as a
-// single part.
+// Router logits.  The matrix-core path (T >= kRouterMfmaMinTokens) splits
+// the hidden dimension into n_part slices (n_part <= kRouterMaxParts) and
+// writes unbiased partial sums part[p][t][row] of all E+1 rows (row E, the
+// shared gate, from vector-unit products).  The per-row path writes finished
+// logits of all E+1 rows (bias included) as a single part.
 struct RouterParts {
   int n_part;
   bool biased;   // bias already added
-  bool gate;     // column E holds the shared-gate logit
 };
 hipError_t launch_router_logits(int act, const uint16_t* x, const uint16_t* wr, const float* bias, float* part,
                                 int T, int H, int E, hipStream_t s, RouterParts* out);
 // Top-K over z[t][e] = sum_p part[p][t][e] (p ascending) + bias[e] (bias may
-// be null).  The shared-gate logit is column E of the parts, or x[t] . gate_w
-// when gate_w is non-null.  Writes the selection, the renormalised weights,
-// the shared gate (when gamma is non-null) and, when logits is non-null, the
-// logits themselves.
-hipError_t launch_topk(int act, const float* part, int n_part, const float* bias, const uint16_t* x,
-                       const uint16_t* gate_w, int H, int T, int E, int K, int32_t* idx, float* w, float* gamma,
-                       float* logits, hipStream_t s);
+// be null); the shared-gate logit is column E, summed the same way.  Writes
+// the selection, the renormalised weights, the shared gate (when gamma is
+// non-null) and, when logits is non-null, the logits themselves.
+hipError_t launch_topk(const float* part, int n_part, const float* bias, int T, int E, int K, int32_t* idx, float* w,
+                       float* gamma, float* logits, hipStream_t s);
 hipError_t launch_permute(const int32_t* idx, int n, int E, int32_t* off, int32_t* perm, int32_t* inv,
                           const UnitPlan* plan, hipStream_t s);
 

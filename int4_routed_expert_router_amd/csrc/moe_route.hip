@@ -100,102 +100,75 @@ __device__ __forceinline__ void shift_up(uint32_t (&a)[N], bool take, std::integ
   ((a[I] = take ? a[I + 1] : a[I]), ...);
 }
 
-// One wave per token; lane l holds experts l, l+64, ... (kJ of them).  Each
-// lane first sorts its own entries by (logit desc, expert index asc), as a
-// 64-bit key (order_key(logit), kJ-1-j).  Then K rounds: the wave maximum of
-// the lanes' head keys picks the logit; among the lanes whose head holds it
-// (one, unless logits tie across lanes) the lowest expert index wins, and
-// the winning lane pops its head.  So ties resolve to the lower expert index.
+// Top-K of one token on one wave.  Lane l holds experts l, l+64, ... (kJ of
+// them).  Each lane first sorts its own entries by (logit desc, expert index
+// asc), as a 64-bit key (order_key(logit), kJ-1-j).  Then K rounds: the wave
+// maximum of the lanes' head keys picks the logit; among the lanes whose head
+// holds it (one, unless logits tie across lanes) the lowest expert index
+// wins, and the winning lane pops its head.  So ties resolve to the lower
+// expert index.  The shared-gate logit is column E of the slices.
 //
-// The shared-gate logit comes from column E of the parts, or, when gate_w is
-// given (the matrix-core router leaves that row out, so that its grid is a
-// whole number of 16-row blocks), from a dot product of x[t] with gate_w
-// computed here: lane l takes columns 512 i + 8 l .. +7 in order, then a wave
-// sum.
-template <int kJ, int ACT>
-__global__ __launch_bounds__(64) void k_topk(const float* __restrict__ part, int n_part,
-                                              const float* __restrict__ bias, const uint16_t* __restrict__ x,
-                                              const uint16_t* __restrict__ gate_w, int H, int T, int E, int K,
-                                              int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-                                              float* __restrict__ gamma, float* __restrict__ logits) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x;   // one token per workgroup: spreads the loads over the compute units
-  if (t >= T) return;
-  // gate operands first (columns past H read column 0 and are zeroed below)
-  constexpr int kGI = kMaxH / 512;
-  uint4 gx[kGI], gw[kGI];
-  const int ngi = gate_w != nullptr ? (H + 511) / 512 : 0;
-#pragma unroll
-  for (int i = 0; i < kGI; ++i) {
-    if (i < ngi) {   // uniform
-      const int c = 512 * i + 8 * lane;
-      const int cc = c < H ? c : 0;
-      gx[i] = *reinterpret_cast<const uint4*>(x + static_cast<size_t>(t) * H + cc);
-      gw[i] = *reinterpret_cast<const uint4*>(gate_w + cc);
-    }
-  }
-  // z = part[0] + part[1] + ... (in order) + bias.  Every load is issued
-  // before any is used: the expert index is clamped to E (the shared-gate
-  // column) and the part index to n_part - 1, both valid memory.
+// topk_issue issues every load of a token (all slices of the lane's kJ
+// logits and of the gate column; indices clamped to valid memory) without
+// using them, so a wave can fetch its next token while it selects this one.
+template <int kJ>
+struct TopkIn {
+  float raw[kRouterMaxParts][kJ];
+  float zg[kRouterMaxParts];
+};
+template <int kJ>
+__device__ __forceinline__ void topk_issue(const float* __restrict__ part, int n_part, int T, int E, int t, int lane,
+                                           TopkIn<kJ>& in) {
   const size_t pstride = static_cast<size_t>(T) * (E + 1);
   const float* z = part + static_cast<size_t>(t) * (E + 1);
-  float raw[kRouterMaxParts][kJ], zgp[kRouterMaxParts], bj[kJ];
 #pragma unroll
   for (int p = 0; p < kRouterMaxParts; ++p) {
     const float* zp = z + min(p, n_part - 1) * pstride;
 #pragma unroll
-    for (int j = 0; j < kJ; ++j) raw[p][j] = zp[min(lane + 64 * j, E)];
-    zgp[p] = zp[E];
+    for (int j = 0; j < kJ; ++j) in.raw[p][j] = zp[min(lane + 64 * j, E)];
+    in.zg[p] = zp[E];
   }
-#pragma unroll
-  for (int j = 0; j < kJ; ++j) bj[j] = bias != nullptr ? bias[min(lane + 64 * j, E - 1)] : 0.0f;
+}
+
+// z = slice 0 + slice 1 + ... (in order) + bias; selection; softmax weights
+// of the selected set; sigmoid gate.  Writes idx/w (and the token's indices
+// to sidx when given), gamma when non-null, logits when non-null.
+template <int kJ>
+__device__ __forceinline__ void topk_finish(TopkIn<kJ>& in, const float (&bj)[kJ], bool has_bias, int n_part, int E,
+                                            int K, int t, int lane, int32_t* __restrict__ topk_idx,
+                                            float* __restrict__ topk_w, float* __restrict__ gamma,
+                                            float* __restrict__ logits, int32_t* sidx) {
   // opaque to the optimiser, so no load is sunk into a branch
 #pragma unroll
   for (int p = 0; p < kRouterMaxParts; ++p) {
 #pragma unroll
-    for (int j = 0; j < kJ; ++j) asm volatile("" : "+v"(raw[p][j]));
-    asm volatile("" : "+v"(zgp[p]));
+    for (int j = 0; j < kJ; ++j) asm volatile("" : "+v"(in.raw[p][j]));
+    asm volatile("" : "+v"(in.zg[p]));
   }
-  float zg = zgp[0];
+  float zg = in.zg[0];
 #pragma unroll
   for (int p = 1; p < kRouterMaxParts; ++p) {
     if (p < n_part) {   // uniform
-      zg += zgp[p];
+      zg += in.zg[p];
 #pragma unroll
-      for (int j = 0; j < kJ; ++j) raw[0][j] += raw[p][j];
+      for (int j = 0; j < kJ; ++j) in.raw[0][j] += in.raw[p][j];
     }
   }
-  if (gate_w != nullptr) {
-    float acc = 0.0f;
+  if (has_bias) {
 #pragma unroll
-    for (int i = 0; i < kGI; ++i) {
-      if (i < ngi && 512 * i + 8 * lane < H) {
-        const uint32_t xs[4] = {gx[i].x, gx[i].y, gx[i].z, gx[i].w};
-        const uint32_t ws[4] = {gw[i].x, gw[i].y, gw[i].z, gw[i].w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc = fmaf(act_to_f32<ACT>(xs[q] & 0xFFFFu), f16_bits_to_f32(ws[q] & 0xFFFFu), acc);
-          acc = fmaf(act_to_f32<ACT>(xs[q] >> 16), f16_bits_to_f32(ws[q] >> 16), acc);
-        }
-      }
-    }
-    zg = wave_sum(acc);
-  }
-  if (bias != nullptr) {
-#pragma unroll
-    for (int j = 0; j < kJ; ++j) raw[0][j] += bj[j];
+    for (int j = 0; j < kJ; ++j) in.raw[0][j] += bj[j];
   }
   if (logits != nullptr) {
     float* lo_out = logits + static_cast<size_t>(t) * (E + 1);
 #pragma unroll
     for (int j = 0; j < kJ; ++j)
-      if (lane + 64 * j < E) lo_out[lane + 64 * j] = raw[0][j];
+      if (lane + 64 * j < E) lo_out[lane + 64 * j] = in.raw[0][j];
     if (lane == 0) lo_out[E] = zg;
   }
   uint32_t hi[kJ], lo[kJ];
 #pragma unroll
   for (int j = 0; j < kJ; ++j) {
-    hi[j] = (lane + 64 * j < E) ? order_key(raw[0][j]) : 0u;
+    hi[j] = (lane + 64 * j < E) ? order_key(in.raw[0][j]) : 0u;
     lo[j] = kJ - 1 - j;
   }
   oddeven_merge_sort<kJ>([&](int a, int b) {
@@ -250,8 +223,31 @@ __global__ __launch_bounds__(64) void k_topk(const float* __restrict__ part, int
   if (lane < K) {
     topk_idx[static_cast<size_t>(t) * K + lane] = my_i;
     topk_w[static_cast<size_t>(t) * K + lane] = ex / s;
+    if (sidx != nullptr) sidx[t * K + lane] = my_i;
   }
   if (lane == 0 && gamma != nullptr) gamma[t] = 1.0f / (1.0f + expf(-zg));
+}
+
+template <int kJ>
+__device__ __forceinline__ void load_bias(const float* __restrict__ bias, int E, int lane, float (&bj)[kJ]) {
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) bj[j] = bias != nullptr ? bias[min(lane + 64 * j, E - 1)] : 0.0f;
+}
+
+// One token per 64-lane workgroup: spreads the loads over the compute units.
+template <int kJ>
+__global__ __launch_bounds__(64) void k_topk(const float* __restrict__ part, int n_part,
+                                              const float* __restrict__ bias, int T, int E, int K,
+                                              int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+                                              float* __restrict__ gamma, float* __restrict__ logits) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x;
+  if (t >= T) return;
+  TopkIn<kJ> in;
+  topk_issue(part, n_part, T, E, t, lane, in);
+  float bj[kJ];
+  load_bias(bias, E, lane, bj);
+  topk_finish(in, bj, bias != nullptr, n_part, E, K, t, lane, topk_idx, topk_w, gamma, logits, nullptr);
 }
 
 // Inclusive prefix sums of two values at once over a 1024-thread block.
@@ -403,7 +399,10 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ to
 // order.  The slice sums go to part[z] (no bias); top-K adds the slices in
 // order and the bias.  Slicing spreads a small batch over all compute units.
 // The fp16 router weights enter bf16 MFMAs as an exact hi + lo pair (fp16 has
-// 11 significant bits); with fp16 activations they enter as they are.
+// 11 significant bits); with fp16 activations they enter as they are.  The
+// shared-gate row E is not a matrix-core row (the grid stays a whole number
+// of 16-row blocks): the workgroups of row block 0 also form its slice sums
+// with exact fp32 products on the vector units and write them to column E.
 template <int ACT>
 __global__ __launch_bounds__(1024) void k_router_mfma(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
                                                       float* __restrict__ part, int T, int H, int E, int steps) {
@@ -411,6 +410,7 @@ __global__ __launch_bounds__(1024) void k_router_mfma(const uint16_t* __restrict
   typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
   typedef float f32x4_t __attribute__((ext_vector_type(4)));
   __shared__ float wpart[16][16][17];   // per-wave partial tiles
+  __shared__ float wgate[16][16];       // per-wave shared-gate partials
   const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, kb = lane >> 4;
@@ -425,20 +425,33 @@ __global__ __launch_bounds__(1024) void k_router_mfma(const uint16_t* __restrict
   const bool tok_ok = tok < T, row_ok = row < E;   // row E (shared gate) is left to top-k
   const uint16_t* xrow = x + static_cast<size_t>(tok_ok ? tok : T - 1) * H + col0;
   const uint16_t* wrow = wr + static_cast<size_t>(row_ok ? row : E - 1) * H + col0;
+  const uint16_t* grow = wr + static_cast<size_t>(E) * H + col0;   // shared-gate row
+  const bool do_gate = blockIdx.x == 0;   // uniform
   f32x4_t acc = {0, 0, 0, 0};
+  float gacc = 0.0f;
   for (int st0 = wave; st0 < nsteps; st0 += kBatch * nw) {
-    uint4 av[kBatch], bv[kBatch];
+    uint4 av[kBatch], bv[kBatch], gv[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int col = 32 * min(st0 + u * nw, nsteps - 1) + 8 * kb;
       av[u] = *reinterpret_cast<const uint4*>(xrow + col);
       bv[u] = *reinterpret_cast<const uint4*>(wrow + col);
+      if (do_gate) gv[u] = *reinterpret_cast<const uint4*>(grow + col);
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       if (st0 + u * nw >= nsteps) break;   // wave-uniform
       if (!tok_ok) av[u] = make_uint4(0, 0, 0, 0);
       if (!row_ok) bv[u] = make_uint4(0, 0, 0, 0);
+      if (do_gate) {
+        const uint32_t xs[4] = {av[u].x, av[u].y, av[u].z, av[u].w};
+        const uint32_t gs[4] = {gv[u].x, gv[u].y, gv[u].z, gv[u].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          gacc = fmaf(act_to_f32<ACT>(xs[i] & 0xFFFFu), f16_bits_to_f32(gs[i] & 0xFFFFu), gacc);
+          gacc = fmaf(act_to_f32<ACT>(xs[i] >> 16), f16_bits_to_f32(gs[i] >> 16), gacc);
+        }
+      }
       if constexpr (ACT == 2) {
         const uint32_t bw[4] = {bv[u].x, bv[u].y, bv[u].z, bv[u].w};
         uint32_t hi[4], lo[4];
@@ -464,7 +477,19 @@ __global__ __launch_bounds__(1024) void k_router_mfma(const uint16_t* __restrict
   // lane holds tokens 4kb..4kb+3 (tile rows) of router row n (tile column)
 #pragma unroll
   for (int i = 0; i < 4; ++i) wpart[wave][4 * kb + i][n] = acc[i];
+  if (do_gate) {
+    // lanes n, n+16, n+32, n+48 hold token n's four column groups
+    gacc += __shfl_xor(gacc, 16, kWave);
+    gacc += __shfl_xor(gacc, 32, kWave);
+    if (kb == 0) wgate[wave][n] = gacc;
+  }
   __syncthreads();
+  if (do_gate && threadIdx.x < 16) {
+    const int t = blockIdx.y * 16 + static_cast<int>(threadIdx.x);
+    float sum = 0.0f;
+    for (int w = 0; w < nw; ++w) sum += wgate[w][threadIdx.x];
+    if (t < T) logits[static_cast<size_t>(t) * (E + 1) + E] = sum;
+  }
   // 256 outputs per tile; a block may have as few as 2 waves (H = 64)
   for (int q = threadIdx.x; q < 256; q += blockDim.x) {
     const int m = q >> 4, c = q & 15;
@@ -490,14 +515,12 @@ static hipError_t launch_router_t(const uint16_t* x, const uint16_t* wr, const f
     hipLaunchKernelGGL(k_router_mfma<ACT>, grid, dim3(64 * nw), 0, s, x, wr, part, T, H, E, steps);
     out->n_part = S;
     out->biased = false;
-    out->gate = false;
   } else {
     const int tpb = (T <= 8) ? T : 8;
     dim3 grid(E + 1, (T + tpb - 1) / tpb);
     hipLaunchKernelGGL(k_router_logits<ACT>, grid, dim3(64), 0, s, x, wr, bias, part, T, H, E, tpb);
     out->n_part = 1;
     out->biased = true;
-    out->gate = true;
   }
   return hipGetLastError();
 }
@@ -508,34 +531,26 @@ hipError_t launch_router_logits(int act, const uint16_t* x, const uint16_t* wr, 
                   : launch_router_t<1>(x, wr, bias, part, T, H, E, s, out);
 }
 
-hipError_t launch_topk(int act, const float* part, int n_part, const float* bias, const uint16_t* x,
-                       const uint16_t* gate_w, int H, int T, int E, int K, int32_t* idx, float* w, float* gamma,
-                       float* logits, hipStream_t s) {
-  const dim3 grid(T), block(64);
-#define TOPK_LAUNCH(J)                                                                                           \
-  do {                                                                                                           \
-    if (act == 2)                                                                                                \
-      hipLaunchKernelGGL((k_topk<J, 2>), grid, block, 0, s, part, n_part, bias, x, gate_w, H, T, E, K, idx, w,   \
-                         gamma, logits);                                                                         \
-    else                                                                                                         \
-      hipLaunchKernelGGL((k_topk<J, 1>), grid, block, 0, s, part, n_part, bias, x, gate_w, H, T, E, K, idx, w,   \
-                         gamma, logits);                                                                         \
+#define MOE_TOPK_DISPATCH(LAUNCH)                                       \
+  do {                                                                  \
+    static_assert(kMaxExperts == 1024, "dispatch covers up to 16 logits per lane"); \
+    if (E <= 64) LAUNCH(1);                                             \
+    else if (E <= 128) LAUNCH(2);                                       \
+    else if (E <= 256) LAUNCH(4);                                       \
+    else if (E <= 512) LAUNCH(8);                                       \
+    else LAUNCH(16);                                                    \
   } while (0)
-  if (E <= 64) {
-    TOPK_LAUNCH(1);
-  } else if (E <= 128) {
-    TOPK_LAUNCH(2);
-  } else if (E <= 256) {
-    TOPK_LAUNCH(4);
-  } else if (E <= 512) {
-    TOPK_LAUNCH(8);
-  } else {
-    static_assert(kMaxExperts == 1024, "top-k dispatch covers up to 16 entries per lane");
-    TOPK_LAUNCH(16);
-  }
+
+hipError_t launch_topk(const float* part, int n_part, const float* bias, int T, int E, int K, int32_t* idx, float* w,
+                       float* gamma, float* logits, hipStream_t s) {
+#define TOPK_LAUNCH(J) \
+  hipLaunchKernelGGL((k_topk<J>), dim3(T), dim3(64), 0, s, part, n_part, bias, T, E, K, idx, w, gamma, logits)
+  MOE_TOPK_DISPATCH(TOPK_LAUNCH);
 #undef TOPK_LAUNCH
   return hipGetLastError();
 }
+
+#undef MOE_TOPK_DISPATCH
 
 hipError_t launch_permute(const int32_t* idx, int n, int E, int32_t* off, int32_t* perm, int32_t* inv,
                           const UnitPlan* plan, hipStream_t s) {
