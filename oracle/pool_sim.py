@@ -23,7 +23,18 @@ it, in plain Python:
        the call fails (pool full);
 * release(layer) unpins every slot of that layer;
 * evict(layer, expert) removes an unpinned resident expert (pinned: busy;
-  not resident: no-op).
+  not resident: no-op);
+* prefetch(layer, experts, step), experts distinct: a best-effort early load
+  of experts predicted for a later acquire (pre-gating: the next layer's
+  router applied to the current layer's input).  Aging is applied first.
+  Requested experts that are resident are left as they are (no count, no
+  pin).  Each other requested expert, in request order, takes the
+  lowest-numbered free slot, else evicts the unpinned resident expert with the
+  smallest (count, last_use, expert id) among those not requested in this
+  call and not loaded by it; with no such slot it is skipped.  A loaded expert
+  enters unpinned with count = 0 and last_use = step, so a correct prediction
+  leaves, after the acquire that hits it (count + 1, last_use = step), the
+  same entry a miss would have made; its blob is copied.
 
 Parity status: pinned by a hand-computed trace in tests/test_oracle_pool.py.
 """
@@ -51,7 +62,7 @@ class PoolSim:
         self.last_use = [[0] * slots for _ in range(n_layers)]
         self.pinned = [[False] * slots for _ in range(n_layers)]
         self.epoch = [0] * n_layers
-        self.hits = self.misses = self.evictions = self.bytes_h2d = 0
+        self.hits = self.misses = self.evictions = self.bytes_h2d = self.prefetches = 0
 
     def _age(self, layer: int, step: int) -> None:
         if self.period == 0:
@@ -113,6 +124,42 @@ class PoolSim:
     def release(self, layer: int) -> None:
         self.pinned[layer] = [False] * self.slots
 
+    def prefetch(self, layer: int, experts, step: int):
+        """Returns a list of (expert, slot, evicted_expert_or_-1) for the experts it loaded, in request order."""
+        experts = [int(e) for e in experts]
+        if len(set(experts)) != len(experts):
+            raise ValueError("experts of one call must be distinct")
+        if any(e < 0 or e >= self.n_experts for e in experts):
+            raise ValueError("expert id out of range")
+        self._age(layer, step)
+        slot_of = self.slot_of[layer]
+        keep = set(experts)            # never evicted by this call
+        loaded = []
+        for e in experts:
+            if slot_of[e] >= 0:
+                continue
+            victim = -1
+            free_slots = [s for s in range(self.slots) if self.expert_in[layer][s] < 0]
+            if free_slots:
+                s = free_slots[0]
+            else:
+                cands = [(self.count[layer][s], self.last_use[layer][s], self.expert_in[layer][s], s)
+                         for s in range(self.slots)
+                         if not self.pinned[layer][s] and self.expert_in[layer][s] not in keep]
+                if not cands:
+                    continue
+                _, _, victim, s = min(cands)
+                slot_of[victim] = -1
+                self.evictions += 1
+            self.expert_in[layer][s] = e
+            slot_of[e] = s
+            self.count[layer][s] = 0
+            self.last_use[layer][s] = step
+            self.prefetches += 1
+            self.bytes_h2d += self.blob_bytes
+            loaded.append((e, s, victim))
+        return loaded
+
     def evict(self, layer: int, expert: int) -> None:
         s = self.slot_of[layer][expert]
         if s < 0:
@@ -126,4 +173,5 @@ class PoolSim:
         self.evictions += 1
 
     def stats(self):
-        return dict(hits=self.hits, misses=self.misses, evictions=self.evictions, bytes_h2d=self.bytes_h2d)
+        return dict(hits=self.hits, misses=self.misses, evictions=self.evictions, bytes_h2d=self.bytes_h2d,
+                    prefetches=self.prefetches)
