@@ -40,6 +40,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--pregate", type=int, default=0,
+                    help="pool80: prefetch this many of the next layer's predicted experts per layer (0 = none)")
+    ap.add_argument("--pool-copy", default="kernel", choices=["kernel", "engine"],
+                    help="pool80: copy misses with the copy kernel (mapped host reads) or the copy engine")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (scale reference for HBM byte counters)")
     return ap.parse_args()
@@ -199,10 +203,14 @@ def cpu_baseline(wl, budget_s):
 def run_pool(args):
     """Slot-pool streaming (pool80): all 48 x 512 expert blobs in pinned host
     memory, 128 HBM slots per layer, batch-1 decode for the workload's steps
-    with the router bias re-drawn every drift period.  Per layer: route, read
-    the indices back, acquire (misses copied on a side stream), expert FFN from
-    the slots, release, residual epilogue.  Reports tokens/s, hit rate and the
-    bytes copied host to device."""
+    with the router bias re-drawn every drift period.  Each token is one call
+    of the native driver (moe_pool_decode_step): per layer, route (and, with
+    pre-gating, the next layer's router on this layer's input), read the
+    indices back, acquire (misses copied on a side stream), prefetch the
+    predicted experts of the next layer (their copies overlap this layer's
+    FFN and the next routing), expert FFN from the slots, residual epilogue,
+    release.  Reports tokens/s, hit rate and the bytes copied host to
+    device."""
     import torch
     import synth
     from int4_routed_expert_router_amd import api
@@ -232,37 +240,26 @@ def run_pool(args):
     offsets = torch.zeros(L * E, dtype=torch.int64, device="cuda")
     copy_stream = torch.cuda.Stream()
     compute = torch.cuda.current_stream()
-    pool = api.SlotPool(L, E, S, wl.drift_period, stride, stride, host, slab, offsets, copy_stream)
+    pool = api.SlotPool(L, E, S, wl.drift_period, stride, stride, host, slab, offsets, copy_stream,
+                        dma_copy=args.pool_copy == "engine")
     desc = api.Desc(H, E, K, wl.inter, wl.shared_inter, wl.group, wl.act_dtype, 0)
     ws = api.workspace(desc, 1)
     toks = torch.from_numpy(np.stack([synth.tokens(wl, step=s)[0] for s in range(steps)]).view(np.int16)).cuda()
-    x_buf = [torch.empty(1, H, dtype=torch.int16, device="cuda") for _ in range(2)]
-    r = torch.empty(1, H, dtype=torch.float32, device="cuda")
-    y = torch.empty(1, H, dtype=torch.float32, device="cuda")
-    idx = torch.empty(1, K, dtype=torch.int32, device="cuda")
-    w = torch.empty(1, K, dtype=torch.float32, device="cuda")
-    g = torch.empty(1, dtype=torch.float32, device="cuda")
-    idx_host = torch.empty(1, K, dtype=torch.int32, pin_memory=True)
+    x_buf = torch.empty(2, H, dtype=torch.int16, device="cuda")
+    r = torch.empty(H, dtype=torch.float32, device="cuda")
+    idx_host = torch.empty(2, K, dtype=torch.int32, pin_memory=True)
+    pregate = args.pregate
+    layers = [[api.Layer(routers[l], biases[l][ep], slab, stride, offsets, shared[l * sstride:]) for l in range(L)]
+              for ep in range(epochs)]
     torch.cuda.synchronize()
     print(f"[bench] pool80 ready in {time.time() - t0:.1f} s; {steps} steps x {L} layers", file=sys.stderr,
           flush=True)
     t_start = time.perf_counter()
     for s in range(steps):
-        ep = s // wl.drift_period
         x = toks[s:s + 1]
-        r.copy_(x.view(torch.bfloat16).float())
-        for l in range(L):
-            lay = api.Layer(routers[l], biases[l][ep], slab[l * S * stride:], stride, offsets[l * E:],
-                            shared[l * sstride:])
-            api.route(desc, lay, x, idx, w, g, ws=ws)
-            idx_host.copy_(idx)
-            torch.cuda.current_stream().synchronize()
-            pool.acquire(l, idx_host.numpy()[0], s, compute)
-            api.expert_ffn(desc, lay, x, idx, w, g, y, ws=ws)
-            pool.release(l, compute)
-            xn = x_buf[l & 1]
-            api.stack_epilogue(desc, y, r, xn)
-            x = xn
+        r.copy_(x.view(torch.bfloat16).float()[0])
+        api.pool_decode_step(desc, layers[s // wl.drift_period], pool, s, x, r, x_buf, idx_host, ws,
+                             pregate=pregate, stream=compute)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     st = pool.stats()
@@ -271,11 +268,14 @@ def run_pool(args):
            "value": round(steps / elapsed, 2), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
            "ms_per_step": round(1e3 * elapsed / steps, 3), "higher_is_better": True,
            "hit_rate": round(st["hits"] / max(req, 1), 4), "hits": st["hits"], "misses": st["misses"],
-           "evictions": st["evictions"], "bytes_h2d": st["bytes_h2d"],
+           "evictions": st["evictions"], "prefetches": st["prefetches"], "bytes_h2d": st["bytes_h2d"],
            "h2d_GBps": round(st["bytes_h2d"] / elapsed / 1e9, 2),
            "config": {"workload": f"pool80: {L} layers x {E} experts as pinned host blobs of {stride} B, "
                                   f"{S} HBM slots per layer, batch 1, {steps} steps, router bias re-drawn every "
-                                  f"{wl.drift_period} steps, router weights x3"},
+                                  f"{wl.drift_period} steps, router weights x3, "
+                                  + (f"pre-gated prefetch of the top {pregate} predictions of the next layer"
+                                     if pregate else "no prefetch")
+                                  + f", copies by the copy {args.pool_copy}"},
            "data": "synthetic (seeded)"}
     pool.close()
     print(json.dumps(out))

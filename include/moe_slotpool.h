@@ -22,13 +22,24 @@
  *    lowest-numbered free slot, else evicts the unpinned resident expert with
  *    the smallest (count, last_use, expert id); it enters with count 1,
  *    last_use = step, pinned, and its blob is copied into the slot;
- *  - release unpins every slot of the layer.
+ *  - release unpins every slot of the layer;
+ *  - prefetch (pre-gating: experts predicted for a later acquire, e.g. the
+ *    next layer's router applied to the current layer's input) is best
+ *    effort: aging first; requested experts already resident are left as
+ *    they are; each other one, in request order, takes the lowest-numbered
+ *    free slot, else evicts the unpinned resident expert with the smallest
+ *    (count, last_use, expert id) among those this call does not request,
+ *    else is skipped; it enters unpinned with count 0 and last_use = step,
+ *    so the acquire that then hits it leaves the entry a miss would have
+ *    left.
  *
  * Hazards (explicit, as the pages' what-was-built list says theirs are):
  *  - read-after-write: the compute stream waits on an event recorded on
  *    copy_stream after the acquire's copies;
  *  - write-after-read: a copy into a slot of layer l waits on the event that
- *    the last slotpool_release(l) recorded on the compute stream.
+ *    the last slotpool_release(l) recorded on the compute stream;
+ *  - prefetch copies run on copy_stream without making the compute stream
+ *    wait; the next acquire of that layer does (also when it has no miss).
  * One compute stream per pool; a pool is not thread-safe.
  */
 #ifndef MOE_AMD_MOE_SLOTPOOL_H
@@ -59,6 +70,7 @@ typedef struct {
 
 typedef struct {
   uint64_t hits, misses, evictions, bytes_h2d;
+  uint64_t prefetches;   /* experts loaded by slotpool_prefetch */
 } moe_slotpool_stats;
 
 moe_status slotpool_create(const moe_slotpool_config* cfg, moe_slotpool** out);
@@ -72,6 +84,16 @@ moe_status slotpool_create(const moe_slotpool_config* cfg, moe_slotpool** out);
 moe_status slotpool_acquire(moe_slotpool* pool, int32_t layer, const int32_t* experts, int32_t n, uint64_t step,
                             moe_stream compute, int32_t* slot_out, int32_t* victim_out, uint8_t* hit_out);
 
+/* Best-effort early load of experts[0..n) of `layer` (host array, distinct
+ * ids; policy above).  Enqueues their copies on copy_stream and their
+ * device-offset updates on `compute`, which does not wait for the copies.
+ * Optional host outputs, capacity n: *n_loaded_out = number of experts
+ * loaded; expert_out, slot_out, victim_out (evicted expert or -1) describe
+ * them in request order.  Never fails for lack of slots. */
+moe_status slotpool_prefetch(moe_slotpool* pool, int32_t layer, const int32_t* experts, int32_t n, uint64_t step,
+                             moe_stream compute, int32_t* n_loaded_out, int32_t* expert_out, int32_t* slot_out,
+                             int32_t* victim_out);
+
 /* Unpin every slot of `layer` and record its write-after-read event on compute. */
 moe_status slotpool_release(moe_slotpool* pool, int32_t layer, moe_stream compute);
 
@@ -79,6 +101,45 @@ moe_status slotpool_release(moe_slotpool* pool, int32_t layer, moe_stream comput
 moe_status slotpool_evict(moe_slotpool* pool, int32_t layer, int32_t expert);
 
 moe_status slotpool_stats(const moe_slotpool* pool, moe_slotpool_stats* out);
+
+/* The configuration the pool was created with. */
+moe_status slotpool_get_config(const moe_slotpool* pool, moe_slotpool_config* out);
+
+/* One batch-1 decode token through n_layers MoE layers whose routed experts
+ * stream through `pool` (the pages' expert streaming: Show HN page,
+ * how-it-works list), driven natively: for layer l, route x_l; with
+ * pregate > 0, also route x_l with layer l+1's router (pre-gating); copy both
+ * index sets to idx_host and wait for them; slotpool_acquire(l);
+ * slotpool_prefetch(l+1) of the pregate highest-ranked predictions; expert
+ * FFN from the pool's slots; combine with the residual epilogue;
+ * slotpool_release(l).  So the prefetch copies of layer l+1 run while layer
+ * l computes, and no per-layer work waits on an interpreter.
+ *   pregate:  number of predictions to prefetch per layer (0 = none, values
+ *             above top_k mean top_k)
+ *   desc:     layer shape; top_k <= 64
+ *   layers:   [n_layers] weights; router_w, router_bias and shared are used,
+ *             experts / expert_stride / expert_offset are taken from the pool
+ *             (device_slab + l * slots_per_layer * blob_stride, blob_stride,
+ *             device_offsets + l * n_experts)
+ *   step:     the pool's step (one per token)
+ *   x0:       device [H] act_dtype, the token's input
+ *   r:        device [H] fp32 residual, x0 as fp32 on entry, the final
+ *             residual on exit
+ *   x_buf:    device [2][H] act_dtype; layer l's epilogue writes x_{l+1} to
+ *             x_buf[l % 2]
+ *   idx_host: host [2][top_k] int32 staging for the index copies (pinned
+ *             memory keeps the copies asynchronous)
+ *   idx_log:  host [n_layers][2][top_k] int32 or NULL: layer l's selection,
+ *             then the predictions prefetched at layer l for layer l+1 (-1
+ *             where none)
+ *   ws:       workspace of moe_workspace_bytes(desc, 1) bytes
+ * Returns after the last layer is enqueued on `compute` (the copy stream is
+ * the pool's).  The pool must have been created for n_layers layers with
+ * device copies (not MOE_POOL_HOST_ONLY). */
+moe_status moe_pool_decode_step(const moe_layer_desc* desc, const moe_layer_weights* layers, int32_t n_layers,
+                                moe_slotpool* pool, uint64_t step, const void* x0, float* r, void* x_buf,
+                                int32_t* idx_host, int32_t* idx_log, int32_t pregate, void* ws, size_t ws_bytes,
+                                moe_stream compute);
 
 void slotpool_destroy(moe_slotpool* pool);
 

@@ -40,7 +40,8 @@ class SlotPoolConfig(C.Structure):
 
 
 class SlotPoolStats(C.Structure):
-    _fields_ = [("hits", C.c_uint64), ("misses", C.c_uint64), ("evictions", C.c_uint64), ("bytes_h2d", C.c_uint64)]
+    _fields_ = [("hits", C.c_uint64), ("misses", C.c_uint64), ("evictions", C.c_uint64), ("bytes_h2d", C.c_uint64),
+                ("prefetches", C.c_uint64)]
 
 
 class MoeError(RuntimeError):
@@ -75,10 +76,13 @@ PROTOS = {
     "moe_synth_philox": (i32, [vp, vp, vp, i32, vp]),
     "slotpool_create": (i32, [C.POINTER(SlotPoolConfig), C.POINTER(vp)]),
     "slotpool_acquire": (i32, [vp, i32, vp, i32, u64, vp, vp, vp, vp]),
+    "slotpool_prefetch": (i32, [vp, i32, vp, i32, u64, vp, vp, vp, vp, vp]),
     "slotpool_release": (i32, [vp, i32, vp]),
     "slotpool_evict": (i32, [vp, i32, i32]),
     "slotpool_stats": (i32, [vp, C.POINTER(SlotPoolStats)]),
     "slotpool_destroy": (None, [vp]),
+    "slotpool_get_config": (i32, [vp, C.POINTER(SlotPoolConfig)]),
+    "moe_pool_decode_step": (i32, [vp, vp, i32, vp, u64, vp, vp, vp, vp, vp, i32, vp, C.c_size_t, vp]),
 }
 
 

@@ -18,7 +18,7 @@ from ._lib import (MOE_BF16, MOE_F16, MOE_PATH_AUTO, MOE_POOL_DMA_COPY, MOE_POOL
 
 __all__ = ["Desc", "Layer", "blob_bytes", "pack_expert", "workspace_bytes", "workspace", "route", "permute",
            "expert_ffn", "layer_forward", "stack_epilogue", "stack_forward", "StackGraph", "synth_fill_experts",
-           "synth_philox", "SlotPool"]
+           "synth_philox", "SlotPool", "pool_decode_step"]
 
 
 def _ptr(t):
@@ -185,6 +185,21 @@ class StackGraph:
             pass
 
 
+def pool_decode_step(desc, layers, pool, step, x0, r, x_buf, idx_host, ws, pregate=0, idx_log=None,
+                     stream=None):
+    """One batch-1 token through len(layers) layers streamed through `pool`
+    (moe_pool_decode_step): x0 [1, H] or [H] device, r [H] fp32 device,
+    x_buf [2, H] device, idx_host pinned int32 [2, K], pregate = predictions
+    prefetched per layer (0 = none), idx_log optional host int32 numpy array
+    [L, 2, K]."""
+    d = desc.c()
+    arr = _layer_array(layers)
+    log = None if idx_log is None else idx_log.ctypes.data
+    check(lib().moe_pool_decode_step(C.byref(d), arr, len(layers), pool._h, step, _ptr(x0), _ptr(r), _ptr(x_buf),
+                                     _ptr(idx_host), log, int(pregate), _ptr(ws), ws.numel(),
+                                     _stream(stream)))
+
+
 def synth_fill_experts(seed, layer, expert_first, n_experts, hidden, inter, group, scale_lo, scale_hi, dst, stride,
                        stream=None, bits: int = 4):
     """Fill blobs on the GPU with the seeded synthetic weights (see include/moe_synth.h)."""
@@ -223,6 +238,18 @@ class SlotPool:
                                      victim.ctypes.data, hit.ctypes.data))
         return [(int(e), bool(h), int(s), int(v)) for e, h, s, v in zip(ex, hit, slot, victim)]
 
+    def prefetch(self, layer, experts, step, compute_stream=None):
+        """Returns [(expert, slot, victim)] for the experts the call loaded."""
+        ex = np.ascontiguousarray(experts, dtype=np.int32)
+        n = ex.size
+        n_loaded = C.c_int32(0)
+        loaded, slot, victim = (np.zeros(max(n, 1), np.int32) for _ in range(3))
+        cs = None if compute_stream is False else _stream(compute_stream)
+        check(lib().slotpool_prefetch(self._h, layer, ex.ctypes.data, n, step, cs, C.byref(n_loaded),
+                                      loaded.ctypes.data, slot.ctypes.data, victim.ctypes.data))
+        k = n_loaded.value
+        return [(int(e), int(s), int(v)) for e, s, v in zip(loaded[:k], slot[:k], victim[:k])]
+
     def release(self, layer, compute_stream=None):
         cs = None if compute_stream is False else _stream(compute_stream)
         check(lib().slotpool_release(self._h, layer, cs))
@@ -233,7 +260,8 @@ class SlotPool:
     def stats(self):
         s = SlotPoolStats()
         check(lib().slotpool_stats(self._h, C.byref(s)))
-        return dict(hits=s.hits, misses=s.misses, evictions=s.evictions, bytes_h2d=s.bytes_h2d)
+        return dict(hits=s.hits, misses=s.misses, evictions=s.evictions, bytes_h2d=s.bytes_h2d,
+                    prefetches=s.prefetches)
 
     def close(self):
         if self._h:

@@ -8,6 +8,7 @@
 
 #include "moe.h"
 #include "moe_kernels.h"
+#include "moe_slotpool.h"
 
 namespace {
 
@@ -26,6 +27,13 @@ moe_status ok() {
 }
 moe_status hip_fail(hipError_t e, const char* what) {
   return fail(MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+// Prefixes the current message with "<what> <layer>: " (the message is
+// copied first: it lives in the buffer being written).
+moe_status fail_layer(moe_status code, const char* what, int layer) {
+  char msg[sizeof(g_err)];
+  snprintf(msg, sizeof(msg), "%s", g_err);
+  return fail(code, "%s %d: %s", what, layer, msg);
 }
 
 struct KernelTimer {
@@ -87,7 +95,7 @@ moe_status check_weights(const moe_layer_desc* d, const moe_layer_weights* w) {
 size_t al(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct Ws {
-  size_t logits, idx, w, gamma, off, perm, inv, units, nunits, h, hsum, yrow, total;
+  size_t logits, idx, w, gamma, off, perm, inv, units, nunits, h, hsum, yrow, pre, total;
 };
 
 Ws layout(const moe_layer_desc* d, int T) {
@@ -109,6 +117,7 @@ Ws layout(const moe_layer_desc* d, int T) {
   s.h = o; o += al(rows * hstride * 4 * 2 * moe::kGemvSplit);
   s.hsum = o; o += al(rows * (hstride / 16) * 4);
   s.yrow = o; o += al(rows * H * 4);
+  s.pre = o; o += al(T * K * 8 + T * 4);   // pre-gated selection: idx, w, gamma
   s.total = o;
   return s;
 }
@@ -438,7 +447,7 @@ static moe_status stack_enqueue(const moe_layer_desc* d, const moe_layer_weights
   if (!x0 || !aligned(x0, 16) || !r || !x_buf || !aligned(x_buf, 16))
     return fail(MOE_EINVAL, "x0, r and x_buf are required (16-byte aligned)");
   for (int l = 0; l < L_; ++l)
-    if ((st = check_weights(d, &layers[l]))) return fail(st, "layer %d: %s", l, moe_last_error());
+    if ((st = check_weights(d, &layers[l]))) return fail_layer(st, "layer", l);
   Ws L;
   if ((st = check_ws(d, T, ws, ws_bytes, L))) return st;
   const size_t TH = static_cast<size_t>(T) * d->hidden, TK = static_cast<size_t>(T) * d->top_k;
@@ -501,6 +510,80 @@ moe_status moe_stack_graph_create(const moe_layer_desc* d, const moe_layer_weigh
   mg->graph = g;
   mg->exec = ex;
   *out = mg;
+  return ok();
+}
+
+moe_status moe_pool_decode_step(const moe_layer_desc* d, const moe_layer_weights* layers, int32_t L_,
+                                moe_slotpool* pool, uint64_t step, const void* x0, float* r, void* x_buf,
+                                int32_t* idx_host, int32_t* idx_log, int32_t pregate, void* ws, size_t ws_bytes,
+                                moe_stream compute) {
+  moe_status st = check_desc(d);
+  if (st) return st;
+  if (!pool) return fail(MOE_EINVAL, "pool is NULL");
+  if (L_ < 0 || (L_ > 0 && !layers)) return fail(MOE_EINVAL, "bad layer array");
+  if (pregate < 0) return fail(MOE_EINVAL, "pregate=%d < 0", pregate);
+  if (!x0 || !aligned(x0, 16) || !r || !x_buf || !aligned(x_buf, 16) || !idx_host)
+    return fail(MOE_EINVAL, "x0, r, x_buf (16-byte aligned) and idx_host are required");
+  moe_slotpool_config pc{};
+  if ((st = slotpool_get_config(pool, &pc))) return st;
+  if (pc.flags & MOE_POOL_HOST_ONLY) return fail(MOE_EINVAL, "the pool makes no device copies (MOE_POOL_HOST_ONLY)");
+  if (pc.n_layers < L_ || pc.n_experts != d->n_experts)
+    return fail(MOE_ESHAPE, "pool of %d layers x %d experts does not fit %d layers x %d experts", pc.n_layers,
+                pc.n_experts, L_, d->n_experts);
+  if (pc.blob_bytes < blob_size(d->hidden, d->inter, d->group_size, wbits(d)))
+    return fail(MOE_ESHAPE, "pool blobs of %llu bytes are smaller than the layer's", (unsigned long long)pc.blob_bytes);
+  if (L_ == 0) return ok();
+  Ws L;
+  if ((st = check_ws(d, 1, ws, ws_bytes, L))) return st;
+  const int K = d->top_k, H = d->hidden;
+  const uint64_t S = static_cast<uint64_t>(pc.slots_per_layer), E = static_cast<uint64_t>(pc.n_experts);
+  auto pooled = [&](int l) {
+    moe_layer_weights w = layers[l];
+    w.experts = pc.device_slab + static_cast<uint64_t>(l) * S * pc.blob_stride;
+    w.expert_stride = pc.blob_stride;
+    w.expert_offset = pc.device_offsets + static_cast<uint64_t>(l) * E;
+    return w;
+  };
+  for (int l = 0; l < L_; ++l) {
+    moe_layer_weights w = pooled(l);
+    if ((st = check_weights(d, &w))) return fail_layer(st, "layer", l);
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(compute);
+  int32_t* idx = at<int32_t>(ws, L.idx);
+  float* tw = at<float>(ws, L.w);
+  float* gamma = at<float>(ws, L.gamma);
+  int32_t* pidx = at<int32_t>(ws, L.pre);
+  float* pw = at<float>(ws, L.pre + static_cast<size_t>(K) * 4);
+  float* pg = at<float>(ws, L.pre + static_cast<size_t>(K) * 8);
+  const size_t xbytes = static_cast<size_t>(H) * 2;
+  for (int l = 0; l < L_; ++l) {
+    const void* xl = (l == 0) ? x0 : static_cast<const char*>(x_buf) + ((l - 1) & 1) * xbytes;
+    void* xn = static_cast<char*>(x_buf) + (l & 1) * xbytes;
+    const moe_layer_weights w = pooled(l);
+    if ((st = do_route(d, &w, xl, 1, idx, tw, gamma, at<float>(ws, L.logits), nullptr, s))) return st;
+    hipError_t e = hipMemcpyAsync(idx_host, idx, K * 4, hipMemcpyDeviceToHost, s);
+    const bool pre = pregate > 0 && l + 1 < L_;
+    const int n_pre = pregate < K ? pregate : K;   // the highest-ranked predictions
+    if (pre && e == hipSuccess) {
+      const moe_layer_weights wn = pooled(l + 1);
+      if ((st = do_route(d, &wn, xl, 1, pidx, pw, pg, at<float>(ws, L.logits), nullptr, s))) return st;
+      e = hipMemcpyAsync(idx_host + K, pidx, K * 4, hipMemcpyDeviceToHost, s);
+    }
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "index read-back");
+    if (idx_log) {   // [l][0] the selection, [l][1] the prediction for layer l + 1 (-1: none)
+      int32_t* lg = idx_log + static_cast<size_t>(l) * 2 * K;
+      memcpy(lg, idx_host, K * 4);
+      for (int k = 0; k < K; ++k) lg[K + k] = (pre && k < n_pre) ? idx_host[K + k] : -1;
+    }
+    if ((st = slotpool_acquire(pool, l, idx_host, K, step, compute, nullptr, nullptr, nullptr)))
+      return fail_layer(st, "acquire, layer", l);
+    if (pre && (st = slotpool_prefetch(pool, l + 1, idx_host + K, n_pre, step, compute, nullptr, nullptr, nullptr,
+                                       nullptr)))
+      return fail_layer(st, "prefetch, layer", l + 1);
+    if ((st = do_ffn(d, &w, xl, 1, idx, tw, gamma, nullptr, r, xn, ws, L, s))) return st;
+    if ((st = slotpool_release(pool, l, compute))) return fail_layer(st, "release, layer", l);
+  }
   return ok();
 }
 

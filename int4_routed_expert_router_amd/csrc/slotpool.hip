@@ -66,13 +66,17 @@ __global__ __launch_bounds__(256) void k_copy_blobs(const uint8_t* __restrict__ 
 
 }  // namespace
 
+struct moe_slotpool;
+static hipError_t enqueue_loads(moe_slotpool* p, int layer, const std::vector<moe::PoolEvent>& ev, hipStream_t ks);
+
 struct moe_slotpool {
   moe_slotpool_config cfg{};
   moe::PoolCore core;
   std::vector<hipEvent_t> ready, released;  // per layer
   std::vector<uint8_t> released_recorded;
+  std::vector<uint8_t> pending;   // per layer: prefetch copies whose wait no acquire has enqueued yet
   uint64_t bytes_h2d = 0;
-  std::vector<moe::PoolEvent> events;
+  std::vector<moe::PoolEvent> events, loaded;
   const uint8_t* host_dev = nullptr;   // device mapping of host_blobs (copy kernel), or null (copy engine)
   moe_slotpool(const moe_slotpool_config& c)
       : cfg(c), core(c.n_layers, c.n_experts, c.slots_per_layer, c.aging_period) {}
@@ -80,6 +84,58 @@ struct moe_slotpool {
 };
 
 using moe::set_error;
+
+// Copies of the loaded (non-hit) entries of ev into their slots on the copy
+// stream, after the layer's write-after-read event, and their device offset
+// updates on ks; then records the layer's ready event on the copy stream.
+static hipError_t enqueue_loads(moe_slotpool* p, int layer, const std::vector<moe::PoolEvent>& ev, hipStream_t ks) {
+  hipStream_t cs = reinterpret_cast<hipStream_t>(p->cfg.copy_stream);
+  const uint64_t stride = p->cfg.blob_stride;
+  const uint64_t S = static_cast<uint64_t>(p->cfg.slots_per_layer), E = static_cast<uint64_t>(p->cfg.n_experts);
+  hipError_t e = hipSuccess;
+  if (p->released_recorded[layer]) e = hipStreamWaitEvent(cs, p->released[layer], 0);  // WAR
+  uint8_t* slab = p->cfg.device_slab + static_cast<uint64_t>(layer) * S * stride;
+  const uint64_t host_off = static_cast<uint64_t>(layer) * E * stride;
+  const uint8_t* host = p->cfg.host_blobs + host_off;
+  OffsetBatch batch{};
+  CopyBatch copies{};
+  auto flush_copies = [&]() {
+    if (copies.n == 0) return;
+    hipLaunchKernelGGL(k_copy_blobs, dim3(kCopySlices, copies.n), dim3(256), 0, cs, p->host_dev + host_off, slab,
+                       p->cfg.blob_bytes, copies);
+    copies.n = 0;
+    if (e == hipSuccess) e = hipGetLastError();
+  };
+  for (size_t i = 0; i < ev.size() && e == hipSuccess; ++i) {
+    if (ev[i].hit) continue;
+    if (p->host_dev) {
+      copies.src[copies.n] = static_cast<uint64_t>(ev[i].expert) * stride;
+      copies.dst[copies.n] = static_cast<uint64_t>(ev[i].slot) * stride;
+      if (++copies.n == kOffsetBatch) flush_copies();
+    } else {
+      e = hipMemcpyAsync(slab + static_cast<uint64_t>(ev[i].slot) * stride,
+                         host + static_cast<uint64_t>(ev[i].expert) * stride, p->cfg.blob_bytes,
+                         hipMemcpyHostToDevice, cs);
+    }
+    p->bytes_h2d += p->cfg.blob_bytes;
+    batch.expert[batch.n] = ev[i].expert;
+    batch.offset[batch.n] = static_cast<uint64_t>(ev[i].slot) * stride;
+    if (++batch.n == kOffsetBatch) {
+      hipLaunchKernelGGL(k_set_offsets, dim3(1), dim3(kOffsetBatch), 0, ks,
+                         p->cfg.device_offsets + static_cast<uint64_t>(layer) * E, batch);
+      batch.n = 0;
+      if (e == hipSuccess) e = hipGetLastError();
+    }
+  }
+  if (e == hipSuccess) flush_copies();
+  if (e == hipSuccess && batch.n > 0) {
+    hipLaunchKernelGGL(k_set_offsets, dim3(1), dim3(kOffsetBatch), 0, ks,
+                       p->cfg.device_offsets + static_cast<uint64_t>(layer) * E, batch);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) e = hipEventRecord(p->ready[layer], cs);
+  return e;
+}
 
 extern "C" {
 
@@ -107,6 +163,7 @@ moe_status slotpool_create(const moe_slotpool_config* c, moe_slotpool** out) {
     p->ready.assign(c->n_layers, nullptr);
     p->released.assign(c->n_layers, nullptr);
     p->released_recorded.assign(c->n_layers, 0);
+    p->pending.assign(c->n_layers, 0);
     if (!(c->flags & MOE_POOL_DMA_COPY)) {
       void* dev = nullptr;
       if (hipHostGetDevicePointer(&dev, const_cast<uint8_t*>(c->host_blobs), 0) == hipSuccess && dev != nullptr)
@@ -147,55 +204,41 @@ moe_status slotpool_acquire(moe_slotpool* p, int32_t layer, const int32_t* exper
     p->bytes_h2d += static_cast<uint64_t>(n_miss) * p->cfg.blob_bytes;
     return set_error(MOE_OK, "");
   }
-  if (n_miss == 0) return set_error(MOE_OK, "");
-  hipStream_t cs = reinterpret_cast<hipStream_t>(p->cfg.copy_stream);
   hipStream_t ks = reinterpret_cast<hipStream_t>(compute);
-  const uint64_t stride = p->cfg.blob_stride;
-  const uint64_t S = static_cast<uint64_t>(p->cfg.slots_per_layer), E = static_cast<uint64_t>(p->cfg.n_experts);
   hipError_t e = hipSuccess;
-  if (p->released_recorded[layer]) e = hipStreamWaitEvent(cs, p->released[layer], 0);  // WAR
-  uint8_t* slab = p->cfg.device_slab + static_cast<uint64_t>(layer) * S * stride;
-  const uint64_t host_off = static_cast<uint64_t>(layer) * E * stride;
-  const uint8_t* host = p->cfg.host_blobs + host_off;
-  OffsetBatch batch{};
-  CopyBatch copies{};
-  auto flush_copies = [&]() {
-    if (copies.n == 0) return;
-    hipLaunchKernelGGL(k_copy_blobs, dim3(kCopySlices, copies.n), dim3(256), 0, cs, p->host_dev + host_off, slab,
-                       p->cfg.blob_bytes, copies);
-    copies.n = 0;
-    if (e == hipSuccess) e = hipGetLastError();
-  };
-  for (int i = 0; i < n && e == hipSuccess; ++i) {
-    const moe::PoolEvent& ev = p->events[i];
-    if (ev.hit) continue;
-    if (p->host_dev) {
-      copies.src[copies.n] = static_cast<uint64_t>(ev.expert) * stride;
-      copies.dst[copies.n] = static_cast<uint64_t>(ev.slot) * stride;
-      if (++copies.n == kOffsetBatch) flush_copies();
-    } else {
-      e = hipMemcpyAsync(slab + static_cast<uint64_t>(ev.slot) * stride, host + static_cast<uint64_t>(ev.expert) * stride,
-                         p->cfg.blob_bytes, hipMemcpyHostToDevice, cs);
-    }
-    p->bytes_h2d += p->cfg.blob_bytes;
-    batch.expert[batch.n] = ev.expert;
-    batch.offset[batch.n] = static_cast<uint64_t>(ev.slot) * stride;
-    if (++batch.n == kOffsetBatch) {
-      hipLaunchKernelGGL(k_set_offsets, dim3(1), dim3(kOffsetBatch), 0, ks,
-                         p->cfg.device_offsets + static_cast<uint64_t>(layer) * E, batch);
-      batch.n = 0;
-      if (e == hipSuccess) e = hipGetLastError();
-    }
-  }
-  if (e == hipSuccess) flush_copies();
-  if (e == hipSuccess && batch.n > 0) {
-    hipLaunchKernelGGL(k_set_offsets, dim3(1), dim3(kOffsetBatch), 0, ks,
-                       p->cfg.device_offsets + static_cast<uint64_t>(layer) * E, batch);
-    e = hipGetLastError();
-  }
-  if (e == hipSuccess) e = hipEventRecord(p->ready[layer], cs);
-  if (e == hipSuccess) e = hipStreamWaitEvent(ks, p->ready[layer], 0);  // RAW
+  if (n_miss > 0) e = enqueue_loads(p, layer, p->events, ks);
+  // RAW: the compute stream waits for this acquire's copies and for any
+  // earlier prefetch copies of the layer (the copy stream is in order, so
+  // the ready event recorded last covers both)
+  if (e == hipSuccess && (n_miss > 0 || p->pending[layer])) e = hipStreamWaitEvent(ks, p->ready[layer], 0);
   if (e != hipSuccess) return set_error(MOE_EHIP, "slot pool copy/offset enqueue: %s", hipGetErrorString(e));
+  p->pending[layer] = 0;
+  return set_error(MOE_OK, "");
+}
+
+moe_status slotpool_prefetch(moe_slotpool* p, int32_t layer, const int32_t* experts, int32_t n, uint64_t step,
+                             moe_stream compute, int32_t* n_loaded_out, int32_t* expert_out, int32_t* slot_out,
+                             int32_t* victim_out) {
+  if (!p) return set_error(MOE_EINVAL, "pool is NULL");
+  if (layer < 0 || layer >= p->cfg.n_layers) return set_error(MOE_EINVAL, "layer %d out of range", layer);
+  if (n < 0 || (n > 0 && !experts)) return set_error(MOE_EINVAL, "bad expert list");
+  const moe::PoolCore::Result r = p->core.prefetch(layer, experts, n, step, p->loaded);
+  if (r == moe::PoolCore::kBadInput) return set_error(MOE_EINVAL, "expert ids must be distinct and in [0, %d)", p->cfg.n_experts);
+  const int nl = static_cast<int>(p->loaded.size());
+  if (n_loaded_out) *n_loaded_out = nl;
+  for (int i = 0; i < nl; ++i) {
+    if (expert_out) expert_out[i] = p->loaded[i].expert;
+    if (slot_out) slot_out[i] = p->loaded[i].slot;
+    if (victim_out) victim_out[i] = p->loaded[i].victim;
+  }
+  if (p->host_only()) {
+    p->bytes_h2d += static_cast<uint64_t>(nl) * p->cfg.blob_bytes;
+    return set_error(MOE_OK, "");
+  }
+  if (nl == 0) return set_error(MOE_OK, "");
+  const hipError_t e = enqueue_loads(p, layer, p->loaded, reinterpret_cast<hipStream_t>(compute));
+  if (e != hipSuccess) return set_error(MOE_EHIP, "slot pool prefetch enqueue: %s", hipGetErrorString(e));
+  p->pending[layer] = 1;
   return set_error(MOE_OK, "");
 }
 
@@ -219,12 +262,19 @@ moe_status slotpool_evict(moe_slotpool* p, int32_t layer, int32_t expert) {
   return set_error(MOE_OK, "");
 }
 
+moe_status slotpool_get_config(const moe_slotpool* p, moe_slotpool_config* out) {
+  if (!p || !out) return set_error(MOE_EINVAL, "NULL pool or out");
+  *out = p->cfg;
+  return set_error(MOE_OK, "");
+}
+
 moe_status slotpool_stats(const moe_slotpool* p, moe_slotpool_stats* out) {
   if (!p || !out) return set_error(MOE_EINVAL, "NULL pool or out");
   out->hits = p->core.hits();
   out->misses = p->core.misses();
   out->evictions = p->core.evictions();
   out->bytes_h2d = p->bytes_h2d;
+  out->prefetches = p->core.prefetches();
   return set_error(MOE_OK, "");
 }
 

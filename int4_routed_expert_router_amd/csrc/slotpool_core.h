@@ -36,16 +36,7 @@ class PoolCore {
     if (layer < 0 || layer >= L_ || n < 0) return kBadInput;
     int32_t* slot_of = &slot_of_[static_cast<size_t>(layer) * E_];
     const size_t sb = static_cast<size_t>(layer) * S_;
-    // distinct, in range
-    bool bad = false;
-    for (int i = 0; i < n && !bad; ++i) {
-      const int e = experts[i];
-      if (e < 0 || e >= E_ || mark_[e]) bad = true;
-      else mark_[e] = 1;
-    }
-    for (int i = 0; i < n; ++i)
-      if (experts[i] >= 0 && experts[i] < E_) mark_[experts[i]] = 0;
-    if (bad) return kBadInput;
+    if (!distinct_in_range(experts, n)) return kBadInput;
     int misses = 0;
     for (int i = 0; i < n; ++i)
       if (slot_of[experts[i]] < 0) ++misses;
@@ -99,6 +90,44 @@ class PoolCore {
     return kOk;
   }
 
+  // Best-effort early load of predicted experts (see include/moe_slotpool.h):
+  // loaded[k] describes the k-th expert this call brought in (hit = false).
+  Result prefetch(int layer, const int32_t* experts, int n, uint64_t step, std::vector<PoolEvent>& loaded) {
+    loaded.clear();
+    if (layer < 0 || layer >= L_ || n < 0) return kBadInput;
+    if (!distinct_in_range(experts, n)) return kBadInput;
+    int32_t* slot_of = &slot_of_[static_cast<size_t>(layer) * E_];
+    const size_t sb = static_cast<size_t>(layer) * S_;
+    age(layer, step);
+    for (int i = 0; i < n; ++i) {
+      const int e = experts[i];
+      if (slot_of[e] >= 0) continue;
+      int s = -1, victim = -1;
+      for (int k = 0; k < S_; ++k)
+        if (expert_in_[sb + k] < 0) {
+          s = k;
+          break;
+        }
+      if (s < 0) {
+        for (int k = 0; k < S_; ++k) {
+          if (pinned_[sb + k] || requested(expert_in_[sb + k], experts, n)) continue;
+          if (s < 0 || better_victim(sb, k, s)) s = k;
+        }
+        if (s < 0) continue;   // every slot is pinned or holds a requested expert
+        victim = expert_in_[sb + s];
+        slot_of[victim] = -1;
+        ++evictions_;
+      }
+      expert_in_[sb + s] = e;
+      slot_of[e] = s;
+      count_[sb + s] = 0;
+      last_use_[sb + s] = step;
+      loaded.push_back(PoolEvent{e, s, victim, false});
+      ++prefetches_;
+    }
+    return kOk;
+  }
+
   void release(int layer) {
     const size_t sb = static_cast<size_t>(layer) * S_;
     for (int s = 0; s < S_; ++s) pinned_[sb + s] = 0;
@@ -121,11 +150,23 @@ class PoolCore {
   uint64_t hits() const { return hits_; }
   uint64_t misses() const { return misses_; }
   uint64_t evictions() const { return evictions_; }
+  uint64_t prefetches() const { return prefetches_; }
   int layers() const { return L_; }
   int experts() const { return E_; }
   int slots() const { return S_; }
 
  private:
+  bool distinct_in_range(const int32_t* experts, int n) {
+    bool bad = false;
+    for (int i = 0; i < n && !bad; ++i) {
+      const int e = experts[i];
+      if (e < 0 || e >= E_ || mark_[e]) bad = true;
+      else mark_[e] = 1;
+    }
+    for (int i = 0; i < n; ++i)
+      if (experts[i] >= 0 && experts[i] < E_) mark_[experts[i]] = 0;
+    return !bad;
+  }
   static bool requested(int e, const int32_t* experts, int n) {
     for (int i = 0; i < n; ++i)
       if (experts[i] == e) return true;
@@ -154,7 +195,7 @@ class PoolCore {
   std::vector<uint8_t> pinned_;
   std::vector<uint64_t> epoch_;
   std::vector<uint8_t> mark_;
-  uint64_t hits_ = 0, misses_ = 0, evictions_ = 0;
+  uint64_t hits_ = 0, misses_ = 0, evictions_ = 0, prefetches_ = 0;
 };
 
 }  // namespace moe

@@ -162,6 +162,33 @@ def test_pool_core_matches_oracle_simulator(seed, slots, period):
     assert pool.stats() == sim.stats()
 
 
+@pytest.mark.parametrize("seed,slots,period", [(5, 8, 4), (6, 4, 0), (7, 12, 2)])
+def test_pool_prefetch_matches_oracle_simulator(seed, slots, period):
+    # before each acquire, a prefetch of a prediction: the true set with one or
+    # two entries replaced by random experts (as a pre-gated router would err)
+    from int4_routed_expert_router_amd import api
+    layers, experts, k = 3, 24, 4
+    rng = np.random.default_rng(seed + 100)
+    pool = api.SlotPool(layers, experts, slots, period, blob_bytes_=100, host_only=True)
+    sim = PoolSim(layers, experts, slots, period, blob_bytes=100)
+    for s, l, ex in _pool_trace(seed, layers, experts, slots, period, 100, k):
+        if s % 5 != 4:   # some acquires come without a prefetch
+            pred = list(ex)
+            for j in rng.choice(k, size=int(rng.integers(0, 3)), replace=False):
+                c = int(rng.integers(0, experts))
+                if c not in pred:
+                    pred[j] = c
+            assert pool.prefetch(l, pred, s, compute_stream=False) == sim.prefetch(l, pred, s), (s, l, pred)
+        assert pool.acquire(l, ex, s, compute_stream=False) == sim.acquire(l, ex, s), (s, l, ex)
+        if s % 7 == 3:   # a prefetch while the layer is pinned may not take pinned slots
+            other = [int(e) for e in rng.choice(experts, size=3, replace=False)]
+            assert pool.prefetch(l, other, s, compute_stream=False) == sim.prefetch(l, other, s)
+        pool.release(l, compute_stream=False)
+        sim.release(l)
+    assert pool.stats() == sim.stats()
+    assert sim.stats()["prefetches"] > 0
+
+
 def test_pool_error_paths():
     from int4_routed_expert_router_amd import api, MoeError
     pool = api.SlotPool(1, 6, 2, 4, host_only=True)
@@ -173,6 +200,12 @@ def test_pool_error_paths():
         pool.acquire(0, [2], 1, False)
     with pytest.raises(PoolFull):
         sim.acquire(0, [2], 1)
+    # prefetch never fails for lack of slots (both slots are pinned) but rejects bad ids
+    assert pool.prefetch(0, [2, 3], 1, False) == sim.prefetch(0, [2, 3], 1) == []
+    with pytest.raises(MoeError, match="MOE_EINVAL"):
+        pool.prefetch(0, [4, 4], 1, False)
+    with pytest.raises(MoeError, match="MOE_EINVAL"):
+        pool.prefetch(0, [6], 1, False)
     with pytest.raises(MoeError, match="MOE_EINVAL"):
         pool.acquire(0, [3, 3], 1, False)
     with pytest.raises(MoeError, match="MOE_EINVAL"):
