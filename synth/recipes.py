@@ -95,6 +95,26 @@ DEC80I8 = dataclasses.replace(DEC80, name="dec80i8", bits=8, scale_lo=1e-4, scal
 WORKLOADS = {w.name: w for w in (TINY, DEC35, DEC80, BAT80, POOL80, DEC80I8)}
 
 
+@dataclasses.dataclass(frozen=True)
+class GdnWorkload:
+    """Gated DeltaNet decode step beside the MoE block (the pages give no sizes;
+    these follow the public Qwen3-Next-80B configuration: 32 value heads and 16
+    key heads of 128 dims, 36 of the 48 layers)."""
+    name: str
+    batch: int
+    k_heads: int
+    v_heads: int
+    head_k_dim: int
+    head_v_dim: int
+    layers: int
+    act_dtype: str
+    seed: int
+
+
+GDN80 = GdnWorkload("gdn80", 64, 16, 32, 128, 128, 36, "bf16", 201)
+GDN_TINY = GdnWorkload("gdn_tiny", 3, 2, 4, 128, 32, 1, "f16", 202)
+
+
 # ---------------------------------------------------------------------------
 # rounding of generated fp32 draws to the stored 16-bit formats
 # ---------------------------------------------------------------------------
@@ -197,7 +217,7 @@ def random_affine_bias(raw, seed: int, bits: int = 4):
 # router, bias, tokens (host numpy streams)
 # ---------------------------------------------------------------------------
 
-TAG_ROUTER, TAG_BIAS, TAG_TOKENS, TAG_DRIFT = 1, 2, 3, 4
+TAG_ROUTER, TAG_BIAS, TAG_TOKENS, TAG_DRIFT, TAG_GDN, TAG_GDN_STATE = 1, 2, 3, 4, 5, 6
 
 
 def router_weights(wl: Workload, layer: int, seed: int | None = None) -> np.ndarray:
@@ -237,3 +257,31 @@ def tokens(wl: Workload, n_tokens: int | None = None, seed: int | None = None, s
     rng = np.random.default_rng([seed, step, TAG_TOKENS])
     v = rng.standard_normal((n_tokens, wl.hidden), dtype=np.float32)
     return f32_to_f16_bits(v) if wl.act_dtype == "f16" else f32_to_bf16_bits(v)
+
+
+# ---------------------------------------------------------------------------
+# Gated DeltaNet step inputs (host numpy streams)
+# ---------------------------------------------------------------------------
+
+
+def gdn_inputs(wl: GdnWorkload, layer: int, step: int, batch: int | None = None):
+    """One token's q, k [B, Hk, dk] and v [B, Hv, dv] as activation bit patterns
+    (RNE from fp32 N(0,1)), the log-gate g [B, Hv] fp32 with exp(g) ~ U(0.85, 1)
+    and beta [B, Hv] fp32 ~ U(0, 1)."""
+    b = wl.batch if batch is None else batch
+    rng = np.random.default_rng([wl.seed, layer, step, TAG_GDN])
+    to_bits = f32_to_f16_bits if wl.act_dtype == "f16" else f32_to_bf16_bits
+    q = to_bits(rng.standard_normal((b, wl.k_heads, wl.head_k_dim), dtype=np.float32))
+    k = to_bits(rng.standard_normal((b, wl.k_heads, wl.head_k_dim), dtype=np.float32))
+    v = to_bits(rng.standard_normal((b, wl.v_heads, wl.head_v_dim), dtype=np.float32))
+    g = np.log(rng.uniform(0.85, 1.0, (b, wl.v_heads))).astype(np.float32)
+    beta = rng.uniform(0.0, 1.0, (b, wl.v_heads)).astype(np.float32)
+    return q, k, v, g, beta
+
+
+def gdn_state(wl: GdnWorkload, layer: int, batch: int | None = None) -> np.ndarray:
+    """An initial recurrent state [B, Hv, dv, dk] fp32 ~ N(0, 0.05^2)."""
+    b = wl.batch if batch is None else batch
+    rng = np.random.default_rng([wl.seed, layer, TAG_GDN_STATE])
+    shape = (b, wl.v_heads, wl.head_v_dim, wl.head_k_dim)
+    return (rng.standard_normal(shape, dtype=np.float32) * np.float32(0.05)).astype(np.float32)

@@ -109,3 +109,16 @@ def test_tiny_oracle_regression_snapshot():
     assert np.array_equal(out["idx"], ref["idx"])
     for k in ("y", "w", "gamma", "z"):
         assert np.allclose(out[k], ref[k], rtol=1e-13, atol=1e-15)
+
+
+def test_gdn_inputs_shapes_and_ranges():
+    wl = synth.GDN80
+    q, k, v, g, beta = synth.gdn_inputs(wl, 3, 1, batch=4)
+    assert q.shape == k.shape == (4, 16, 128) and v.shape == (4, 32, 128) and q.dtype == np.uint16
+    assert g.shape == beta.shape == (4, 32) and g.dtype == beta.dtype == np.float32
+    assert (g <= 0).all() and (np.exp(g) >= 0.85 - 1e-6).all() and ((beta >= 0) & (beta <= 1)).all()
+    q2 = synth.gdn_inputs(wl, 3, 1, batch=4)[0]
+    assert np.array_equal(q, q2)                          # seeded
+    assert not np.array_equal(q, synth.gdn_inputs(wl, 3, 2, batch=4)[0])
+    st = synth.gdn_state(synth.GDN_TINY, 0)
+    assert st.shape == (3, 4, 32, 128) and st.dtype == np.float32 and 0.04 < st.std() < 0.06
