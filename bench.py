@@ -33,7 +33,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="bat80", choices=["bat80", "dec80", "dec35", "pool80", "dec80i8"])
+    ap.add_argument("--workload", default="bat80", choices=["bat80", "dec80", "dec35", "pool80", "dec80i8", "gdn80"])
     ap.add_argument("--layers", type=int, default=0, help="override the number of layers (0 = workload's)")
     ap.add_argument("--path", type=int, default=0, help="0 auto, 1 GEMV family, 2 grouped family")
     ap.add_argument("--eager", action="store_true", help="launch kernels one by one instead of a HIP graph")
@@ -281,6 +281,94 @@ def run_pool(args):
     print(json.dumps(out))
 
 
+def run_gdn(args):
+    """Gated DeltaNet decode step (gdn80): one token for each of 64 sequences
+    through 36 DeltaNet layers, every layer's [32 heads][128][128] fp32 state
+    per sequence resident in HBM (4.8 GB) and updated in place.  One step =
+    36 launches of moe_gdn_step."""
+    import math
+    import torch
+    import synth
+    from int4_routed_expert_router_amd import api
+    from oracle import deltanet_oracle as dn
+    from oracle import moe_oracle as mo
+    wl = synth.GDN80
+    L = args.layers or wl.layers
+    B, Hk, Hv, dk, dv = wl.batch, wl.k_heads, wl.v_heads, wl.head_k_dim, wl.head_v_dim
+    qs = 1.0 / math.sqrt(dk)
+    print(f"[bench] gdn80: {L} layers x {B} sequences, state {L * B * Hv * dv * dk * 4 / 1e9:.2f} GB",
+          file=sys.stderr, flush=True)
+    states, ins = [], []
+    for l in range(L):
+        states.append(torch.from_numpy(synth.gdn_state(wl, l)).cuda())
+        q, k, v, g, beta = synth.gdn_inputs(wl, l, 0)
+        ins.append([torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda()
+                    for a in (q, k, v, g, beta)])
+    o = torch.empty(B, Hv, dv, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.Stream()
+
+    def step():
+        for l in range(L):
+            q, k, v, g, beta = ins[l]
+            api.gdn_step(q, k, v, g, beta, states[l], o, qs, wl.act_dtype, stream=stream)
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        # HIP events on the launch stream around every layer's launch
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
+        durs = []
+        for _ in range(max(3, min(args.steps, 10))):
+            for l in range(L):
+                q, k, v, g, beta = ins[l]
+                ev[l][0].record(stream)
+                api.gdn_step(q, k, v, g, beta, states[l], o, qs, wl.act_dtype, stream=stream)
+                ev[l][1].record(stream)
+            torch.cuda.synchronize()
+            durs += [ev[l][0].elapsed_time(ev[l][1]) for l in range(L)]
+    avg_us = float(np.mean(durs)) * 1e3
+    state_b = B * Hv * dv * dk * 4
+    per_launch = 2 * state_b + 2 * B * Hk * dk * 2 + B * Hv * dv * 2 + B * Hv * 8 + B * Hv * dv * 4
+    achieved = per_launch / (avg_us * 1e-6) / 1e9
+    ms = 1e3 * elapsed / args.steps
+    print(f"[bench] {ms:.3f} ms/step, {B * args.steps / elapsed:.0f} tok/s, launch {avg_us:.2f} us, "
+          f"{achieved:.0f} GB/s", file=sys.stderr, flush=True)
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the oracle on whole layers (all 64 sequences), as many as fit the budget
+        q, k, v, g, beta = synth.gdn_inputs(wl, 0, 0)
+        host = [mo.act_bits_to_f64(a, wl.act_dtype) for a in (q, k, v)] + [g.astype(np.float64), beta.astype(np.float64)]
+        st = synth.gdn_state(wl, 0).astype(np.float64)
+        t0 = time.perf_counter()
+        done = 0
+        while True:
+            st, _ = dn.gdn_step(st, *host, qs)
+            done += 1
+            el = time.perf_counter() - t0
+            if el >= min(args.cpu_seconds, 10.0) or done >= L:
+                break
+        cpu = dict(value=round(B / (el / done * L), 2), unit="tokens/s", cores=len(os.sched_getaffinity(0)),
+                   kind="oracle", sample=f"{done} layer step(s) x {B} sequences in {el:.1f} s, scaled to {L} layers")
+    out = {"metric": "Gated DeltaNet decode step tokens/sec + state HBM GB/s (80B-shaped, 64 sequences)",
+           "value": round(B * args.steps / elapsed, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded)",
+           "config": {"workload": f"gdn80: {L} Gated DeltaNet layers, {B} sequences, {Hv} value / {Hk} key heads, "
+                                  f"head dims {dk}, state fp32 in place, {wl.act_dtype} q/k/v"},
+           "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "k_gdn_step",
+                        "avg_us": round(avg_us, 2), "bytes_per_launch": int(per_launch),
+                        "events": "HIP events on the launch stream around each layer's launch"},
+           "cpu_baseline": cpu}
+    print(json.dumps(out))
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -292,6 +380,9 @@ def main():
         sys.exit(2)
     if args.workload == "pool80":
         run_pool(args)
+        return
+    if args.workload == "gdn80":
+        run_gdn(args)
         return
     import torch
     import synth

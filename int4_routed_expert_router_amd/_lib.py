@@ -32,6 +32,11 @@ class LayerWeights(C.Structure):
                 ("expert_stride", C.c_uint64), ("expert_offset", C.c_void_p), ("shared", C.c_void_p)]
 
 
+class GdnDesc(C.Structure):
+    _fields_ = [("batch", C.c_int32), ("k_heads", C.c_int32), ("v_heads", C.c_int32), ("head_k_dim", C.c_int32),
+                ("head_v_dim", C.c_int32), ("act_dtype", C.c_int32)]
+
+
 class SlotPoolConfig(C.Structure):
     _fields_ = [("n_layers", C.c_int32), ("n_experts", C.c_int32), ("slots_per_layer", C.c_int32),
                 ("aging_period", C.c_int32), ("blob_stride", C.c_uint64), ("blob_bytes", C.c_uint64),
@@ -74,6 +79,7 @@ PROTOS = {
     "moe_graph_destroy": (None, [vp]),
     "moe_synth_fill_experts": (i32, [u64, i32, i32, i32, i32, i32, i32, i32, f32, f32, vp, u64, vp]),
     "moe_synth_philox": (i32, [vp, vp, vp, i32, vp]),
+    "moe_gdn_step": (i32, [C.POINTER(GdnDesc), vp, vp, vp, vp, vp, f32, vp, vp, vp]),
     "slotpool_create": (i32, [C.POINTER(SlotPoolConfig), C.POINTER(vp)]),
     "slotpool_acquire": (i32, [vp, i32, vp, i32, u64, vp, vp, vp, vp]),
     "slotpool_prefetch": (i32, [vp, i32, vp, i32, u64, vp, vp, vp, vp, vp]),

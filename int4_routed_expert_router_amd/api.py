@@ -13,12 +13,12 @@ import dataclasses
 import numpy as np
 import torch
 
-from ._lib import (MOE_BF16, MOE_F16, MOE_PATH_AUTO, MOE_POOL_DMA_COPY, MOE_POOL_HOST_ONLY, LayerDesc,  # noqa: F401
+from ._lib import (GdnDesc, MOE_BF16, MOE_F16, MOE_PATH_AUTO, MOE_POOL_DMA_COPY, MOE_POOL_HOST_ONLY, LayerDesc,  # noqa: F401
                    LayerWeights, SlotPoolConfig, SlotPoolStats, check, lib)
 
 __all__ = ["Desc", "Layer", "blob_bytes", "pack_expert", "workspace_bytes", "workspace", "route", "permute",
            "expert_ffn", "layer_forward", "stack_epilogue", "stack_forward", "StackGraph", "synth_fill_experts",
-           "synth_philox", "SlotPool", "pool_decode_step"]
+           "synth_philox", "SlotPool", "pool_decode_step", "gdn_step"]
 
 
 def _ptr(t):
@@ -198,6 +198,17 @@ def pool_decode_step(desc, layers, pool, step, x0, r, x_buf, idx_host, ws, prega
     check(lib().moe_pool_decode_step(C.byref(d), arr, len(layers), pool._h, step, _ptr(x0), _ptr(r), _ptr(x_buf),
                                      _ptr(idx_host), log, int(pregate), _ptr(ws), ws.numel(),
                                      _stream(stream)))
+
+
+def gdn_step(q, k, v, g, beta, state, o, q_scale, act_dtype="bf16", stream=None):
+    """One Gated DeltaNet token (moe_gdn_step): q, k [B, Hk, 128] and v [B, Hv, dv]
+    16-bit tensors, g, beta [B, Hv] fp32, state [B, Hv, dv, 128] fp32 (in place),
+    o [B, Hv, dv] fp32."""
+    B, Hk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    d = GdnDesc(B, Hk, Hv, dk, dv, {"bf16": MOE_BF16, "f16": MOE_F16}.get(act_dtype, 0))
+    check(lib().moe_gdn_step(C.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(q_scale), _ptr(state),
+                             _ptr(o), _stream(stream)))
 
 
 def synth_fill_experts(seed, layer, expert_first, n_experts, hidden, inter, group, scale_lo, scale_hi, dst, stride,

@@ -218,3 +218,22 @@ def test_pool_error_paths():
         api.SlotPool(1, 4, 5, 4, host_only=True)
     with pytest.raises(MoeError, match="MOE_EINVAL"):
         api.SlotPool(1, 8, 4, 4)               # device pool without buffers
+
+
+def test_gdn_validation_before_any_gpu_work():
+    import ctypes as C
+    from int4_routed_expert_router_amd._lib import GdnDesc, lib, MOE_BF16
+    L = lib()
+    bad = [GdnDesc(4, 16, 32, 64, 128, MOE_BF16), GdnDesc(4, 16, 32, 128, 24, MOE_BF16),
+           GdnDesc(4, 16, 24, 128, 128, MOE_BF16), GdnDesc(4, 16, 32, 128, 272, MOE_BF16),
+           GdnDesc(-1, 16, 32, 128, 128, MOE_BF16), GdnDesc(70000, 16, 32, 128, 128, MOE_BF16)]
+    for d in bad:
+        assert L.moe_gdn_step(C.byref(d), None, None, None, None, None, 1.0, None, None, None) == -2
+    d = GdnDesc(4, 16, 32, 128, 128, 7)
+    assert L.moe_gdn_step(C.byref(d), None, None, None, None, None, 1.0, None, None, None) == -1
+    d = GdnDesc(0, 16, 32, 128, 128, MOE_BF16)     # empty batch: no-op, no buffers needed
+    assert L.moe_gdn_step(C.byref(d), None, None, None, None, None, 1.0, None, None, None) == 0
+    d = GdnDesc(2, 16, 32, 128, 128, MOE_BF16)
+    assert L.moe_gdn_step(C.byref(d), None, None, None, None, None, 1.0, None, None, None) == -1
+    st = L.moe_gdn_step(C.byref(d), 4096, 4096, 4096, 4096, 4096, 1.0, 4100, 4096, None)
+    assert st == -1 and b"aligned" in L.moe_last_error()
