@@ -52,6 +52,8 @@ def parse():
 COPY_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gateup_bat80.txt")
 GROUPED_SRC = os.path.join(ROOT, "int4_routed_expert_router_amd", "csrc", "moe_ffn_grouped.hip")
+GDN_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gdn_step_gdn80.txt")
+GDN_SRC = os.path.join(ROOT, "int4_routed_expert_router_amd", "csrc", "gdn.hip")
 
 
 def copy_calibration():
@@ -68,12 +70,12 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_per_dispatch": COPY_BYTES, "dispatches": 3}))
 
 
-def measured_traffic():
-    """HBM bytes per gate/up launch from the committed counter summary, or
+def measured_traffic(path=TRAFFIC_FILE, src=GROUPED_SRC):
+    """HBM bytes per launch of a kernel from its committed counter summary, or
     None when the kernel source changed since the counters were taken."""
     import hashlib
     try:
-        text = open(TRAFFIC_FILE).read()
+        text = open(path).read()
     except OSError:
         return None
     vals = {}
@@ -81,7 +83,7 @@ def measured_traffic():
         if line.startswith("- ") and ":" in line:
             k, v = line[2:].split(":", 1)
             vals[k.strip()] = v.strip().strip("`")
-    src_hash = hashlib.sha256(open(GROUPED_SRC, "rb").read()).hexdigest()
+    src_hash = hashlib.sha256(open(src, "rb").read()).hexdigest()
     if vals.get("kernel_source_sha256") != src_hash:
         return None
     try:
@@ -333,6 +335,7 @@ def run_gdn(args):
             torch.cuda.synchronize()
             durs += [ev[l][0].elapsed_time(ev[l][1]) for l in range(L)]
     avg_us = float(np.mean(durs)) * 1e3
+    tb = measured_traffic(GDN_TRAFFIC_FILE, GDN_SRC)
     state_b = B * Hv * dv * dk * 4
     per_launch = 2 * state_b + 2 * B * Hk * dk * 2 + B * Hv * dv * 2 + B * Hv * 8 + B * Hv * dv * 4
     achieved = per_launch / (avg_us * 1e-6) / 1e9
@@ -362,8 +365,10 @@ def run_gdn(args):
            "config": {"workload": f"gdn80: {L} Gated DeltaNet layers, {B} sequences, {Hv} value / {Hk} key heads, "
                                   f"head dims {dk}, state fp32 in place, {wl.act_dtype} q/k/v"},
            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "k_gdn_step",
-                        "avg_us": round(avg_us, 2), "bytes_per_launch": int(per_launch),
+                        "frac": round(achieved / HBM_PEAK_GBS, 4),
+                        "traffic": None if tb is None else round(tb / (avg_us * 1e-6) / 1e9, 1),
+                        "kernel": "k_gdn_step", "avg_us": round(avg_us, 2), "bytes_per_launch": int(per_launch),
+                        "traffic_bytes_per_launch": None if tb is None else int(tb),
                         "events": "HIP events on the launch stream around each layer's launch"},
            "cpu_baseline": cpu}
     print(json.dumps(out))

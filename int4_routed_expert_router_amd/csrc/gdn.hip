@@ -7,20 +7,18 @@
 #include "moe_gdn.h"
 
 namespace moe {
+// moe_api.cpp owns the thread-local error string; this file reports through it.
 moe_status set_error(moe_status code, const char* fmt, ...);
-}  // namespace moe
 
 namespace {
-
-using moe::act_to_f32;
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+}  // namespace
 
 constexpr int kDK = 128;
 constexpr int kRowsPerPass = 16;   // 256 threads, one row of 16 lanes per state row
 constexpr int kPassBatch = 8;      // passes whose state loads a thread issues together
 
-__device__ __forceinline__ float row_sum(float x) {
-  return __uint_as_float(moe::dpp_row_sum(__float_as_uint(x)));
-}
+__device__ __forceinline__ float row_sum(float x) { return __uint_as_float(dpp_row_sum(__float_as_uint(x))); }
 
 // One workgroup per (sequence, value head).  A row of 16 lanes owns one state
 // row per pass; lane l16 of it holds columns 4 l16 .. 4 l16 + 3 and
@@ -118,13 +116,14 @@ __global__ __launch_bounds__(256) void k_gdn_step(const uint16_t* __restrict__ q
   }
 }
 
-bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
-
-}  // namespace
+}  // namespace moe
 
 extern "C" moe_status moe_gdn_step(const moe_gdn_desc* d, const void* q, const void* k, const void* v,
                                    const float* g, const float* beta, float q_scale, float* state, float* o,
                                    moe_stream stream) {
+  using moe::aligned;
+  using moe::kDK;
+  using moe::kRowsPerPass;
   using moe::set_error;
   if (!d) return set_error(MOE_EINVAL, "desc is NULL");
   if (d->batch < 0 || d->batch > 65535) return set_error(MOE_ESHAPE, "batch=%d must be in [0, 65535]", d->batch);
@@ -145,10 +144,10 @@ extern "C" moe_status moe_gdn_step(const moe_gdn_desc* d, const void* q, const v
   const auto* kb = static_cast<const uint16_t*>(k);
   const auto* vb = static_cast<const uint16_t*>(v);
   if (d->act_dtype == MOE_BF16)
-    hipLaunchKernelGGL(k_gdn_step<2>, grid, dim3(256), 0, s, qb, kb, vb, g, beta, q_scale, state, o, d->k_heads,
+    hipLaunchKernelGGL(moe::k_gdn_step<2>, grid, dim3(256), 0, s, qb, kb, vb, g, beta, q_scale, state, o, d->k_heads,
                        d->v_heads, d->head_v_dim);
   else
-    hipLaunchKernelGGL(k_gdn_step<1>, grid, dim3(256), 0, s, qb, kb, vb, g, beta, q_scale, state, o, d->k_heads,
+    hipLaunchKernelGGL(moe::k_gdn_step<1>, grid, dim3(256), 0, s, qb, kb, vb, g, beta, q_scale, state, o, d->k_heads,
                        d->v_heads, d->head_v_dim);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(MOE_EHIP, "Gated DeltaNet kernel launch: %s", hipGetErrorString(e));

@@ -5,7 +5,8 @@
 #include "moe.h"
 #include "moe_synth.h"
 
-namespace {
+namespace moe {
+namespace synth {
 
 // Philox4x32-10 (Salmon et al., SC'11, section 3.2): multipliers and Weyl key
 // increments of the 4x32 variant, ten rounds.
@@ -150,8 +151,11 @@ __global__ void k_philox(const uint32_t* ctr, const uint32_t* key, uint32_t* out
   for (int k = 0; k < 4; ++k) out[4 * i + k] = r.v[k];
 }
 
-thread_local char g_err[256] = "";
+}  // namespace synth
+}  // namespace moe
 
+namespace {
+thread_local char g_err[256] = "";
 }  // namespace
 
 extern "C" moe_status moe_synth_fill_experts(uint64_t seed, int32_t layer, int32_t expert_first, int32_t n_experts,
@@ -166,10 +170,10 @@ extern "C" moe_status moe_synth_fill_experts(uint64_t seed, int32_t layer, int32
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const uint32_t k0 = static_cast<uint32_t>(seed & 0xFFFFFFFFu), ly = static_cast<uint32_t>(layer);
   if (bits == 8)
-    hipLaunchKernelGGL(k_fill<8>, dim3(gx, n_experts), dim3(256), 0, s, k0, ly, expert_first, H, I, G, lo, span, dst,
+    hipLaunchKernelGGL(moe::synth::k_fill<8>, dim3(gx, n_experts), dim3(256), 0, s, k0, ly, expert_first, H, I, G, lo, span, dst,
                        stride);
   else
-    hipLaunchKernelGGL(k_fill<4>, dim3(gx, n_experts), dim3(256), 0, s, k0, ly, expert_first, H, I, G, lo, span, dst,
+    hipLaunchKernelGGL(moe::synth::k_fill<4>, dim3(gx, n_experts), dim3(256), 0, s, k0, ly, expert_first, H, I, G, lo, span, dst,
                        stride);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
@@ -179,7 +183,7 @@ extern "C" moe_status moe_synth_philox(const uint32_t* ctr, const uint32_t* key,
   if (n < 0) return MOE_ESHAPE;
   if (n == 0) return MOE_OK;
   if (!ctr || !key || !out) return MOE_EINVAL;
-  hipLaunchKernelGGL(k_philox, dim3((n + 255) / 256), dim3(256), 0, reinterpret_cast<hipStream_t>(stream), ctr, key,
+  hipLaunchKernelGGL(moe::synth::k_philox, dim3((n + 255) / 256), dim3(256), 0, reinterpret_cast<hipStream_t>(stream), ctr, key,
                      out, n);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
