@@ -65,11 +65,12 @@ def test_tiny_chained_steps():
     _check(synth.GDN_TINY, steps=4)
 
 
-@pytest.mark.parametrize("dv,hk,hv,act", [(16, 1, 1, "bf16"), (256, 2, 6, "f16"), (48, 3, 3, "bf16")],
-                         ids=["dv16_one_head", "dv256_two_batches", "dv48_group1"])
-def test_shape_edges(dv, hk, hv, act):
+@pytest.mark.parametrize("dv,hk,hv,act,b", [(16, 1, 1, "bf16", 2), (256, 2, 6, "f16", 2), (48, 3, 3, "bf16", 2),
+                                            (128, 16, 32, "bf16", 1)],
+                         ids=["dv16_one_head", "dv256_two_batches", "dv48_group1", "decode_batch1"])
+def test_shape_edges(dv, hk, hv, act, b):
     wl = dataclasses.replace(synth.GDN_TINY, name=f"gdn_dv{dv}", head_v_dim=dv, k_heads=hk, v_heads=hv,
-                             act_dtype=act, batch=2, seed=203 + dv)
+                             act_dtype=act, batch=b, seed=203 + dv)
     _check(wl, steps=2)
 
 

@@ -190,3 +190,23 @@ def test_native_pool_decode_equals_resident_stack(pregate):
     assert pool.stats() == sim.stats()
     assert (pool.stats()["prefetches"] > 0) == (pregate > 0)
     pool.close()
+
+
+def test_native_pool_decode_rejects_a_pool_of_other_geometry():
+    import torch
+    from int4_routed_expert_router_amd import api, MoeError
+    wl = POOLED4
+    dl = DeviceLayer(wl, 0, use_gpu_fill=False)
+    stride = dl.stride
+    host = torch.empty(8 * stride, dtype=torch.uint8, pin_memory=True)
+    slab = torch.zeros(4 * stride, dtype=torch.uint8, device="cuda")
+    offsets = torch.zeros(8, dtype=torch.int64, device="cuda")
+    pool = api.SlotPool(1, 8, 4, 0, stride, stride, host, slab, offsets, torch.cuda.Stream())   # 8 experts, not 16
+    desc = desc_for(wl, path=1)
+    x = torch.zeros(1, wl.hidden, dtype=torch.int16, device="cuda")
+    r = torch.zeros(wl.hidden, dtype=torch.float32, device="cuda")
+    xb = torch.empty(2, wl.hidden, dtype=torch.int16, device="cuda")
+    idx_host = torch.empty(2, wl.top_k, dtype=torch.int32, pin_memory=True)
+    with pytest.raises(MoeError, match="MOE_ESHAPE"):
+        api.pool_decode_step(desc, [dl.api_layer()], pool, 0, x, r, xb, idx_host, api.workspace(desc, 1))
+    pool.close()

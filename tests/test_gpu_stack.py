@@ -106,10 +106,10 @@ def test_stack_teacher_forced_parity(path, n_tokens, wl):
     assert_close(got["r"], r, "final residual")
 
 
-def test_graph_replay_matches_eager_bitwise():
+@pytest.mark.parametrize("wl", [STACK, STACK8], ids=["int4_grouped", "int8_gemv"])
+def test_graph_replay_matches_eager_bitwise(wl):
     import torch
     from int4_routed_expert_router_amd import api
-    wl = STACK
     st = Stack(wl, 40, 0)
     st.run_eager()
     want = st.snapshot()

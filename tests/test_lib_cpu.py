@@ -237,3 +237,22 @@ def test_gdn_validation_before_any_gpu_work():
     assert L.moe_gdn_step(C.byref(d), None, None, None, None, None, 1.0, None, None, None) == -1
     st = L.moe_gdn_step(C.byref(d), 4096, 4096, 4096, 4096, 4096, 1.0, 4100, 4096, None)
     assert st == -1 and b"aligned" in L.moe_last_error()
+
+
+def test_pool_decode_validation_before_any_gpu_work():
+    import ctypes as C
+    from int4_routed_expert_router_amd import api
+    from int4_routed_expert_router_amd._lib import lib
+    L = lib()
+    d = api.Desc(256, 16, 2, 64, 64, 32, "f16").c()
+    arr = api._layer_array([api.Layer(4096, None, 4096, 30720, None, 4096)])
+    host = np.zeros((2, 2), np.int32)
+    args = (C.byref(d), arr, 1)
+    tail = (0, 4096, 4096, 4096, host.ctypes.data, None, 0, 4096, 1 << 20, None)
+    assert L.moe_pool_decode_step(*args, None, *tail) == -1 and b"pool" in L.moe_last_error()
+    pool = api.SlotPool(1, 16, 4, 0, host_only=True)
+    assert L.moe_pool_decode_step(*args, pool._h, *tail) == -1 and b"HOST_ONLY" in L.moe_last_error()
+    st = L.moe_pool_decode_step(*args, pool._h, 0, 4096, 4096, 4096, host.ctypes.data, None, -1, 4096, 1 << 20,
+                                None)
+    assert st == -1 and b"pregate" in L.moe_last_error()
+    pool.close()
