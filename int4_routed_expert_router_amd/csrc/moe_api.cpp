@@ -143,24 +143,45 @@ bool use_grouped(const moe_layer_desc* d, int T) {
   return static_cast<long long>(T) * d->top_k > MOE_GEMV_MAX_ROWS && grouped_fits(d);
 }
 
-moe_status do_route(const moe_layer_desc* d, const moe_layer_weights* w, const void* x, int T, int32_t* idx,
-                    float* tw, float* gamma, float* part, float* logits_out, hipStream_t s, int layer = -1) {
+// The router kernel alone: its logit slices go to part.
+moe_status do_router(const moe_layer_desc* d, const moe_layer_weights* w, const void* x, int T, float* part,
+                     hipStream_t s, int layer, moe::RouterParts* rp) {
   hipError_t e = timer_mark(true, MOE_TIME_ROUTER, layer, s);
-  moe::RouterParts rp{1, true};
+  *rp = moe::RouterParts{1, true};
   if (e == hipSuccess)
     e = moe::launch_router_logits(d->act_dtype, static_cast<const uint16_t*>(x), w->router_w, w->router_bias, part, T,
-                                  d->hidden, d->n_experts, s, &rp);
+                                  d->hidden, d->n_experts, s, rp);
   if (e == hipSuccess) e = timer_mark(false, MOE_TIME_ROUTER, layer, s);
   if (e != hipSuccess) return hip_fail(e, "router kernel launch");
-  e = moe::launch_topk(part, rp.n_part, rp.biased ? nullptr : w->router_bias, T, d->n_experts, d->top_k, idx, tw,
-                       gamma, logits_out, s);
+  return MOE_OK;
+}
+
+moe_status do_route(const moe_layer_desc* d, const moe_layer_weights* w, const void* x, int T, int32_t* idx,
+                    float* tw, float* gamma, float* part, float* logits_out, hipStream_t s, int layer = -1) {
+  moe::RouterParts rp{};
+  moe_status st = do_router(d, w, x, T, part, s, layer, &rp);
+  if (st) return st;
+  hipError_t e = moe::launch_topk(part, rp.n_part, rp.biased ? nullptr : w->router_bias, T, d->n_experts, d->top_k,
+                                  idx, tw, gamma, logits_out, s);
   if (e != hipSuccess) return hip_fail(e, "top-k kernel launch");
   return MOE_OK;
 }
 
+// Top-K fused into the batch-1 gate/up GEMV: the router's slices and the
+// buffers the selection is written to.
+struct FusedTopk {
+  const float* part;
+  moe::RouterParts rp;
+  int32_t* idx;
+  float* w;
+  float* gamma;
+};
+
+bool fuse_topk(const moe_layer_desc* d, int T) { return !use_grouped(d, T) && d->n_experts <= 512; }
+
 moe_status do_ffn(const moe_layer_desc* d, const moe_layer_weights* w, const void* x, int T, const int32_t* idx,
                   const float* tw, const float* gamma, float* y, float* r, void* x_next, void* ws, const Ws& L,
-                  hipStream_t s, int layer = -1) {
+                  hipStream_t s, int layer = -1, const FusedTopk* fz = nullptr) {
   moe::FfnArgs a{};
   a.x = static_cast<const uint16_t*>(x);
   a.topk_idx = idx;
@@ -179,6 +200,14 @@ moe_status do_ffn(const moe_layer_desc* d, const moe_layer_weights* w, const voi
   a.E = d->n_experts;
   a.hstride = d->inter > d->shared_inter ? d->inter : d->shared_inter;
   a.bits = wbits(d);
+  if (fz != nullptr) {
+    a.route_part = fz->part;
+    a.route_bias = fz->rp.biased ? nullptr : w->router_bias;
+    a.route_nparts = fz->rp.n_part;
+    a.sel_idx = fz->idx;
+    a.sel_w = fz->w;
+    a.sel_gamma = fz->gamma;
+  }
   const int32_t* inv = nullptr;
   hipError_t e;
   if (use_grouped(d, T)) {
@@ -418,6 +447,12 @@ moe_status moe_layer_forward(const moe_layer_desc* d, const moe_layer_weights* w
   int32_t* idx = idx_out ? idx_out : at<int32_t>(ws, L.idx);
   float* tw = w_out ? w_out : at<float>(ws, L.w);
   float* gamma = gamma_out ? gamma_out : at<float>(ws, L.gamma);
+  if (fuse_topk(d, T)) {
+    FusedTopk fz{at<float>(ws, L.logits), {}, idx, tw, gamma};
+    if ((st = do_router(d, w, x, T, at<float>(ws, L.logits), s, -1, &fz.rp))) return st;
+    if ((st = do_ffn(d, w, x, T, idx, tw, gamma, y, nullptr, nullptr, ws, L, s, -1, &fz))) return st;
+    return ok();
+  }
   if ((st = do_route(d, w, x, T, idx, tw, gamma, at<float>(ws, L.logits), nullptr, s))) return st;
   if ((st = do_ffn(d, w, x, T, idx, tw, gamma, y, nullptr, nullptr, ws, L, s))) return st;
   return ok();
@@ -461,6 +496,12 @@ static moe_status stack_enqueue(const moe_layer_desc* d, const moe_layer_weights
     float* tw = w_all ? w_all + l * TK : at<float>(ws, L.w);
     float* gamma = gamma_all ? gamma_all + static_cast<size_t>(l) * T : at<float>(ws, L.gamma);
     float* y = y_all ? y_all + l * TH : nullptr;
+    if (fuse_topk(d, T)) {
+      FusedTopk fz{at<float>(ws, L.logits), {}, idx, tw, gamma};
+      if ((st = do_router(d, &layers[l], xl, T, at<float>(ws, L.logits), s, l, &fz.rp))) return st;
+      if ((st = do_ffn(d, &layers[l], xl, T, idx, tw, gamma, y, r, x_buf, ws, L, s, l, &fz))) return st;
+      continue;
+    }
     if ((st = do_route(d, &layers[l], xl, T, idx, tw, gamma, at<float>(ws, L.logits), nullptr, s, l))) return st;
     if ((st = do_ffn(d, &layers[l], xl, T, idx, tw, gamma, y, r, x_buf, ws, L, s, l))) return st;
   }

@@ -14,6 +14,7 @@
 // one FMA per (row, group) with the group sum of x computed once per row.
 #include "moe_common.h"
 #include "moe_kernels.h"
+#include "moe_topk.h"
 
 namespace moe {
 
@@ -68,7 +69,13 @@ constexpr int kGemvGateUpWaves = 8;
 // activations are staged: they do not depend on them.  int4 products run as
 // packed 16-bit dot products of re-based nibbles with the raw activations;
 // int8 bytes multiply activations staged as fp32.
-template <int ACT, int BITS>
+//
+// KJ > 0 (batch-1 decode): top-K runs here instead of in its own kernel.
+// Wave 0 of a routed row's workgroup selects the token's K experts from the
+// router's logit slices (KJ logits per lane, the top-K kernel's code) and
+// passes its rank's expert through LDS; the other rows skip it.  The weight
+// loads then follow as usual.
+template <int ACT, int BITS, int KJ>
 __global__ __launch_bounds__(64 * kGemvGateUpWaves) void k_gateup_gemv(FfnArgs a) {
   constexpr int NW = kGemvGateUpWaves;
   constexpr int NQ = BITS / 4;   // 16-byte loads per lane and chunk
@@ -80,8 +87,34 @@ __global__ __launch_bounds__(64 * kGemvGateUpWaves) void k_gateup_gemv(FfnArgs a
   const uint8_t* blob;
   int t, inter;
   const int j = blockIdx.x;
-  row_source(a, j, blob, t, inter);
   const int p = blockIdx.y, z = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if constexpr (KJ > 0) {
+    __shared__ int32_t ssel[kMaxTopK];
+    if (j < a.T * a.K) {   // uniform: a routed row
+      if (p * 16 >= a.I) return;
+      t = j / a.K;
+      const int k = j - t * a.K;
+      if (wave == 0) {
+        TopkIn<KJ> in;
+        topk_issue(a.route_part, a.route_nparts, a.T, a.E, t, lane, in);
+        float bj[KJ];
+        load_bias(a.route_bias, a.E, lane, bj);
+        const bool writer = p == 0 && z == 0 && k == 0;
+        topk_finish(in, bj, a.route_bias != nullptr, a.route_nparts, a.E, a.K, t, lane, writer ? a.sel_idx : nullptr,
+                    writer ? a.sel_w : nullptr, writer ? a.sel_gamma : nullptr, nullptr, ssel);
+      }
+      __syncthreads();
+      const int e = ssel[k];
+      blob = a.experts + (a.offsets ? a.offsets[e] : static_cast<uint64_t>(e) * a.stride);
+      inter = a.I;
+    } else {
+      row_source(a, j, blob, t, inter);
+    }
+  } else {
+    row_source(a, j, blob, t, inter);
+  }
   if (p * 16 >= inter) return;
   const int rows = gridDim.x;
   float* part = a.h + ((static_cast<size_t>(z) * rows + j) * a.hstride + 16 * p) * 2;
@@ -91,8 +124,6 @@ __global__ __launch_bounds__(64 * kGemvGateUpWaves) void k_gateup_gemv(FfnArgs a
   }
   const int H = a.H, G = a.G;
   const int ng = H / G;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, kb = lane >> 4;
   const int nc = H / 64;
   const uint4* qblk = reinterpret_cast<const uint4*>(blob) + static_cast<size_t>(p) * nc * 64 * NQ;
@@ -480,13 +511,31 @@ hipError_t launch_gateup_gemv(int act, const FfnArgs& a, hipStream_t s) {
   const int rows = a.T * a.K + (a.Is > 0 ? a.T : 0);
   dim3 grid(rows, (a.hstride + 15) / 16, kGemvSplit);
   const dim3 block(64 * kGemvGateUpWaves);
-  if (a.bits == 8) {
-    if (act == 2) hipLaunchKernelGGL((k_gateup_gemv<2, 8>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_gateup_gemv<1, 8>), grid, block, 0, s, a);
-  } else {
-    if (act == 2) hipLaunchKernelGGL((k_gateup_gemv<2, 4>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_gateup_gemv<1, 4>), grid, block, 0, s, a);
+  int kj = 0;   // logits per lane of the fused top-K (0: not fused)
+  if (a.route_part != nullptr) {
+    if (a.E > 512) return hipErrorInvalidValue;
+    kj = a.E <= 64 ? 1 : a.E <= 128 ? 2 : a.E <= 256 ? 4 : 8;
   }
+#define GATEUP_LAUNCH(ACT_, BITS_, KJ_) hipLaunchKernelGGL((k_gateup_gemv<ACT_, BITS_, KJ_>), grid, block, 0, s, a)
+#define GATEUP_KJ(ACT_, BITS_)               \
+  do {                                       \
+    switch (kj) {                            \
+      case 1: GATEUP_LAUNCH(ACT_, BITS_, 1); break; \
+      case 2: GATEUP_LAUNCH(ACT_, BITS_, 2); break; \
+      case 4: GATEUP_LAUNCH(ACT_, BITS_, 4); break; \
+      case 8: GATEUP_LAUNCH(ACT_, BITS_, 8); break; \
+      default: GATEUP_LAUNCH(ACT_, BITS_, 0); break; \
+    }                                        \
+  } while (0)
+  if (a.bits == 8) {
+    if (act == 2) GATEUP_KJ(2, 8);
+    else GATEUP_KJ(1, 8);
+  } else {
+    if (act == 2) GATEUP_KJ(2, 4);
+    else GATEUP_KJ(1, 4);
+  }
+#undef GATEUP_KJ
+#undef GATEUP_LAUNCH
   return hipGetLastError();
 }
 

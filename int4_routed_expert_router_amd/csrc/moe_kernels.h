@@ -34,6 +34,16 @@ struct FfnArgs {
   int T, H, K, I, Is, G, E;
   int hstride;                // max(I, Is)
   int bits;                   // expert weight width, 4 or 8 (8: GEMV family only)
+  // GEMV family with top-K fused into gate/up (route_part != nullptr): every
+  // routed row's workgroups select the token's experts from the router's
+  // logit slices themselves; one workgroup per token (rank 0, pair-tile 0,
+  // split 0) writes the selection to sel_idx (== topk_idx), sel_w, sel_gamma
+  const float* route_part;    // [route_nparts][T][E+1]
+  const float* route_bias;    // [E] or nullptr (also nullptr when the slices hold it)
+  int route_nparts;
+  int32_t* sel_idx;
+  float* sel_w;
+  float* sel_gamma;
 };
 
 // Units of the grouped family, written by the bucketing kernel.  A unit is up

@@ -192,3 +192,36 @@ def test_deterministic_repeat():
         a = run_layer(wl, dl, x_bits, path)
         b = run_layer(wl, dl, x_bits, path)
         assert np.array_equal(a["y"], b["y"])
+
+
+@pytest.mark.parametrize("wl,n_tokens", [(synth.TINY, 4), (RAGGED, 7), (synth.DEC80, 1), (synth.DEC80, 3)],
+                         ids=["tiny_E16", "ragged_E24", "dec80_T1", "dec80_T3"])
+def test_fused_topk_gemv_matches_separate_kernels(wl, n_tokens):
+    """On the GEMV family a layer call selects the experts inside the gate/up
+    kernel (no top-K launch); moe_route + moe_expert_ffn run the top-K
+    kernel.  Same code, same order: bit-identical selection, weights, gate
+    and output."""
+    import torch
+    from int4_routed_expert_router_amd import api
+    dl = DeviceLayer(wl, 2)
+    desc = desc_for(wl, path=1)
+    x = torch.from_numpy(synth.tokens(wl, n_tokens=n_tokens).view(np.int16).copy()).cuda()
+    T, K, H = n_tokens, wl.top_k, wl.hidden
+    layer = dl.api_layer()
+    ws = api.workspace(desc, T)
+    outs = []
+    for fused in (True, False):
+        y = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
+        idx = torch.full((T, K), -7, dtype=torch.int32, device="cuda")
+        w = torch.full((T, K), float("nan"), dtype=torch.float32, device="cuda")
+        g = torch.full((T,), float("nan"), dtype=torch.float32, device="cuda")
+        if fused:
+            api.layer_forward(desc, layer, x, y, idx, w, g, ws=ws)
+        else:
+            api.route(desc, layer, x, idx, w, g, ws=ws)
+            api.expert_ffn(desc, layer, x, idx, w, g, y, ws=ws)
+        torch.cuda.synchronize()
+        outs.append([t.cpu().numpy() for t in (y, idx, w, g)])
+    for name, a, b in zip(("y", "idx", "w", "gamma"), outs[0], outs[1]):
+        assert np.array_equal(a, b), f"{wl.name} T={n_tokens}: {name} differs between fused and separate top-K"
+    assert np.isfinite(outs[0][0]).all()
