@@ -479,6 +479,78 @@ __global__ __launch_bounds__(512) void k_combine(const float* __restrict__ yrow,
   }
 }
 
+// The same combine when row (t, k) sits at t*K + k (no bucketing): the source
+// rows are known before any load, so every row load, the weights and the
+// residual are issued at once; the sums are the same as k_combine's, in the
+// same order (rank 0..K-1, shared last).
+template <int ACT, bool EPI>
+__global__ __launch_bounds__(512) void k_combine_direct(const float* __restrict__ yrow, const float* __restrict__ w,
+                                                        const float* __restrict__ gamma, int T, int K, int H,
+                                                        int has_shared, float* __restrict__ y,
+                                                        float* __restrict__ r, uint16_t* __restrict__ x_next) {
+  __shared__ float lds16[16];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const int H4 = H / 4;
+  constexpr int kPer = kMaxH / 4 / 512;
+  constexpr int kB = 16;
+  const int ns = K + has_shared;
+  auto src_row = [&](int i) { return i < K ? t * K + i : T * K + t; };
+  auto weight = [&](int i) { return i < K ? w[t * K + i] : gamma[t]; };
+  float ss = 0.0f;
+  float4 rr[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int c4 = tid + 512 * u;
+    if (c4 < H4) {
+      if constexpr (EPI) rr[u] = reinterpret_cast<const float4*>(r + static_cast<size_t>(t) * H)[c4];
+      float4 acc = make_float4(0, 0, 0, 0);
+      for (int k0 = 0; k0 < ns; k0 += kB) {
+        float4 v[kB];
+#pragma unroll
+        for (int b = 0; b < kB; ++b)
+          v[b] = reinterpret_cast<const float4*>(yrow + static_cast<size_t>(src_row(min(k0 + b, ns - 1))) * H)[c4];
+#pragma unroll
+        for (int b = 0; b < kB; ++b) {
+          if (k0 + b < ns) {   // uniform
+            const float wk = weight(k0 + b);
+            acc.x = fmaf(wk, v[b].x, acc.x);
+            acc.y = fmaf(wk, v[b].y, acc.y);
+            acc.z = fmaf(wk, v[b].z, acc.z);
+            acc.w = fmaf(wk, v[b].w, acc.w);
+          }
+        }
+      }
+      if (y) reinterpret_cast<float4*>(y + static_cast<size_t>(t) * H)[c4] = acc;
+      if constexpr (EPI) {
+        float4 rv = rr[u];
+        rv.x += acc.x;
+        rv.y += acc.y;
+        rv.z += acc.z;
+        rv.w += acc.w;
+        reinterpret_cast<float4*>(r + static_cast<size_t>(t) * H)[c4] = rv;
+        rr[u] = rv;
+        ss = fmaf(rv.x, rv.x, ss);
+        ss = fmaf(rv.y, rv.y, ss);
+        ss = fmaf(rv.z, rv.z, ss);
+        ss = fmaf(rv.w, rv.w, ss);
+      }
+    }
+  }
+  if constexpr (EPI) {
+    const float tot = block_sum(ss, lds16);
+    const float inv_rms = 1.0f / sqrtf(tot / static_cast<float>(H) + 1e-6f);
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int c4 = tid + 512 * u;
+      if (c4 < H4) {
+        const uint32_t a0 = f32_to_act<ACT>(rr[u].x * inv_rms), a1 = f32_to_act<ACT>(rr[u].y * inv_rms);
+        const uint32_t a2 = f32_to_act<ACT>(rr[u].z * inv_rms), a3 = f32_to_act<ACT>(rr[u].w * inv_rms);
+        reinterpret_cast<uint2*>(x_next + static_cast<size_t>(t) * H)[c4] = make_uint2(a0 | (a1 << 16), a2 | (a3 << 16));
+      }
+    }
+  }
+}
+
 template <int ACT>
 __global__ __launch_bounds__(256) void k_epilogue(const float* __restrict__ y, float* __restrict__ r,
                                                   uint16_t* __restrict__ x_next, int H) {
@@ -550,6 +622,19 @@ hipError_t launch_down_gemv(const FfnArgs& a, hipStream_t s) {
 hipError_t launch_combine(int act, const float* yrow, const int32_t* inv, const float* w, const float* gamma, int T,
                           int K, int H, bool has_shared, float* y, float* r, uint16_t* x_next, hipStream_t s) {
   const int hs = has_shared ? 1 : 0;
+  if (inv == nullptr) {
+    if (r == nullptr) {
+      hipLaunchKernelGGL((k_combine_direct<2, false>), dim3(T), dim3(512), 0, s, yrow, w, gamma, T, K, H, hs, y, r,
+                         x_next);
+    } else if (act == 2) {
+      hipLaunchKernelGGL((k_combine_direct<2, true>), dim3(T), dim3(512), 0, s, yrow, w, gamma, T, K, H, hs, y, r,
+                         x_next);
+    } else {
+      hipLaunchKernelGGL((k_combine_direct<1, true>), dim3(T), dim3(512), 0, s, yrow, w, gamma, T, K, H, hs, y, r,
+                         x_next);
+    }
+    return hipGetLastError();
+  }
   if (r == nullptr) {
     hipLaunchKernelGGL((k_combine<2, false>), dim3(T), dim3(512), 0, s, yrow, inv, w, gamma, T, K, H, hs, y, r,
                        x_next);
