@@ -202,8 +202,11 @@ moe_status moe_expert_ffn(const moe_layer_desc* desc, const moe_layer_weights* w
                           const float* shared_gate, float* y, void* ws, size_t ws_bytes,
                           moe_stream stream);
 
-/* The whole block: moe_route then moe_expert_ffn.  Optional device outputs
- * topk_idx_or_null [T][K], topk_w_or_null [T][K], shared_gate_or_null [T]. */
+/* The whole block, bit for bit the results of moe_route then
+ * moe_expert_ffn.  On the GEMV family with E <= 512 the top-K selection runs
+ * inside the gate/up kernel instead of a launch of its own.  Optional device
+ * outputs topk_idx_or_null [T][K], topk_w_or_null [T][K],
+ * shared_gate_or_null [T]. */
 moe_status moe_layer_forward(const moe_layer_desc* desc, const moe_layer_weights* w, const void* x,
                              int32_t n_tokens, float* y, int32_t* topk_idx_or_null,
                              float* topk_w_or_null, float* shared_gate_or_null,
