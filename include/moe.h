@@ -76,9 +76,7 @@ enum { MOE_PATH_AUTO = 0, MOE_PATH_GEMV = 1, MOE_PATH_GROUPED = 2 };
  *   act_dtype:       MOE_F16 or MOE_BF16 (dtype of x); y is always fp32
  *   path:            MOE_PATH_*
  *   weight_bits:     4 (or 0, the same) for int4 experts, 8 for int8 experts
- *                    (routed and shared alike).  int8 experts run on the GEMV
- *                    family at every batch size: AUTO picks it, GROUPED is
- *                    MOE_ESHAPE. */
+ *                    (routed and shared alike), on either kernel family. */
 typedef struct {
   int32_t hidden, n_experts, top_k, inter, shared_inter, group_size;
   int32_t act_dtype;

@@ -70,7 +70,6 @@ moe_status check_desc(const moe_layer_desc* d) {
   if (d->path < MOE_PATH_AUTO || d->path > MOE_PATH_GROUPED) return fail(MOE_EINVAL, "path=%d is not a MOE_PATH_*", d->path);
   if (d->weight_bits != 0 && d->weight_bits != 4 && d->weight_bits != 8)
     return fail(MOE_ESHAPE, "weight_bits=%d must be 4 (or 0) or 8", d->weight_bits);
-  if (d->path == MOE_PATH_GROUPED && wbits(d) == 8) return fail(MOE_ESHAPE, "int8 experts run on the GEMV family only");
   if (d->path == MOE_PATH_GROUPED && !grouped_fits(d))
     return fail(MOE_ESHAPE, "the grouped family needs hidden <= %d and inter, shared_inter <= %d", moe::kGroupedMaxH,
                 moe::kGroupedMaxInter);
@@ -138,7 +137,7 @@ bool grouped_fits(const moe_layer_desc* d) {
 }
 
 bool use_grouped(const moe_layer_desc* d, int T) {
-  if (d->path == MOE_PATH_GEMV || wbits(d) == 8) return false;
+  if (d->path == MOE_PATH_GEMV) return false;
   if (d->path == MOE_PATH_GROUPED) return true;
   return static_cast<long long>(T) * d->top_k > MOE_GEMV_MAX_ROWS && grouped_fits(d);
 }

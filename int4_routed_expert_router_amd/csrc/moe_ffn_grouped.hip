@@ -37,6 +37,14 @@
 // written operand-ready by the gate/up kernel together with the fp32 sums of
 // hi + lo over 16-column blocks for the down kernel's bias term.
 //
+// int8 experts (BITS = 8) use the same stream with two 16-byte loads per lane
+// and chunk (the tile A and tile B planes of the blob).  A byte q becomes
+// the fp16 subnormal q * 2^-24 with the same kind of mask: w & 0x00FF00FF and
+// (w >> 8) & 0x00FF00FF hold values (0, 2) and (1, 3) of a word, so the A
+// operand is packed in that order, (x0, x2, x1, x3, x4, x6, x5, x7), and
+// unscaled; the gate/up epilogue stores h with the columns of every 4 in
+// the order (0, 2, 1, 3) for the down projection.
+//
 // Operand layout of v_mfma_f32_16x16x32 (64 lanes, lane l: n = l % 16,
 // kb = l / 16): A lane holds row m = n, k = 8kb..8kb+7; B lane holds column n,
 // k = 8kb..8kb+7; C lane holds rows 4kb..4kb+3 of column n.  The expert blob
@@ -67,6 +75,14 @@ __device__ __forceinline__ uint4 word_operand(uint32_t w) {
   const uint32_t t = w >> 8;
   return make_uint4(w & 0x000F000Fu, w & 0x00F000F0u, t & 0x000F000Fu, t & 0x00F000F0u);
 }
+// B operand of 8 int8 values (bytes 0..3 of lo, then of hi): halves
+// (v0, v2), (v1, v3), (v4, v6), (v5, v7) as q * 2^-24.
+__device__ __forceinline__ uint4 byte_operand(uint32_t lo, uint32_t hi) {
+  return make_uint4(lo & 0x00FF00FFu, (lo >> 8) & 0x00FF00FFu, hi & 0x00FF00FFu, (hi >> 8) & 0x00FF00FFu);
+}
+// Storage column of column c of h for the int8 down projection: within every
+// group of 4 the order (0, 2, 1, 3).
+__device__ __forceinline__ int h8_col(int c) { return (c & ~3) | ((c & 1) << 1) | ((c >> 1) & 1); }
 
 __device__ __forceinline__ uint32_t f32_to_f16_bits(float v) {
   return __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
@@ -75,18 +91,34 @@ __device__ __forceinline__ float f16_bits_f32(uint32_t b) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(b)));
 }
 
-// A operand from 8 activations (16 bytes, value j at half j): fp16, values
-// 2, 3, 6, 7 scaled by 1/16.  Adds the 8 activations to sum.
-template <int ACT>
+// A operand from 8 activations (16 bytes, value j at half j): fp16; int4:
+// values 2, 3, 6, 7 scaled by 1/16; int8: unscaled, in the order 0, 2, 1, 3,
+// 4, 6, 5, 7.  Adds the 8 activations to sum.
+template <int ACT, int BITS = 4>
 __device__ __forceinline__ uint4 act_operand(uint4 raw, float& sum) {
   const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
   uint32_t o[4];
+  if constexpr (BITS == 8) {
+    float v[8];
 #pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const float v0 = act_to_f32<ACT>(w[d] & 0xFFFFu), v1 = act_to_f32<ACT>(w[d] >> 16);
-    sum += v0 + v1;
-    const float f = (d & 1) ? 0.0625f : 1.0f;
-    o[d] = f32_to_f16_bits(v0 * f) | (f32_to_f16_bits(v1 * f) << 16);
+    for (int d = 0; d < 4; ++d) {
+      v[2 * d] = act_to_f32<ACT>(w[d] & 0xFFFFu);
+      v[2 * d + 1] = act_to_f32<ACT>(w[d] >> 16);
+      sum += v[2 * d] + v[2 * d + 1];
+    }
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      o[2 * p] = f32_to_f16_bits(v[4 * p]) | (f32_to_f16_bits(v[4 * p + 2]) << 16);
+      o[2 * p + 1] = f32_to_f16_bits(v[4 * p + 1]) | (f32_to_f16_bits(v[4 * p + 3]) << 16);
+    }
+  } else {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const float v0 = act_to_f32<ACT>(w[d] & 0xFFFFu), v1 = act_to_f32<ACT>(w[d] >> 16);
+      sum += v0 + v1;
+      const float f = (d & 1) ? 0.0625f : 1.0f;
+      o[d] = f32_to_f16_bits(v0 * f) | (f32_to_f16_bits(v1 * f) << 16);
+    }
   }
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
@@ -126,15 +158,24 @@ __device__ __forceinline__ int logical_wg() {
   return (blockIdx.x & 7) * (W >> 3) + (blockIdx.x >> 3);
 }
 
-// One slot of the weight stream: 16 bytes of nibbles and the fp16 (s, b) pairs
-// of the chunk's group(s) for the lane's row n of both tiles.
+// One slot of the weight stream: 16 bytes of nibbles (int8: 16 bytes of each
+// tile plane) and the fp16 (s, b) pairs of the chunk's group(s) for the
+// lane's row n of both tiles.
 struct Slot {
-  uint4 q;
+  uint4 q, q2;    // q2: tile B plane (int8 only)
   uint2 s0, s1;   // s1: second group of the chunk (G = 32 only)
 };
-template <int G>
+// vector-memory loads of one slot (the down kernel's staged barrier counts them)
+template <int G, int BITS>
+constexpr int kLoadsPerSlot = BITS / 4 + (G == 32 ? 2 : 1);
+template <int G, int BITS = 4>
 __device__ __forceinline__ void load_slot(Slot& sl, const uint4* qb, const uint8_t* sb, int c) {
-  sl.q = qb[static_cast<size_t>(c) * 64];
+  if constexpr (BITS == 8) {
+    sl.q = qb[static_cast<size_t>(2 * c) * 64];
+    sl.q2 = qb[static_cast<size_t>(2 * c + 1) * 64];
+  } else {
+    sl.q = qb[static_cast<size_t>(c) * 64];
+  }
   if constexpr (G == 32) {
     sl.s0 = *reinterpret_cast<const uint2*>(sb + static_cast<size_t>(2 * c) * 128);
     sl.s1 = *reinterpret_cast<const uint2*>(sb + static_cast<size_t>(2 * c + 1) * 128);
@@ -161,13 +202,20 @@ struct Decoded {
   float sA0, sB0, sA1, sB1;
   float cA0, cB0, cA1, cB1;
 };
-template <int G>
+template <int G, int BITS = 4>
 __device__ __forceinline__ Decoded decode_slot(const Slot& sl) {
   Decoded d;
-  d.bA0 = word_operand(sl.q.x);
-  d.bA1 = word_operand(sl.q.y);
-  d.bB0 = word_operand(sl.q.z);
-  d.bB1 = word_operand(sl.q.w);
+  if constexpr (BITS == 8) {
+    d.bA0 = byte_operand(sl.q.x, sl.q.y);
+    d.bA1 = byte_operand(sl.q.z, sl.q.w);
+    d.bB0 = byte_operand(sl.q2.x, sl.q2.y);
+    d.bB1 = byte_operand(sl.q2.z, sl.q2.w);
+  } else {
+    d.bA0 = word_operand(sl.q.x);
+    d.bA1 = word_operand(sl.q.y);
+    d.bB0 = word_operand(sl.q.z);
+    d.bB1 = word_operand(sl.q.w);
+  }
   d.sA0 = f16_bits_to_f32(sl.s0.x & 0xFFFFu);
   d.sB0 = f16_bits_to_f32(sl.s0.y & 0xFFFFu);
   d.cA0 = f16_bits_to_f32(sl.s0.x >> 16);
@@ -318,8 +366,9 @@ __device__ __forceinline__ void staged_barrier() {
 // (columns with (col & 2) != 0 scaled by 1/16), at rows row0.., columns
 // 16 pt.., and hsum[row][pt] = sum over the 16 columns of h (hi + lo).
 // ---------------------------------------------------------------------------
-template <int ACT, int G>
+template <int ACT, int G, int BITS>
 __global__ __launch_bounds__(512) void k_gateup_tiles(FfnArgs a) {
+  constexpr int NQ = BITS / 4;   // 16-byte weight loads per lane and chunk
   // tiles are processed in pairs (one barrier per pair); the two tiles of a
   // pair use the two slot groups, so kDepth = 2 tiles are in flight per wave
   constexpr int kDepth = 2;
@@ -407,8 +456,8 @@ __global__ __launch_bounds__(512) void k_gateup_tiles(FfnArgs a) {
 #pragma unroll
     for (int j = 0; j < kSlot; ++j) {
       float s0 = 0.0f, s1 = 0.0f;
-      xa[j][0] = act_operand<ACT>(xr[j][0], s0);
-      xa[j][1] = act_operand<ACT>(xr[j][1], s1);
+      xa[j][0] = act_operand<ACT, BITS>(xr[j][0], s0);
+      xa[j][1] = act_operand<ACT, BITS>(xr[j][1], s1);
       float hs[kHalves];
       if constexpr (G == 32) {
         hs[0] = s0;
@@ -459,8 +508,8 @@ __global__ __launch_bounds__(512) void k_gateup_tiles(FfnArgs a) {
         else want = cr.u;
       }
     }
-    qb = reinterpret_cast<const uint4*>(sblob) + static_cast<size_t>(cr.pt) * nc * 64 + lane;
-    sb = sblob + blob_gu_s(H, sI) + (static_cast<size_t>(cr.pt) * ng * 16 + n) * 8;
+    qb = reinterpret_cast<const uint4*>(sblob) + static_cast<size_t>(cr.pt) * nc * 64 * NQ + lane;
+    sb = sblob + blob_gu_s(H, sI, BITS) + (static_cast<size_t>(cr.pt) * ng * 16 + n) * 8;
   };
   Cursor cc = locate(t0);   // compute cursor (tile t)
   Cursor rc = cc;           // refill cursor (tile min(t + kDepth, t1 - 1))
@@ -474,7 +523,7 @@ __global__ __launch_bounds__(512) void k_gateup_tiles(FfnArgs a) {
     const uint8_t* sb;
     tile_src(rc, qb, sb);
 #pragma unroll
-    for (int j = 0; j < kSlot; ++j) load_slot<G>(sl[hf * kSlot + j], qb, sb, min(wave + kWaves * j, nc - 1));
+    for (int j = 0; j < kSlot; ++j) load_slot<G, BITS>(sl[hf * kSlot + j], qb, sb, min(wave + kWaves * j, nc - 1));
     if (rt + 1 < t1) {
       ++rt;
       advance(rc);
@@ -512,8 +561,8 @@ __global__ __launch_bounds__(512) void k_gateup_tiles(FfnArgs a) {
     for (int j = 0; j < kSlot; ++j) {
       const int c = wave + kWaves * j;
       Slot& s = sl[hf * kSlot + j];
-      const Decoded d = decode_slot<G>(s);
-      load_slot<G>(s, qnx, snx, min(c, nc - 1));
+      const Decoded d = decode_slot<G, BITS>(s);
+      load_slot<G, BITS>(s, qnx, snx, min(c, nc - 1));
       Prod p;
       if (c < nc) p = chunk_mfma<G, false>(d, xa[j][0], xa[j][1], xa[j][0], xa[j][1]);
       if (j > 0 && c - kWaves < nc) {
@@ -556,8 +605,9 @@ __global__ __launch_bounds__(512) void k_gateup_tiles(FfnArgs a) {
       // few ulp, far inside the block's tolerance)
       const float hv = ga * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * ga)) * up;
       // operand-ready fp16 hi + lo of h * f, f = 1/16 on the columns the down
-      // projection's B operand carries as q * 2^-20 (column 16 pt + nn)
-      const bool sc = (nn & 2) != 0;
+      // projection's B operand carries as q * 2^-20 (column 16 pt + nn); int8:
+      // f = 1, stored at the permuted column h8_col
+      const bool sc = BITS == 4 && (nn & 2) != 0;
       const float hf_v = sc ? hv * 0.0625f : hv;
       const uint32_t hi = f32_to_f16_bits(hf_v);
       const uint32_t lo = f32_to_f16_bits(hf_v - f16_bits_f32(hi));
@@ -566,7 +616,8 @@ __global__ __launch_bounds__(512) void k_gateup_tiles(FfnArgs a) {
       // sum over the 16 columns of this row of the tile (one 16-lane DPP row)
       hs = __uint_as_float(dpp_row_sum(__float_as_uint(hs)));
       if (m < o.mc) {
-        const size_t off = static_cast<size_t>(o.row0 + m) * a.hstride + 16 * o.pt + nn;
+        const int col = BITS == 8 ? h8_col(nn) : nn;
+        const size_t off = static_cast<size_t>(o.row0 + m) * a.hstride + 16 * o.pt + col;
         h_hi[off] = static_cast<uint16_t>(hi);
         h_lo[off] = static_cast<uint16_t>(lo);
         if (nn == 0) a.hsum[static_cast<size_t>(o.row0 + m) * hs_stride + o.pt] = hs;
@@ -597,9 +648,11 @@ __global__ __launch_bounds__(512) void k_gateup_tiles(FfnArgs a) {
 // hi, lo) of the unit's rows is staged in LDS.  The second wave's partial
 // goes through LDS; the first adds it and stores yrow (unweighted, fp32).
 // ---------------------------------------------------------------------------
-template <int G>
+template <int G, int BITS>
 __global__ __launch_bounds__(512) void k_down_tiles(FfnArgs a) {
-  constexpr int kDepth = G == 32 ? 2 : 4;
+  constexpr int NQ = BITS / 4;   // 16-byte weight loads per lane and chunk
+  // quads whose weights are in flight (int8 slots are twice as large)
+  constexpr int kDepth = (G == 32 || BITS == 8) ? 2 : 4;
   constexpr int kHalves = G == 32 ? 2 : 1;
   __shared__ __attribute__((aligned(16))) uint16_t hsh[kSub * kGroupedMaxInter];
   __shared__ __attribute__((aligned(16))) uint16_t hsl[kSub * kGroupedMaxInter];
@@ -638,8 +691,8 @@ __global__ __launch_bounds__(512) void k_down_tiles(FfnArgs a) {
       sI = hd.expert < 0 ? a.Is : a.I;
     }
     ncq = sI / 64;
-    qb = reinterpret_cast<const uint4*>(sblob + blob_d_q(H, sI)) + static_cast<size_t>(pt) * ncq * 64 + lane;
-    sb = sblob + blob_d_s(H, sI, G) + (static_cast<size_t>(pt) * (sI / G) * 16 + n) * 8;
+    qb = reinterpret_cast<const uint4*>(sblob + blob_d_q(H, sI, BITS)) + static_cast<size_t>(pt) * ncq * 64 * NQ + lane;
+    sb = sblob + blob_d_s(H, sI, G, BITS) + (static_cast<size_t>(pt) * (sI / G) * 16 + n) * 8;
   };
   // stage h (hi, lo) of a unit's rows (direct-to-LDS) and fetch the sums of
   // h over 16-column blocks; the 32-column sums are stored afterwards, so
@@ -675,11 +728,12 @@ __global__ __launch_bounds__(512) void k_down_tiles(FfnArgs a) {
     int ncq;
     tile_src(min(s0 + hf, s1 - 1), qb, sb, ncq);
 #pragma unroll
-    for (int j = 0; j < kSlot; ++j) load_slot<G>(sl[hf * kSlot + j], qb, sb, min(kh + 2 * j, ncq - 1));
+    for (int j = 0; j < kSlot; ++j) load_slot<G, BITS>(sl[hf * kSlot + j], qb, sb, min(kh + 2 * j, ncq - 1));
   }
-  staged_barrier<kDepth * kSlot * (G == 32 ? 3 : 2)>();
+  // the weight loads just issued may stay in flight; the staging before them may not
+  staged_barrier<kDepth * kSlot * kLoadsPerSlot<G, BITS>>();
   stage_finish(nc * 64, hp0, hp1);
-  staged_barrier<kDepth * kSlot * (G == 32 ? 3 : 2)>();
+  staged_barrier<kDepth * kSlot * kLoadsPerSlot<G, BITS>>();
   auto process = [&](const int q, auto hfc) {
     constexpr int hf = decltype(hfc)::value;
     const int u = q / qpu;
@@ -717,8 +771,8 @@ __global__ __launch_bounds__(512) void k_down_tiles(FfnArgs a) {
     for (int j = 0; j < kSlot; ++j) {
       const int c = kh + 2 * j;
       Slot& s = sl[hf * kSlot + j];
-      const Decoded d = decode_slot<G>(s);
-      load_slot<G>(s, qnx, snx, min(c, ncn - 1));
+      const Decoded d = decode_slot<G, BITS>(s);
+      load_slot<G, BITS>(s, qnx, snx, min(c, ncn - 1));
       Prod p;
       float cs0[4], cs1[4];
       if (c < nc) {
@@ -786,24 +840,37 @@ __global__ __launch_bounds__(512) void k_down_tiles(FfnArgs a) {
 }
 
 hipError_t launch_gateup_grouped(int act, const FfnArgs& a, hipStream_t s) {
-#define GU_LAUNCH(A_, G_) hipLaunchKernelGGL((k_gateup_tiles<A_, G_>), dim3(kGridTiles), dim3(512), 0, s, a)
-  if (act == 2) {
-    if (a.G == 32) GU_LAUNCH(2, 32);
-    else if (a.G == 64) GU_LAUNCH(2, 64);
-    else GU_LAUNCH(2, 128);
+#define GU_LAUNCH(A_, G_, B_) hipLaunchKernelGGL((k_gateup_tiles<A_, G_, B_>), dim3(kGridTiles), dim3(512), 0, s, a)
+#define GU_G(A_, B_)                      \
+  do {                                    \
+    if (a.G == 32) GU_LAUNCH(A_, 32, B_); \
+    else if (a.G == 64) GU_LAUNCH(A_, 64, B_); \
+    else GU_LAUNCH(A_, 128, B_);          \
+  } while (0)
+  if (a.bits == 8) {
+    if (act == 2) GU_G(2, 8);
+    else GU_G(1, 8);
   } else {
-    if (a.G == 32) GU_LAUNCH(1, 32);
-    else if (a.G == 64) GU_LAUNCH(1, 64);
-    else GU_LAUNCH(1, 128);
+    if (act == 2) GU_G(2, 4);
+    else GU_G(1, 4);
   }
+#undef GU_G
 #undef GU_LAUNCH
   return hipGetLastError();
 }
 
 hipError_t launch_down_grouped(const FfnArgs& a, hipStream_t s) {
-  if (a.G == 32) hipLaunchKernelGGL((k_down_tiles<32>), dim3(kGridTiles), dim3(512), 0, s, a);
-  else if (a.G == 64) hipLaunchKernelGGL((k_down_tiles<64>), dim3(kGridTiles), dim3(512), 0, s, a);
-  else hipLaunchKernelGGL((k_down_tiles<128>), dim3(kGridTiles), dim3(512), 0, s, a);
+#define DN_LAUNCH(G_, B_) hipLaunchKernelGGL((k_down_tiles<G_, B_>), dim3(kGridTiles), dim3(512), 0, s, a)
+  if (a.bits == 8) {
+    if (a.G == 32) DN_LAUNCH(32, 8);
+    else if (a.G == 64) DN_LAUNCH(64, 8);
+    else DN_LAUNCH(128, 8);
+  } else {
+    if (a.G == 32) DN_LAUNCH(32, 4);
+    else if (a.G == 64) DN_LAUNCH(64, 4);
+    else DN_LAUNCH(128, 4);
+  }
+#undef DN_LAUNCH
   return hipGetLastError();
 }
 

@@ -1,6 +1,7 @@
 """GPU parity of int8 affine experts (the pages' other group-quantisation
-width) against the fp64 oracle, through the C ABI.  int8 runs on the GEMV
-kernel family at every batch size."""
+width) against the fp64 oracle, through the C ABI, on both kernel families:
+the per-row GEMVs and the grouped matrix-core kernels (bytes enter the
+matrix cores as exact fp16 subnormals)."""
 import dataclasses
 
 import numpy as np
@@ -21,23 +22,32 @@ TINY8_G128 = dataclasses.replace(TINY8, name="tiny_i8_g128", inter=128, shared_i
 BAT80I8 = dataclasses.replace(synth.BAT80, name="bat80i8", bits=8, scale_lo=1e-4, scale_hi=1e-3)
 
 
-@pytest.mark.parametrize("path", [0, 1], ids=["auto", "gemv"])
+@pytest.mark.parametrize("path", [0, 1, 2], ids=["auto", "gemv", "grouped"])
 def test_tiny_int8(path):
     check_layer(TINY8, path, gpu_fill=False)
 
 
-@pytest.mark.parametrize("path", [0, 1], ids=["auto", "gemv"])
+@pytest.mark.parametrize("path", [0, 1, 2], ids=["auto", "gemv", "grouped"])
 def test_ragged_int8(path):
     check_layer(RAGGED8, path, gpu_fill=False)
 
 
-def test_int8_general_affine_bias():
-    check_layer(RAGGED8, 1, general_bias_seed=9)
+@pytest.mark.parametrize("path", [1, 2], ids=["gemv", "grouped"])
+def test_int8_general_affine_bias(path):
+    check_layer(RAGGED8, path, general_bias_seed=9)
 
 
-def test_int8_group_128_no_shared():
-    check_layer(TINY8_G128, 0, gpu_fill=False)
-    check_layer(TINY8_G128, 0, shared=False, gpu_fill=False)
+@pytest.mark.parametrize("path", [1, 2], ids=["gemv", "grouped"])
+def test_int8_group_128_no_shared(path):
+    check_layer(TINY8_G128, path, gpu_fill=False)
+    check_layer(TINY8_G128, path, shared=False, gpu_fill=False)
+
+
+def test_int8_grouped_group_32_many_tokens():
+    # group 32 (two groups per 64-column chunk) with units of up to 16 tokens
+    wl = dataclasses.replace(TINY8, name="tiny_i8_many", tokens=40, zipf_s=1.2, weight_seed=24, token_seed=124)
+    check_layer(wl, 2, gpu_fill=False)
+    check_layer(wl, 0, general_bias_seed=3)
 
 
 def test_int8_gpu_fill_matches_host_packer():
@@ -61,10 +71,11 @@ def test_int8_decode_layer_full_size(layer):
     print(f"dec80i8 layer {layer}: max err {worst:.3e} (tol {tol:.3e}), near ties {flagged}")
 
 
-def test_int8_batched_layer_full_size():
-    # 64 tokens x (10 + 1) rows: AUTO keeps int8 on the GEMV family
-    worst, tol, flagged = check_layer(BAT80I8, 0, layer=3)
-    print(f"bat80i8: max err {worst:.3e} (tol {tol:.3e}), near ties {flagged}")
+@pytest.mark.parametrize("path", [0, 1], ids=["auto_grouped", "gemv"])
+def test_int8_batched_layer_full_size(path):
+    # 64 tokens x (10 + 1) rows: AUTO takes the grouped family
+    worst, tol, flagged = check_layer(BAT80I8, path, layer=3)
+    print(f"bat80i8 path {path}: max err {worst:.3e} (tol {tol:.3e}), near ties {flagged}")
 
 
 def test_int8_and_int4_blobs_differ_in_stride():

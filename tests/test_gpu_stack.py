@@ -73,8 +73,8 @@ def oracle_sets(x64, wr64, b64, gpu_idx, k):
     return np.stack(sets), flagged
 
 
-# int8 experts: 12 tokens x 4 rows are past the GEMV row limit, and AUTO still
-# keeps int8 on the GEMV family
+# int8 experts: 12 tokens x 3 rows are past the GEMV row limit, so AUTO runs
+# them on the grouped matrix-core family
 STACK8 = dataclasses.replace(STACK, name="stack_i8", bits=8, scale_lo=1e-4, scale_hi=1e-3, weight_seed=32)
 
 
@@ -106,7 +106,7 @@ def test_stack_teacher_forced_parity(path, n_tokens, wl):
     assert_close(got["r"], r, "final residual")
 
 
-@pytest.mark.parametrize("wl", [STACK, STACK8], ids=["int4_grouped", "int8_gemv"])
+@pytest.mark.parametrize("wl", [STACK, STACK8], ids=["int4", "int8"])
 def test_graph_replay_matches_eager_bitwise(wl):
     import torch
     from int4_routed_expert_router_amd import api

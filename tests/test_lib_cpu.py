@@ -82,8 +82,7 @@ def test_int8_desc_validation():
     api.workspace_bytes(api.Desc(256, 16, 2, 64, 64, 32, weight_bits=0), 4)   # 0 reads as int4
     with pytest.raises(MoeError, match="MOE_ESHAPE"):
         api.workspace_bytes(api.Desc(256, 16, 2, 64, 64, 32, weight_bits=6), 4)
-    with pytest.raises(MoeError, match="MOE_ESHAPE"):   # int8 has no grouped kernels
-        api.workspace_bytes(api.Desc(256, 16, 2, 64, 64, 32, path=2, weight_bits=8), 4)
+    api.workspace_bytes(api.Desc(256, 16, 2, 64, 64, 32, path=2, weight_bits=8), 4)   # int8 on the matrix cores
 
 
 def test_packer_rejects_bad_nibbles():
