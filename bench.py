@@ -33,7 +33,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="bat80", choices=["bat80", "dec80", "dec35", "pool80", "dec80i8", "gdn80"])
+    ap.add_argument("--workload", default="bat80", choices=["bat80", "dec80", "dec35", "pool80", "dec80i8", "bat80i8", "gdn80"])
     ap.add_argument("--layers", type=int, default=0, help="override the number of layers (0 = workload's)")
     ap.add_argument("--path", type=int, default=0, help="0 auto, 1 GEMV family, 2 grouped family")
     ap.add_argument("--eager", action="store_true", help="launch kernels one by one instead of a HIP graph")
@@ -426,7 +426,7 @@ def main():
     wname = f"int{wl.bits}"
     expert_bytes = sum((a + 1) * B for a in act)
     expert_gbs = expert_bytes / (ms_per_step * 1e-3) / 1e9
-    grouped = wl.bits == 4 and (args.path == 2 or (args.path == 0 and wl.tokens * wl.top_k > 32))
+    grouped = args.path == 2 or (args.path == 0 and wl.tokens * wl.top_k > 32)
     print(f"[bench] {ms_per_step:.3f} ms/step, {tokens_s:.0f} tok/s, {wname} {expert_gbs:.0f} GB/s, "
           f"active experts/layer mean {np.mean(act):.1f}", file=sys.stderr, flush=True)
 
@@ -455,11 +455,11 @@ def main():
                     + 8 * st.desc.inter * st.desc.hidden // st.desc.group_size)
         per_launch = float(np.mean([(a + 1) * gu_bytes for a in act]))
         achieved = per_launch / (avg_us * 1e-6) / 1e9
-        tb = measured_traffic() if (grouped and args.workload == "bat80") else None
+        tb = measured_traffic() if args.workload == "bat80" and args.path != 1 else None
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": None if tb is None else round(tb / (avg_us * 1e-6) / 1e9, 1),
-                "kernel": "k_gateup_tiles (int4 gate/up + SwiGLU)" if grouped else
+                "kernel": f"k_gateup_tiles ({wname} gate/up + SwiGLU)" if grouped else
                           f"k_gateup_gemv ({wname} gate/up partial sums)",
                 "avg_us": round(avg_us, 2), "bytes_per_launch": int(per_launch),
                 "traffic_bytes_per_launch": None if tb is None else int(tb),
@@ -484,7 +484,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16" if grouped else ("f32" if wl.bits == 8 else wl.act_dtype),
-        "precision": "int4 weights as exact f16 matrix-core operands, activations f16, fp32 accumulate"
+        "precision": f"{wname} weights as exact f16 matrix-core operands, activations f16, fp32 accumulate"
                      if grouped else
                      ("int8 weights times activations widened to fp32, fp32 accumulate" if wl.bits == 8 else
                       "int4 weights, bf16/f16 dot2 products, fp32 accumulate"),

@@ -16,6 +16,7 @@ Workloads (shapes from the pages' two model sizes: 8 of 256 experts for the
            router weights x3 (logit noise sigma 3; measured hit rate 66%)
   dec80i8  dec80 shapes with int8 experts (the pages' other affine variant),
            scales U(1e-4, 1e-3) so that weights span the int4 range
+  bat80i8  bat80 with the int8 experts of dec80i8
 
 Expert weights (the bulk: 43.5 GB at the 80B shape) come from Philox4x32-10
 so that any single expert can be regenerated alone, here or on the GPU:
@@ -92,7 +93,8 @@ BAT80 = dataclasses.replace(DEC80, name="bat80", tokens=64, token_seed=103, zipf
 POOL80 = dataclasses.replace(DEC80, name="pool80", token_seed=104, slots_per_layer=128, steps=256,
                              drift_period=32, drift_seed=105, router_sigma=3.0 / math.sqrt(2048))
 DEC80I8 = dataclasses.replace(DEC80, name="dec80i8", bits=8, scale_lo=1e-4, scale_hi=1e-3)
-WORKLOADS = {w.name: w for w in (TINY, DEC35, DEC80, BAT80, POOL80, DEC80I8)}
+BAT80I8 = dataclasses.replace(BAT80, name="bat80i8", bits=8, scale_lo=1e-4, scale_hi=1e-3)
+WORKLOADS = {w.name: w for w in (TINY, DEC35, DEC80, BAT80, POOL80, DEC80I8, BAT80I8)}
 
 
 @dataclasses.dataclass(frozen=True)
