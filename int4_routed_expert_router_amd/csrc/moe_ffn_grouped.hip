@@ -645,8 +645,12 @@ __global__ __launch_bounds__(512) void k_gateup_tiles(FfnArgs a) {
 // down projection.  Tiles are down pair-tiles (32 output rows); a step takes 4
 // consecutive tiles of one unit (quad), tile q4 = wave % 4, and the two waves
 // w, w + 4 split the reduction (chunks w / 4 + 2 j).  h (operand-ready fp16
-// hi, lo) of the unit's rows is staged in LDS.  The second wave's partial
-// goes through LDS; the first adds it and stores yrow (unweighted, fp32).
+// hi, lo) of the unit's rows is staged in LDS, in one of two buffers: a
+// workgroup's range spans at most two units at the batch shapes, and both
+// are staged before the first weight loads, so the switch to the second unit
+// waits for nothing (a third unit, possible at other shapes, is staged at its
+// switch).  The second wave's partial goes through LDS; the first adds it and
+// stores yrow (unweighted, fp32).
 // ---------------------------------------------------------------------------
 template <int G, int BITS>
 __global__ __launch_bounds__(512) void k_down_tiles(FfnArgs a) {
@@ -654,11 +658,11 @@ __global__ __launch_bounds__(512) void k_down_tiles(FfnArgs a) {
   // quads whose weights are in flight (int8 slots are twice as large)
   constexpr int kDepth = (G == 32 || BITS == 8) ? 2 : 4;
   constexpr int kHalves = G == 32 ? 2 : 1;
-  __shared__ __attribute__((aligned(16))) uint16_t hsh[kSub * kGroupedMaxInter];
-  __shared__ __attribute__((aligned(16))) uint16_t hsl[kSub * kGroupedMaxInter];
+  __shared__ __attribute__((aligned(16))) uint16_t hsh[2][kSub * kGroupedMaxInter];
+  __shared__ __attribute__((aligned(16))) uint16_t hsl[2][kSub * kGroupedMaxInter];
   __shared__ float red[2][4][8][65];
-  __shared__ __attribute__((aligned(16))) float cs[kGroupedMaxInter / 32][kSub];   // 32-column sums of h
-  __shared__ int urow[kSub];
+  __shared__ __attribute__((aligned(16))) float cs[2][kGroupedMaxInter / 32][kSub];   // 32-column sums of h
+  __shared__ int urow[2][kSub];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, kb = lane >> 4;
   const int q4 = wave & 3, kh = wave >> 2;
@@ -699,11 +703,10 @@ __global__ __launch_bounds__(512) void k_down_tiles(FfnArgs a) {
   // that loads issued in between stay in flight (kSub * inter / 32 <= 512:
   // one sum per thread)
   static_assert(kSub * (kGroupedMaxInter / 32) <= 512, "one column sum per thread");
-  auto stage_issue = [&](int r0, int mcu, int Iu, float& p0, float& p1) {
-    if (tid < kSub) urow[tid] = r0 + tid;
-    __syncthreads();
-    stage_rows(h_hi, urow, mcu, a.hstride, Iu, hsh, wave, lane);
-    stage_rows(h_lo, urow, mcu, a.hstride, Iu, hsl, wave, lane);
+  // urow[b] must hold the unit's rows (and be visible) before the call
+  auto stage_issue = [&](int b, int r0, int mcu, int Iu, float& p0, float& p1) {
+    stage_rows(h_hi, urow[b], mcu, a.hstride, Iu, hsh[b], wave, lane);
+    stage_rows(h_lo, urow[b], mcu, a.hstride, Iu, hsl[b], wave, lane);
     const int m = tid & (kSub - 1), j = tid >> 4;
     p0 = p1 = 0.0f;
     if (j < Iu / 32 && m < mcu) {
@@ -712,13 +715,26 @@ __global__ __launch_bounds__(512) void k_down_tiles(FfnArgs a) {
       p1 = hs[1];
     }
   };
-  auto stage_finish = [&](int Iu, float p0, float p1) {
+  auto stage_finish = [&](int b, int Iu, float p0, float p1) {
     const int m = tid & (kSub - 1), j = tid >> 4;
-    if (j < Iu / 32) cs[j][m] = p0 + p1;
+    if (j < Iu / 32) cs[b][j][m] = p0 + p1;
   };
   int nc = sI / 64, upr = sI / 8;
-  float hp0, hp1;
-  stage_issue(row0, mc, sI, hp0, hp1);
+  // unit u uses buffer (u - u_first) & 1; the second unit of the range (if
+  // any) is staged right away
+  const int u_first = xu;
+  int hb = 0;
+  const bool two = (s1 - 1) / qpu > u_first;
+  const UnitHdr hd1 = two ? unit_hdr(a.units, u_first + 1) : hd0;
+  const int I1 = hd1.expert < 0 ? a.Is : a.I;
+  if (tid < kSub) {
+    urow[0][tid] = row0 + tid;
+    urow[1][tid] = hd1.row0 + tid;
+  }
+  __syncthreads();
+  float hp0, hp1, hq0 = 0.0f, hq1 = 0.0f;
+  stage_issue(0, row0, mc, sI, hp0, hp1);
+  if (two) stage_issue(1, hd1.row0, hd1.mc, I1, hq0, hq1);
   asm volatile("" ::: "memory");
   Slot sl[kDepth * kSlot];
 #pragma unroll
@@ -732,21 +748,29 @@ __global__ __launch_bounds__(512) void k_down_tiles(FfnArgs a) {
   }
   // the weight loads just issued may stay in flight; the staging before them may not
   staged_barrier<kDepth * kSlot * kLoadsPerSlot<G, BITS>>();
-  stage_finish(nc * 64, hp0, hp1);
+  stage_finish(0, nc * 64, hp0, hp1);
+  if (two) stage_finish(1, I1, hq0, hq1);
   staged_barrier<kDepth * kSlot * kLoadsPerSlot<G, BITS>>();
   auto process = [&](const int q, auto hfc) {
     constexpr int hf = decltype(hfc)::value;
     const int u = q / qpu;
     const int pt = (q - u * qpu) * 4 + q4;
     if (u != xu) {
-      __syncthreads();   // previous unit's readers are done
       const UnitHdr hd = unit_hdr(a.units, u);
       const int Iu = hd.expert < 0 ? a.Is : a.I;
-      float p0, p1;
-      stage_issue(hd.row0, hd.mc, Iu, p0, p1);
-      stage_finish(Iu, p0, p1);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+      hb = (u - u_first) & 1;
+      if (u > u_first + 1) {
+        // not staged yet: wait until the readers of unit u - 2 (same buffer)
+        // are done, then stage and wait for it
+        __syncthreads();
+        if (tid < kSub) urow[hb][tid] = hd.row0 + tid;
+        __syncthreads();
+        float p0, p1;
+        stage_issue(hb, hd.row0, hd.mc, Iu, p0, p1);
+        stage_finish(hb, Iu, p0, p1);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
       xu = u;
       row0 = hd.row0;
       mc = hd.mc;
@@ -757,10 +781,11 @@ __global__ __launch_bounds__(512) void k_down_tiles(FfnArgs a) {
     const uint8_t* snx;
     int ncn;
     tile_src(min(q + kDepth, s1 - 1), qnx, snx, ncn);
-    const uint16_t* ha0 = &hsh[(n * upr + (kb ^ (n & 7))) * 8];
-    const uint16_t* ha1 = &hsh[(n * upr + ((kb + 4) ^ (n & 7))) * 8];
-    const uint16_t* la0 = &hsl[(n * upr + (kb ^ (n & 7))) * 8];
-    const uint16_t* la1 = &hsl[(n * upr + ((kb + 4) ^ (n & 7))) * 8];
+    const uint16_t* ha0 = &hsh[hb][(n * upr + (kb ^ (n & 7))) * 8];
+    const uint16_t* ha1 = &hsh[hb][(n * upr + ((kb + 4) ^ (n & 7))) * 8];
+    const uint16_t* la0 = &hsl[hb][(n * upr + (kb ^ (n & 7))) * 8];
+    const uint16_t* la1 = &hsl[hb][(n * upr + ((kb + 4) ^ (n & 7))) * 8];
+    const float(*csb)[kSub] = cs[hb];
     f32x4_t accA = {0, 0, 0, 0}, accB = {0, 0, 0, 0}, biasA = {0, 0, 0, 0}, biasB = {0, 0, 0, 0};
     // the scale of chunk j is applied after the products of chunk j + 1 are
     // issued (matrix-core latency)
@@ -780,8 +805,8 @@ __global__ __launch_bounds__(512) void k_down_tiles(FfnArgs a) {
         const uint4 h1 = *reinterpret_cast<const uint4*>(ha1 + 64 * c);
         const uint4 l0 = *reinterpret_cast<const uint4*>(la0 + 64 * c);
         const uint4 l1 = *reinterpret_cast<const uint4*>(la1 + 64 * c);
-        const float4 c0 = *reinterpret_cast<const float4*>(&cs[2 * c][4 * kb]);
-        const float4 c1 = *reinterpret_cast<const float4*>(&cs[2 * c + 1][4 * kb]);
+        const float4 c0 = *reinterpret_cast<const float4*>(&csb[2 * c][4 * kb]);
+        const float4 c1 = *reinterpret_cast<const float4*>(&csb[2 * c + 1][4 * kb]);
         if constexpr (G == 32) {
           cs0[0] = c0.x; cs0[1] = c0.y; cs0[2] = c0.z; cs0[3] = c0.w;
           cs1[0] = c1.x; cs1[1] = c1.y; cs1[2] = c1.z; cs1[3] = c1.w;
