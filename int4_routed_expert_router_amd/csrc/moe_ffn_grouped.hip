@@ -655,8 +655,13 @@ __global__ __launch_bounds__(512) void k_gateup_tiles(FfnArgs a) {
 template <int G, int BITS>
 __global__ __launch_bounds__(512) void k_down_tiles(FfnArgs a) {
   constexpr int NQ = BITS / 4;   // 16-byte weight loads per lane and chunk
-  // quads whose weights are in flight (int8 slots are twice as large)
-  constexpr int kDepth = (G == 32 || BITS == 8) ? 2 : 4;
+  // quads whose weights are in flight.  Two, not more: every workgroup
+  // issues its first kDepth quads at once, and the memory system serves all
+  // of them interleaved, so a workgroup's first quad is complete only when
+  // nearly the whole chip-wide burst has arrived; a deeper start only delays
+  // the first products (measured: first quad done at 8.3 us with 2 in
+  // flight, 12 us with 4), while the steady state is paced by the products.
+  constexpr int kDepth = 2;
   constexpr int kHalves = G == 32 ? 2 : 1;
   __shared__ __attribute__((aligned(16))) uint16_t hsh[2][kSub * kGroupedMaxInter];
   __shared__ __attribute__((aligned(16))) uint16_t hsl[2][kSub * kGroupedMaxInter];
@@ -852,16 +857,8 @@ __global__ __launch_bounds__(512) void k_down_tiles(FfnArgs a) {
   for (; sb0 + kDepth <= s1; sb0 += kDepth) {
     process(sb0, Half<0>{});
     process(sb0 + 1, Half<1>{});
-    if constexpr (kDepth == 4) {
-      process(sb0 + 2, Half<2>{});
-      process(sb0 + 3, Half<3>{});
-    }
   }
   if (sb0 < s1) process(sb0, Half<0>{});
-  if constexpr (kDepth == 4) {
-    if (sb0 + 1 < s1) process(sb0 + 1, Half<1>{});
-    if (sb0 + 2 < s1) process(sb0 + 2, Half<2>{});
-  }
 }
 
 hipError_t launch_gateup_grouped(int act, const FfnArgs& a, hipStream_t s) {
