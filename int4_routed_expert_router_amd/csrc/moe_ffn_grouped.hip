@@ -652,7 +652,7 @@ __global__ __launch_bounds__(512) void k_gateup_tiles(FfnArgs a) {
 // switch).  The second wave's partial goes through LDS; the first adds it and
 // stores yrow (unweighted, fp32).
 // ---------------------------------------------------------------------------
-template <int G, int BITS>
+template <int G, int BITS, bool FULL>
 __global__ __launch_bounds__(512) void k_down_tiles(FfnArgs a) {
   constexpr int NQ = BITS / 4;   // 16-byte weight loads per lane and chunk
   // quads whose weights are in flight.  Two, not more: every workgroup
@@ -671,8 +671,10 @@ __global__ __launch_bounds__(512) void k_down_tiles(FfnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, kb = lane >> 4;
   const int q4 = wave & 3, kh = wave >> 2;
-  const int H = a.H, n_pairs = H / 32;
+  const int H = FULL ? kGroupedMaxH : a.H, n_pairs = H / 32;
   const int qpu = (n_pairs + 3) / 4;   // quads per unit
+  // reduction width of a unit's expert (I or I_s)
+  auto inter_of = [&](int expert) { return FULL ? kGroupedMaxInter : (expert < 0 ? a.Is : a.I); };
   const int n_units = load_uniform(a.n_units) + load_uniform(a.n_units + 1);
   const int Q = n_units * qpu, lw = logical_wg();
   const int s0 = static_cast<int>((static_cast<long long>(lw) * Q) >> kGridTilesLog2);
@@ -688,16 +690,16 @@ __global__ __launch_bounds__(512) void k_down_tiles(FfnArgs a) {
   const int ex0 = hd0.expert;
   int su = xu;
   const uint8_t* sblob = expert_blob(a, ex0);
-  int sI = ex0 < 0 ? a.Is : a.I;
+  int sI = inter_of(ex0);
   // weights of this wave's tile of quad q (pair-tile clamped to the last one)
   auto tile_src = [&](int q, const uint4*& qb, const uint8_t*& sb, int& ncq) {
     const int u = q / qpu;
-    const int pt = min((q - u * qpu) * 4 + q4, n_pairs - 1);
+    const int pt = FULL ? (q - u * qpu) * 4 + q4 : min((q - u * qpu) * 4 + q4, n_pairs - 1);
     if (u != su) {
       const UnitHdr hd = unit_hdr(a.units, u);
       su = u;
       sblob = expert_blob(a, hd.expert);
-      sI = hd.expert < 0 ? a.Is : a.I;
+      sI = inter_of(hd.expert);
     }
     ncq = sI / 64;
     qb = reinterpret_cast<const uint4*>(sblob + blob_d_q(H, sI, BITS)) + static_cast<size_t>(pt) * ncq * 64 * NQ + lane;
@@ -731,7 +733,7 @@ __global__ __launch_bounds__(512) void k_down_tiles(FfnArgs a) {
   int hb = 0;
   const bool two = (s1 - 1) / qpu > u_first;
   const UnitHdr hd1 = two ? unit_hdr(a.units, u_first + 1) : hd0;
-  const int I1 = hd1.expert < 0 ? a.Is : a.I;
+  const int I1 = inter_of(hd1.expert);
   if (tid < kSub) {
     urow[0][tid] = row0 + tid;
     urow[1][tid] = hd1.row0 + tid;
@@ -749,7 +751,7 @@ __global__ __launch_bounds__(512) void k_down_tiles(FfnArgs a) {
     int ncq;
     tile_src(min(s0 + hf, s1 - 1), qb, sb, ncq);
 #pragma unroll
-    for (int j = 0; j < kSlot; ++j) load_slot<G, BITS>(sl[hf * kSlot + j], qb, sb, min(kh + 2 * j, ncq - 1));
+    for (int j = 0; j < kSlot; ++j) load_slot<G, BITS>(sl[hf * kSlot + j], qb, sb, FULL ? kh + 2 * j : min(kh + 2 * j, ncq - 1));
   }
   // the weight loads just issued may stay in flight; the staging before them may not
   staged_barrier<kDepth * kSlot * kLoadsPerSlot<G, BITS>>();
@@ -762,7 +764,7 @@ __global__ __launch_bounds__(512) void k_down_tiles(FfnArgs a) {
     const int pt = (q - u * qpu) * 4 + q4;
     if (u != xu) {
       const UnitHdr hd = unit_hdr(a.units, u);
-      const int Iu = hd.expert < 0 ? a.Is : a.I;
+      const int Iu = inter_of(hd.expert);
       hb = (u - u_first) & 1;
       if (u > u_first + 1) {
         // not staged yet: wait until the readers of unit u - 2 (same buffer)
@@ -802,10 +804,10 @@ __global__ __launch_bounds__(512) void k_down_tiles(FfnArgs a) {
       const int c = kh + 2 * j;
       Slot& s = sl[hf * kSlot + j];
       const Decoded d = decode_slot<G, BITS>(s);
-      load_slot<G, BITS>(s, qnx, snx, min(c, ncn - 1));
+      load_slot<G, BITS>(s, qnx, snx, FULL ? c : min(c, ncn - 1));
       Prod p;
       float cs0[4], cs1[4];
-      if (c < nc) {
+      if (FULL || c < nc) {
         const uint4 h0 = *reinterpret_cast<const uint4*>(ha0 + 64 * c);
         const uint4 h1 = *reinterpret_cast<const uint4*>(ha1 + 64 * c);
         const uint4 l0 = *reinterpret_cast<const uint4*>(la0 + 64 * c);
@@ -821,7 +823,7 @@ __global__ __launch_bounds__(512) void k_down_tiles(FfnArgs a) {
         }
         p = chunk_mfma<G, true>(d, h0, h1, l0, l1);
       }
-      if (j > 0 && c - 2 < nc) chunk_scale<G>(pp, pk, pcs0, pcs1, accA, accB, biasA, biasB);
+      if (j > 0 && (FULL || c - 2 < nc)) chunk_scale<G>(pp, pk, pcs0, pcs1, accA, accB, biasA, biasB);
       pp = p;
       pk = coef_of(d);
 #pragma unroll
@@ -830,7 +832,7 @@ __global__ __launch_bounds__(512) void k_down_tiles(FfnArgs a) {
         pcs1[i] = cs1[i];
       }
     }
-    if (kh + 2 * (kSlot - 1) < nc) chunk_scale<G>(pp, pk, pcs0, pcs1, accA, accB, biasA, biasB);
+    if (FULL || kh + 2 * (kSlot - 1) < nc) chunk_scale<G>(pp, pk, pcs0, pcs1, accA, accB, biasA, biasB);
     (void)kHalves;
     constexpr int rb = hf & 1;
     if (kh == 1) {
@@ -841,7 +843,7 @@ __global__ __launch_bounds__(512) void k_down_tiles(FfnArgs a) {
       }
     }
     __syncthreads();
-    if (kh == 0 && pt < n_pairs) {
+    if (kh == 0 && (FULL || pt < n_pairs)) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = 4 * kb + i;
@@ -859,6 +861,12 @@ __global__ __launch_bounds__(512) void k_down_tiles(FfnArgs a) {
     process(sb0 + 1, Half<1>{});
   }
   if (sb0 < s1) process(sb0, Half<0>{});
+}
+
+// the family's largest shape, for which the down kernel drops its bounds
+// tests (FULL: every chunk and pair-tile index it forms is in range)
+static bool full_shape(const FfnArgs& a) {
+  return a.H == kGroupedMaxH && a.I == kGroupedMaxInter && (a.Is == kGroupedMaxInter || a.Is == 0);
 }
 
 hipError_t launch_gateup_grouped(int act, const FfnArgs& a, hipStream_t s) {
@@ -882,9 +890,15 @@ hipError_t launch_gateup_grouped(int act, const FfnArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_down_grouped(const FfnArgs& a, hipStream_t s) {
-#define DN_LAUNCH(G_, B_) hipLaunchKernelGGL((k_down_tiles<G_, B_>), dim3(kGridTiles), dim3(512), 0, s, a)
+  const bool full = full_shape(a);
+#define DN_LAUNCH(G_, B_)                                                                            \
+  do {                                                                                               \
+    if (full) hipLaunchKernelGGL((k_down_tiles<G_, B_, true>), dim3(kGridTiles), dim3(512), 0, s, a); \
+    else hipLaunchKernelGGL((k_down_tiles<G_, B_, false>), dim3(kGridTiles), dim3(512), 0, s, a);     \
+  } while (0)
   if (a.bits == 8) {
-    if (a.G == 32) DN_LAUNCH(32, 8);
+    // group 32 with int8 keeps the generic form (the FULL one needs scratch)
+    if (a.G == 32) hipLaunchKernelGGL((k_down_tiles<32, 8, false>), dim3(kGridTiles), dim3(512), 0, s, a);
     else if (a.G == 64) DN_LAUNCH(64, 8);
     else DN_LAUNCH(128, 8);
   } else {
