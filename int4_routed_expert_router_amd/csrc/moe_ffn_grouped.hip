@@ -366,7 +366,7 @@ __device__ __forceinline__ void staged_barrier() {
 // (columns with (col & 2) != 0 scaled by 1/16), at rows row0.., columns
 // 16 pt.., and hsum[row][pt] = sum over the 16 columns of h (hi + lo).
 // ---------------------------------------------------------------------------
-template <int ACT, int G, int BITS>
+template <int ACT, int G, int BITS, bool FULL>
 __global__ __launch_bounds__(512) void k_gateup_tiles(FfnArgs a) {
   constexpr int NQ = BITS / 4;   // 16-byte weight loads per lane and chunk
   // tiles are processed in pairs (one barrier per pair); the two tiles of a
@@ -564,8 +564,8 @@ __global__ __launch_bounds__(512) void k_gateup_tiles(FfnArgs a) {
       const Decoded d = decode_slot<G, BITS>(s);
       load_slot<G, BITS>(s, qnx, snx, min(c, nc - 1));
       Prod p;
-      if (c < nc) p = chunk_mfma<G, false>(d, xa[j][0], xa[j][1], xa[j][0], xa[j][1]);
-      if (j > 0 && c - kWaves < nc) {
+      if (FULL || c < nc) p = chunk_mfma<G, false>(d, xa[j][0], xa[j][1], xa[j][0], xa[j][1]);
+      if (j > 0 && (FULL || c - kWaves < nc)) {
         float s0[4], s1[4];
         sums_of(j - 1, 0, s0);
         sums_of(j - 1, kHalves - 1, s1);
@@ -574,7 +574,7 @@ __global__ __launch_bounds__(512) void k_gateup_tiles(FfnArgs a) {
       pp = p;
       pk = coef_of(d);
     }
-    if (wave + kWaves * (kSlot - 1) < nc) {
+    if (FULL || wave + kWaves * (kSlot - 1) < nc) {
       float s0[4], s1[4];
       sums_of(kSlot - 1, 0, s0);
       sums_of(kSlot - 1, kHalves - 1, s1);
@@ -870,7 +870,12 @@ static bool full_shape(const FfnArgs& a) {
 }
 
 hipError_t launch_gateup_grouped(int act, const FfnArgs& a, hipStream_t s) {
-#define GU_LAUNCH(A_, G_, B_) hipLaunchKernelGGL((k_gateup_tiles<A_, G_, B_>), dim3(kGridTiles), dim3(512), 0, s, a)
+  const bool full = a.H == kGroupedMaxH;
+#define GU_LAUNCH(A_, G_, B_)                                                                              \
+  do {                                                                                                     \
+    if (full) hipLaunchKernelGGL((k_gateup_tiles<A_, G_, B_, true>), dim3(kGridTiles), dim3(512), 0, s, a); \
+    else hipLaunchKernelGGL((k_gateup_tiles<A_, G_, B_, false>), dim3(kGridTiles), dim3(512), 0, s, a);     \
+  } while (0)
 #define GU_G(A_, B_)                      \
   do {                                    \
     if (a.G == 32) GU_LAUNCH(A_, 32, B_); \
