@@ -136,6 +136,16 @@ def test_batched_layer_full_size(path):
     print(f"bat80 path {path}: max err {worst:.3e} (tol {tol:.3e}), near ties {flagged}")
 
 
+def test_grouped_ranges_over_many_units():
+    # 4096 tokens of the tiny layer: 775 units of 16 rows, so every grouped
+    # workgroup's range crosses several units (about 12 gate/up pair-tiles of
+    # 4 per unit, about 6 down quads of 2 per unit: the down kernel restages h
+    # into a buffer it used two units before)
+    wl = dataclasses.replace(synth.TINY, name="tiny_t4096", tokens=4096, token_seed=114)
+    worst, tol, flagged = check_layer(wl, 2)
+    print(f"tiny, 4096 tokens, grouped: max err {worst:.3e} (tol {tol:.3e}), near ties {flagged}")
+
+
 def test_exact_ties_pick_lower_index():
     import torch
     from int4_routed_expert_router_amd import api
