@@ -133,7 +133,7 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ to
   __shared__ int start[kMaxExperts];
   __shared__ int run[kMaxExperts];
   __shared__ int ubase[kMaxExperts];
-  __shared__ unsigned short wcnt[kMaxExperts][16];   // rows of expert e in wave w of a chunk
+  __shared__ __attribute__((aligned(16))) unsigned short wcnt[kMaxExperts][16];   // rows of expert e in wave w of a chunk
   __shared__ int2 scan_tmp[16];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -197,8 +197,17 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ to
     if (first_peer) wcnt[e][wave] = static_cast<unsigned short>(__popcll(peers));
     __syncthreads();
     if (valid) {
+      // rows of expert e in the waves before this one: the 16 counts of the
+      // expert are read as two 16-byte words and the first `wave` added
+      const uint4 c_lo = *reinterpret_cast<const uint4*>(&wcnt[e][0]);
+      const uint4 c_hi = *reinterpret_cast<const uint4*>(&wcnt[e][8]);
+      const uint32_t cw[8] = {c_lo.x, c_lo.y, c_lo.z, c_lo.w, c_hi.x, c_hi.y, c_hi.z, c_hi.w};
       int before = 0;
-      for (int w = 0; w < wave; ++w) before += wcnt[e][w];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        before += 2 * q < wave ? static_cast<int>(cw[q] & 0xFFFFu) : 0;
+        before += 2 * q + 1 < wave ? static_cast<int>(cw[q] >> 16) : 0;
+      }
       const int r = run[e] + before + rank;   // rank among all rows of expert e
       const int pos = start[e] + r;
       perm[pos] = i;
