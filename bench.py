@@ -419,6 +419,16 @@ def main():
             step()
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t_start
+        # per-step spread, outside the timed region: HIP events on the step's
+        # stream around each of another K steps
+        step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.steps)]
+        for b_ev, e_ev in step_ev:
+            b_ev.record(stream)
+            step()
+            e_ev.record(stream)
+        torch.cuda.synchronize()
+        step_ms = np.array([b_ev.elapsed_time(e_ev) for b_ev, e_ev in step_ev])
     ms_per_step = 1e3 * elapsed / args.steps
     tokens_s = wl.tokens * args.steps / elapsed
     act = st.active_experts()
@@ -480,6 +490,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "step_ms": {"median": round(float(np.median(step_ms)), 4), "p10": round(float(np.percentile(step_ms, 10)), 4),
+                    "p90": round(float(np.percentile(step_ms, 90)), 4),
+                    "events": "HIP events around each step on its stream, a second pass of the same K steps"},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
