@@ -365,6 +365,8 @@ __device__ __forceinline__ void staged_barrier() {
 // Output: h as fp16 hi and lo planes, operand-ready for the down projection
 // (columns with (col & 2) != 0 scaled by 1/16), at rows row0.., columns
 // 16 pt.., and hsum[row][pt] = sum over the 16 columns of h (hi + lo).
+// FULL: H is the family's largest (2048, 32 chunks), so every chunk w + 8 j
+// a wave forms is in range and the product loop carries no range tests.
 // ---------------------------------------------------------------------------
 template <int ACT, int G, int BITS, bool FULL>
 __global__ __launch_bounds__(512) void k_gateup_tiles(FfnArgs a) {
