@@ -136,6 +136,17 @@ def test_batched_layer_full_size(path):
     print(f"bat80 path {path}: max err {worst:.3e} (tol {tol:.3e}), near ties {flagged}")
 
 
+@pytest.mark.parametrize("n_tokens", [17, 128])
+def test_batched_layer_full_size_other_batches(n_tokens):
+    # the full 2048/512 shape (the shape-specialised grouped kernels) at other
+    # batch sizes: 17 tokens leave a one-row shared unit and mostly one-row
+    # experts, 128 tokens give hot experts up to eight units
+    wl = synth.BAT80
+    x_bits = synth.tokens(wl, n_tokens=n_tokens, seed=wl.token_seed + n_tokens)
+    worst, tol, flagged = check_layer(wl, 2, layer=11, x_bits=x_bits)
+    print(f"bat80 shape, {n_tokens} tokens, grouped: max err {worst:.3e} (tol {tol:.3e}), near ties {flagged}")
+
+
 def test_grouped_ranges_over_many_units():
     # 4096 tokens of the tiny layer: 775 units of 16 rows, so every grouped
     # workgroup's range crosses several units (about 12 gate/up pair-tiles of
