@@ -62,7 +62,15 @@ enum { MOE_F16 = 1, MOE_BF16 = 2 };
  * (matrix-core) family when the batch has more than MOE_GEMV_MAX_ROWS
  * routed rows (T*K) and the shape fits it (hidden <= 2048, inter and
  * shared_inter <= 512), the per-row GEMV family otherwise.  Asking for
- * GROUPED with a shape beyond those limits is MOE_ESHAPE. */
+ * GROUPED with a shape beyond those limits is MOE_ESHAPE.
+ *
+ * Range of the grouped family: its matrix-core operands are fp16, so every
+ * activation x and every SwiGLU output h must round to a finite fp16 value
+ * (|v| < 65520; bf16 activations are exact in fp16 inside that range).  A
+ * value outside it (or a non-finite input) makes that call's results
+ * invalid; the call then sets MOE_FLAG_F16_RANGE in its status word (see
+ * moe_workspace_status).  The GEMV family has no such limit (bf16 and fp16
+ * activations enter its products exactly; h is fp32). */
 enum { MOE_PATH_AUTO = 0, MOE_PATH_GEMV = 1, MOE_PATH_GROUPED = 2 };
 #define MOE_GEMV_MAX_ROWS 32
 
@@ -166,6 +174,21 @@ moe_status moe_pack_expert(int32_t hidden, int32_t inter, int32_t group_size,
  * and the stack calls for n_tokens tokens (256-byte aligned base). */
 moe_status moe_workspace_bytes(const moe_layer_desc* desc, int32_t n_tokens, size_t* bytes);
 
+/* Status word of a call.  moe_expert_ffn, moe_layer_forward,
+ * moe_stack_forward (and its graphs) and moe_pool_decode_step clear a
+ * uint32 status word inside the workspace at their start (in their first
+ * FFN kernel) and their kernels set flags in it:
+ *   MOE_FLAG_F16_RANGE  a grouped-family operand (an activation or a SwiGLU
+ *                       output) fell outside the fp16 range: the outputs of
+ *                       the call are not valid (run such inputs with
+ *                       MOE_PATH_GEMV).
+ * moe_workspace_status returns the byte offset of the word in a workspace
+ * laid out for (desc, n_tokens); read it (device memory) after the call's
+ * stream has been synchronised.  Calls that overlap on one workspace race on
+ * it, as they do on the rest of the workspace. */
+#define MOE_FLAG_F16_RANGE 1u
+moe_status moe_workspace_status(const moe_layer_desc* desc, int32_t n_tokens, size_t* offset);
+
 /* Router GEMV (shared-gate row fused), top-K with lower-index tie-break,
  * renormalised weights and sigmoid shared gate (the routing step of the
  * how-it-works list).  x: device [T][H] act_dtype (16-byte aligned rows).
@@ -248,7 +271,12 @@ void moe_graph_destroy(moe_graph* g);
  * begin[l] and end[l] (hipEvent_t handles created by the caller with timing
  * enabled) are recorded on the stream right before and right after layer l's
  * kernel of the chosen kind (MOE_TIME_*).  n_layers = 0 disables it.  The
- * setting is read when the stack is enqueued or captured. */
+ * setting is read when the stack is enqueued or captured.  The events stay
+ * owned by the caller and are only borrowed: they must remain valid while
+ * the setting is in force on this thread (until it is cleared with
+ * n_layers = 0), until every stack call enqueued with them has run, and for
+ * the whole life of any graph captured with them (each replay records into
+ * them). */
 enum { MOE_TIME_GATEUP = 0, MOE_TIME_DOWN = 1, MOE_TIME_ROUTER = 2 };
 moe_status moe_stack_set_kernel_events(void* const* begin, void* const* end, int32_t n_layers, int32_t kind);
 

@@ -16,6 +16,7 @@ MOE_GEMV_MAX_ROWS = 32
 MOE_POOL_HOST_ONLY = 1
 MOE_POOL_DMA_COPY = 2
 MOE_TIME_GATEUP, MOE_TIME_DOWN, MOE_TIME_ROUTER = 0, 1, 2
+MOE_FLAG_F16_RANGE = 1
 
 STATUS_NAMES = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_ESHAPE", -3: "MOE_EWORKSPACE", -4: "MOE_EHIP",
                 -5: "MOE_EPOOLFULL", -6: "MOE_EBUSY", -7: "MOE_ENOMEM"}
@@ -66,6 +67,7 @@ PROTOS = {
     "moe_blob_bytes_q": (u64, [i32, i32, i32, i32]),
     "moe_pack_expert_q": (i32, [i32, i32, i32, i32] + [vp] * 10),
     "moe_workspace_bytes": (i32, [vp, i32, C.POINTER(C.c_size_t)]),
+    "moe_workspace_status": (i32, [vp, i32, C.POINTER(C.c_size_t)]),
     "moe_route": (i32, [vp, vp, vp, i32, vp, vp, vp, vp, vp, C.c_size_t, vp]),
     "moe_permute": (i32, [vp, vp, i32, vp, vp, vp, vp, C.c_size_t, vp]),
     "moe_expert_ffn": (i32, [vp, vp, vp, i32, vp, vp, vp, vp, vp, C.c_size_t, vp]),

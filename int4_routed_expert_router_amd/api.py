@@ -16,16 +16,38 @@ import torch
 from ._lib import (GdnDesc, MOE_BF16, MOE_F16, MOE_PATH_AUTO, MOE_POOL_DMA_COPY, MOE_POOL_HOST_ONLY, LayerDesc,  # noqa: F401
                    LayerWeights, SlotPoolConfig, SlotPoolStats, check, lib)
 
-__all__ = ["Desc", "Layer", "blob_bytes", "pack_expert", "workspace_bytes", "workspace", "route", "permute",
+__all__ = ["Desc", "Layer", "blob_bytes", "pack_expert", "workspace_bytes", "workspace", "workspace_status",
+           "route", "permute",
            "expert_ffn", "layer_forward", "stack_epilogue", "stack_forward", "StackGraph", "synth_fill_experts",
            "synth_philox", "SlotPool", "pool_decode_step", "gdn_step"]
 
 
-def _ptr(t):
+_ACT_DTYPES = (torch.int16, torch.float16, torch.bfloat16)
+
+
+def _ptr(t, name="tensor", dtypes=None, numel=None, host=False):
+    """Address of a tensor for the C ABI, after checking that it is where the
+    call reads it (a CUDA tensor, or with host=True a CPU tensor),
+    contiguous, of an accepted dtype and, when given, of numel elements.
+    None stays NULL; a plain int is taken as an address the caller vouches
+    for."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch tensor, got {type(t).__name__}")
+    if host:
+        if t.device.type != "cpu":
+            raise ValueError(f"{name} must be a host (CPU) tensor, got {t.device}")
+    elif t.device.type != "cuda":
+        raise ValueError(f"{name} must be a CUDA tensor, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
     return t.data_ptr()
 
 
@@ -33,6 +55,31 @@ def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _scratch(desc, T, device, stream):
+    """A temporary workspace for one call.  It is allocated on the current
+    stream; when the call runs on another torch stream the tensor is recorded
+    on that stream too, so the caching allocator does not hand its memory out
+    again before the call's kernels have finished with it."""
+    if stream is not None and not isinstance(stream, torch.cuda.Stream):
+        raise ValueError("pass ws explicitly when stream is a raw stream handle")
+    ws = workspace(desc, T, device)
+    if stream is not None and stream != torch.cuda.current_stream(ws.device):
+        ws.record_stream(stream)
+    return ws
+
+
+def _tokens(x, desc, name="x"):
+    if not isinstance(x, torch.Tensor) or x.dim() < 1:
+        raise ValueError(f"{name} must be a [T, H] tensor")
+    T = x.shape[0]
+    _ptr(x, name, _ACT_DTYPES, T * desc.hidden)
+    return T
+
+
+def _ws(ws):
+    return _ptr(ws, "ws", (torch.uint8,))
 
 
 @dataclasses.dataclass(frozen=True)
@@ -74,8 +121,11 @@ class Layer:
         self.expert_stride, self.expert_offset, self.shared = int(expert_stride), expert_offset, shared
 
     def c(self) -> LayerWeights:
-        return LayerWeights(_ptr(self.router_w), _ptr(self.router_bias), _ptr(self.experts), self.expert_stride,
-                            _ptr(self.expert_offset), _ptr(self.shared))
+        return LayerWeights(_ptr(self.router_w, "router_w", (torch.int16, torch.float16)),
+                            _ptr(self.router_bias, "router_bias", (torch.float32,)),
+                            _ptr(self.experts, "experts", (torch.uint8,)), self.expert_stride,
+                            _ptr(self.expert_offset, "expert_offset", (torch.int64,)),
+                            _ptr(self.shared, "shared", (torch.uint8,)))
 
 
 def blob_bytes(hidden: int, inter: int, group: int, bits: int = 4) -> int:
@@ -105,41 +155,64 @@ def workspace(desc: Desc, n_tokens: int, device="cuda") -> torch.Tensor:
     return torch.empty(max(workspace_bytes(desc, n_tokens), 256), dtype=torch.uint8, device=device)
 
 
+def workspace_status(desc: Desc, n_tokens: int, ws: torch.Tensor) -> int:
+    """The status word (MOE_FLAG_* bits) the last call on ws left in it; the
+    caller synchronises the call's stream first."""
+    off = C.c_size_t(0)
+    d = desc.c()
+    check(lib().moe_workspace_status(C.byref(d), n_tokens, C.byref(off)))
+    o = int(off.value)
+    return int(ws[o:o + 4].view(torch.int32).item()) & 0xFFFFFFFF
+
+
+_I32, _F32 = (torch.int32,), (torch.float32,)
+
+
 def route(desc, layer, x, topk_idx, topk_w, shared_gate=None, logits=None, ws=None, stream=None):
+    T = _tokens(x, desc)
+    K, E = desc.top_k, desc.n_experts
+    args = (_ptr(x), T, _ptr(topk_idx, "topk_idx", _I32, T * K), _ptr(topk_w, "topk_w", _F32, T * K),
+            _ptr(shared_gate, "shared_gate", _F32, T), _ptr(logits, "logits", _F32, T * (E + 1)))
     d, w = desc.c(), layer.c()
-    T = x.shape[0]
-    ws = workspace(desc, T, x.device) if ws is None else ws
-    check(lib().moe_route(C.byref(d), C.byref(w), _ptr(x), T, _ptr(topk_idx), _ptr(topk_w), _ptr(shared_gate),
-                          _ptr(logits), _ptr(ws), ws.numel(), _stream(stream)))
+    ws = _scratch(desc, T, x.device, stream) if ws is None else ws
+    check(lib().moe_route(C.byref(d), C.byref(w), *args, _ws(ws), ws.numel(), _stream(stream)))
 
 
 def permute(desc, topk_idx, expert_off, perm, inv=None, ws=None, stream=None):
-    d = desc.c()
     T = topk_idx.shape[0]
-    ws = workspace(desc, T, topk_idx.device) if ws is None else ws
-    check(lib().moe_permute(C.byref(d), _ptr(topk_idx), T, _ptr(expert_off), _ptr(perm), _ptr(inv), _ptr(ws),
-                            ws.numel(), _stream(stream)))
+    K, E = desc.top_k, desc.n_experts
+    args = (_ptr(topk_idx, "topk_idx", _I32, T * K), T, _ptr(expert_off, "expert_off", _I32, E + 1),
+            _ptr(perm, "perm", _I32, T * K), _ptr(inv, "inv", _I32, T * K))
+    d = desc.c()
+    ws = _scratch(desc, T, topk_idx.device, stream) if ws is None else ws
+    check(lib().moe_permute(C.byref(d), *args, _ws(ws), ws.numel(), _stream(stream)))
 
 
 def expert_ffn(desc, layer, x, topk_idx, topk_w, shared_gate, y, ws=None, stream=None):
+    T = _tokens(x, desc)
+    K, H = desc.top_k, desc.hidden
+    args = (_ptr(x), T, _ptr(topk_idx, "topk_idx", _I32, T * K), _ptr(topk_w, "topk_w", _F32, T * K),
+            _ptr(shared_gate, "shared_gate", _F32, T), _ptr(y, "y", _F32, T * H))
     d, w = desc.c(), layer.c()
-    T = x.shape[0]
-    ws = workspace(desc, T, x.device) if ws is None else ws
-    check(lib().moe_expert_ffn(C.byref(d), C.byref(w), _ptr(x), T, _ptr(topk_idx), _ptr(topk_w), _ptr(shared_gate),
-                               _ptr(y), _ptr(ws), ws.numel(), _stream(stream)))
+    ws = _scratch(desc, T, x.device, stream) if ws is None else ws
+    check(lib().moe_expert_ffn(C.byref(d), C.byref(w), *args, _ws(ws), ws.numel(), _stream(stream)))
 
 
 def layer_forward(desc, layer, x, y, topk_idx=None, topk_w=None, shared_gate=None, ws=None, stream=None):
+    T = _tokens(x, desc)
+    K, H = desc.top_k, desc.hidden
+    args = (_ptr(x), T, _ptr(y, "y", _F32, T * H), _ptr(topk_idx, "topk_idx", _I32, T * K),
+            _ptr(topk_w, "topk_w", _F32, T * K), _ptr(shared_gate, "shared_gate", _F32, T))
     d, w = desc.c(), layer.c()
-    T = x.shape[0]
-    ws = workspace(desc, T, x.device) if ws is None else ws
-    check(lib().moe_layer_forward(C.byref(d), C.byref(w), _ptr(x), T, _ptr(y), _ptr(topk_idx), _ptr(topk_w),
-                                  _ptr(shared_gate), _ptr(ws), ws.numel(), _stream(stream)))
+    ws = _scratch(desc, T, x.device, stream) if ws is None else ws
+    check(lib().moe_layer_forward(C.byref(d), C.byref(w), *args, _ws(ws), ws.numel(), _stream(stream)))
 
 
 def stack_epilogue(desc, y, r, x_next, stream=None):
+    T, H = y.shape[0], desc.hidden
+    args = (T, _ptr(y, "y", _F32, T * H), _ptr(r, "r", _F32, T * H), _ptr(x_next, "x_next", _ACT_DTYPES, T * H))
     d = desc.c()
-    check(lib().moe_stack_epilogue(C.byref(d), y.shape[0], _ptr(y), _ptr(r), _ptr(x_next), _stream(stream)))
+    check(lib().moe_stack_epilogue(C.byref(d), *args, _stream(stream)))
 
 
 def _layer_array(layers):
@@ -147,13 +220,21 @@ def _layer_array(layers):
     return arr
 
 
+def _stack_args(desc, n_layers, x0, r, x_buf, ws, x_all, y_all, idx_all, w_all, gamma_all):
+    T = _tokens(x0, desc, "x0")
+    L, K, H = n_layers, desc.top_k, desc.hidden
+    return (_ptr(x0), T, _ptr(r, "r", _F32, T * H), _ptr(x_buf, "x_buf", _ACT_DTYPES, T * H),
+            _ptr(x_all, "x_all", _ACT_DTYPES, L * T * H), _ptr(y_all, "y_all", _F32, L * T * H),
+            _ptr(idx_all, "idx_all", _I32, L * T * K), _ptr(w_all, "w_all", _F32, L * T * K),
+            _ptr(gamma_all, "gamma_all", _F32, L * T), _ws(ws), ws.numel())
+
+
 def stack_forward(desc, layers, x0, r, x_buf, ws, x_all=None, y_all=None, idx_all=None, w_all=None,
                   gamma_all=None, stream=None):
+    args = _stack_args(desc, len(layers), x0, r, x_buf, ws, x_all, y_all, idx_all, w_all, gamma_all)
     d = desc.c()
     arr = _layer_array(layers)
-    check(lib().moe_stack_forward(C.byref(d), arr, len(layers), _ptr(x0), x0.shape[0], _ptr(r), _ptr(x_buf),
-                                  _ptr(x_all), _ptr(y_all), _ptr(idx_all), _ptr(w_all), _ptr(gamma_all), _ptr(ws),
-                                  ws.numel(), _stream(stream)))
+    check(lib().moe_stack_forward(C.byref(d), arr, len(layers), *args, _stream(stream)))
 
 
 class StackGraph:
@@ -161,13 +242,14 @@ class StackGraph:
 
     def __init__(self, desc, layers, x0, r, x_buf, ws, capture_stream, x_all=None, y_all=None, idx_all=None,
                  w_all=None, gamma_all=None):
+        self._h = None
+        args = _stack_args(desc, len(layers), x0, r, x_buf, ws, x_all, y_all, idx_all, w_all, gamma_all)
         d = desc.c()
         arr = _layer_array(layers)
         h = C.c_void_p()
         self._keep = (layers, x0, r, x_buf, ws, x_all, y_all, idx_all, w_all, gamma_all)
-        check(lib().moe_stack_graph_create(C.byref(d), arr, len(layers), _ptr(x0), x0.shape[0], _ptr(r), _ptr(x_buf),
-                                           _ptr(x_all), _ptr(y_all), _ptr(idx_all), _ptr(w_all), _ptr(gamma_all),
-                                           _ptr(ws), ws.numel(), _stream(capture_stream), C.byref(h)))
+        check(lib().moe_stack_graph_create(C.byref(d), arr, len(layers), *args, _stream(capture_stream),
+                                           C.byref(h)))
         self._h = h
 
     def launch(self, stream=None):
@@ -192,12 +274,19 @@ def pool_decode_step(desc, layers, pool, step, x0, r, x_buf, idx_host, ws, prega
     x_buf [2, H] device, idx_host pinned int32 [2, K], pregate = predictions
     prefetched per layer (0 = none), idx_log optional host int32 numpy array
     [L, 2, K]."""
+    H, K, L = desc.hidden, desc.top_k, len(layers)
+    if idx_log is not None and (not isinstance(idx_log, np.ndarray) or idx_log.dtype != np.int32
+                                or idx_log.size != L * 2 * K or not idx_log.flags.c_contiguous):
+        raise ValueError(f"idx_log must be a contiguous int32 numpy array of {L * 2 * K} elements")
+    args = (_ptr(x0, "x0", _ACT_DTYPES, H), _ptr(r, "r", _F32, H), _ptr(x_buf, "x_buf", _ACT_DTYPES, 2 * H),
+            _ptr(idx_host, "idx_host", _I32, 2 * K, host=True))
+    if isinstance(idx_host, torch.Tensor) and not idx_host.is_pinned():
+        raise ValueError("idx_host must be pinned host memory")
     d = desc.c()
     arr = _layer_array(layers)
     log = None if idx_log is None else idx_log.ctypes.data
-    check(lib().moe_pool_decode_step(C.byref(d), arr, len(layers), pool._h, step, _ptr(x0), _ptr(r), _ptr(x_buf),
-                                     _ptr(idx_host), log, int(pregate), _ptr(ws), ws.numel(),
-                                     _stream(stream)))
+    check(lib().moe_pool_decode_step(C.byref(d), arr, L, pool._h, step, *args, log, int(pregate), _ws(ws),
+                                     ws.numel(), _stream(stream)))
 
 
 def gdn_step(q, k, v, g, beta, state, o, q_scale, act_dtype="bf16", stream=None):
@@ -228,8 +317,12 @@ class SlotPool:
 
     def __init__(self, n_layers, n_experts, slots, aging_period, blob_stride=0, blob_bytes_=0, host_blobs=None,
                  device_slab=None, device_offsets=None, copy_stream=None, host_only=False, dma_copy=False):
-        cfg = SlotPoolConfig(n_layers, n_experts, slots, aging_period, blob_stride, blob_bytes_, _ptr(host_blobs),
-                             _ptr(device_slab), _ptr(device_offsets),
+        if isinstance(host_blobs, torch.Tensor) and not host_only and not host_blobs.is_pinned():
+            raise ValueError("host_blobs must be pinned host memory")
+        cfg = SlotPoolConfig(n_layers, n_experts, slots, aging_period, blob_stride, blob_bytes_,
+                             _ptr(host_blobs, "host_blobs", (torch.uint8,), host=True),
+                             _ptr(device_slab, "device_slab", (torch.uint8,)),
+                             _ptr(device_offsets, "device_offsets", (torch.int64,)),
                              None if copy_stream is None else _stream(copy_stream),
                              (MOE_POOL_HOST_ONLY if host_only else 0) | (MOE_POOL_DMA_COPY if dma_copy else 0))
         h = C.c_void_p()

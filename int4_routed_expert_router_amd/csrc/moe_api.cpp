@@ -94,7 +94,7 @@ moe_status check_weights(const moe_layer_desc* d, const moe_layer_weights* w) {
 size_t al(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct Ws {
-  size_t logits, idx, w, gamma, off, perm, inv, units, nunits, h, hsum, yrow, pre, total;
+  size_t logits, idx, w, gamma, off, perm, inv, units, nunits, h, hsum, yrow, pre, status, total;
 };
 
 Ws layout(const moe_layer_desc* d, int T) {
@@ -117,6 +117,7 @@ Ws layout(const moe_layer_desc* d, int T) {
   s.hsum = o; o += al(rows * (hstride / 16) * 4);
   s.yrow = o; o += al(rows * H * 4);
   s.pre = o; o += al(T * K * 8 + T * 4);   // pre-gated selection: idx, w, gamma
+  s.status = o; o += al(4);                 // status word of the last call (MOE_FLAG_*)
   s.total = o;
   return s;
 }
@@ -178,10 +179,13 @@ struct FusedTopk {
 
 bool fuse_topk(const moe_layer_desc* d, int T) { return !use_grouped(d, T) && d->n_experts <= 512; }
 
+// reset_status: this FFN is the first of the call, so its first kernel clears
+// the call's status word (the grouped gate/up kernel may then set it)
 moe_status do_ffn(const moe_layer_desc* d, const moe_layer_weights* w, const void* x, int T, const int32_t* idx,
                   const float* tw, const float* gamma, float* y, float* r, void* x_next, void* ws, const Ws& L,
-                  hipStream_t s, int layer = -1, const FusedTopk* fz = nullptr) {
+                  hipStream_t s, bool reset_status, int layer = -1, const FusedTopk* fz = nullptr) {
   moe::FfnArgs a{};
+  a.status = at<uint32_t>(ws, L.status);
   a.x = static_cast<const uint16_t*>(x);
   a.topk_idx = idx;
   a.experts = w->experts;
@@ -219,6 +223,7 @@ moe_status do_ffn(const moe_layer_desc* d, const moe_layer_weights* w, const voi
     plan.T = T;
     plan.K = d->top_k;
     plan.shared = d->shared_inter > 0 ? 1 : 0;
+    plan.status_reset = reset_status ? a.status : nullptr;
     e = moe::launch_permute(idx, T * d->top_k, d->n_experts, at<int32_t>(ws, L.off), at<int32_t>(ws, L.perm),
                             at<int32_t>(ws, L.inv), &plan, s);
     if (e != hipSuccess) return hip_fail(e, "permute kernel launch");
@@ -232,6 +237,7 @@ moe_status do_ffn(const moe_layer_desc* d, const moe_layer_weights* w, const voi
     if (e != hipSuccess) return hip_fail(e, "grouped down kernel launch");
     inv = at<int32_t>(ws, L.inv);
   } else {
+    a.status_reset = reset_status ? 1 : 0;
     e = timer_mark(true, MOE_TIME_GATEUP, layer, s);
     if (e == hipSuccess) e = moe::launch_gateup_gemv(d->act_dtype, a, s);
     if (e == hipSuccess) e = timer_mark(false, MOE_TIME_GATEUP, layer, s);
@@ -379,6 +385,15 @@ moe_status moe_workspace_bytes(const moe_layer_desc* d, int32_t n_tokens, size_t
   return ok();
 }
 
+moe_status moe_workspace_status(const moe_layer_desc* d, int32_t n_tokens, size_t* offset) {
+  moe_status st = check_desc(d);
+  if (st) return st;
+  if (n_tokens < 0) return fail(MOE_ESHAPE, "n_tokens=%d < 0", n_tokens);
+  if (!offset) return fail(MOE_EINVAL, "offset is NULL");
+  *offset = layout(d, n_tokens).status;
+  return ok();
+}
+
 moe_status moe_route(const moe_layer_desc* d, const moe_layer_weights* w, const void* x, int32_t T,
                      int32_t* topk_idx, float* topk_w, float* shared_gate, float* logits_or_null, void* ws,
                      size_t ws_bytes, moe_stream stream) {
@@ -426,7 +441,7 @@ moe_status moe_expert_ffn(const moe_layer_desc* d, const moe_layer_weights* w, c
   Ws L;
   if ((st = check_ws(d, T, ws, ws_bytes, L))) return st;
   st = do_ffn(d, w, x, T, topk_idx, topk_w, shared_gate, y, nullptr, nullptr, ws, L,
-              reinterpret_cast<hipStream_t>(stream));
+              reinterpret_cast<hipStream_t>(stream), true);
   return st ? st : ok();
 }
 
@@ -449,11 +464,11 @@ moe_status moe_layer_forward(const moe_layer_desc* d, const moe_layer_weights* w
   if (fuse_topk(d, T)) {
     FusedTopk fz{at<float>(ws, L.logits), {}, idx, tw, gamma};
     if ((st = do_router(d, w, x, T, at<float>(ws, L.logits), s, -1, &fz.rp))) return st;
-    if ((st = do_ffn(d, w, x, T, idx, tw, gamma, y, nullptr, nullptr, ws, L, s, -1, &fz))) return st;
+    if ((st = do_ffn(d, w, x, T, idx, tw, gamma, y, nullptr, nullptr, ws, L, s, true, -1, &fz))) return st;
     return ok();
   }
   if ((st = do_route(d, w, x, T, idx, tw, gamma, at<float>(ws, L.logits), nullptr, s))) return st;
-  if ((st = do_ffn(d, w, x, T, idx, tw, gamma, y, nullptr, nullptr, ws, L, s))) return st;
+  if ((st = do_ffn(d, w, x, T, idx, tw, gamma, y, nullptr, nullptr, ws, L, s, true))) return st;
   return ok();
 }
 
@@ -498,11 +513,11 @@ static moe_status stack_enqueue(const moe_layer_desc* d, const moe_layer_weights
     if (fuse_topk(d, T)) {
       FusedTopk fz{at<float>(ws, L.logits), {}, idx, tw, gamma};
       if ((st = do_router(d, &layers[l], xl, T, at<float>(ws, L.logits), s, l, &fz.rp))) return st;
-      if ((st = do_ffn(d, &layers[l], xl, T, idx, tw, gamma, y, r, x_buf, ws, L, s, l, &fz))) return st;
+      if ((st = do_ffn(d, &layers[l], xl, T, idx, tw, gamma, y, r, x_buf, ws, L, s, l == 0, l, &fz))) return st;
       continue;
     }
     if ((st = do_route(d, &layers[l], xl, T, idx, tw, gamma, at<float>(ws, L.logits), nullptr, s, l))) return st;
-    if ((st = do_ffn(d, &layers[l], xl, T, idx, tw, gamma, y, r, x_buf, ws, L, s, l))) return st;
+    if ((st = do_ffn(d, &layers[l], xl, T, idx, tw, gamma, y, r, x_buf, ws, L, s, l == 0, l))) return st;
   }
   return MOE_OK;
 }
@@ -621,7 +636,7 @@ moe_status moe_pool_decode_step(const moe_layer_desc* d, const moe_layer_weights
     if (pre && (st = slotpool_prefetch(pool, l + 1, idx_host + K, n_pre, step, compute, nullptr, nullptr, nullptr,
                                        nullptr)))
       return fail_layer(st, "prefetch, layer", l + 1);
-    if ((st = do_ffn(d, &w, xl, 1, idx, tw, gamma, nullptr, r, xn, ws, L, s))) return st;
+    if ((st = do_ffn(d, &w, xl, 1, idx, tw, gamma, nullptr, r, xn, ws, L, s, l == 0))) return st;
     if ((st = slotpool_release(pool, l, compute))) return fail_layer(st, "release, layer", l);
   }
   return ok();

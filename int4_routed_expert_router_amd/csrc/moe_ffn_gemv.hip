@@ -90,6 +90,7 @@ __global__ __launch_bounds__(64 * kGemvGateUpWaves) void k_gateup_gemv(FfnArgs a
   const int p = blockIdx.y, z = blockIdx.z;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (a.status_reset && j == 0 && p == 0 && z == 0 && threadIdx.x == 0) *a.status = 0u;
   if constexpr (KJ > 0) {
     __shared__ int32_t ssel[kMaxTopK];
     if (j < a.T * a.K) {   // uniform: a routed row

@@ -32,7 +32,8 @@
 //     sum_c (s q_c + b) x_c = s * 2^24 * P + b * sum_c x_c,
 // with the column sums of the unit's activations computed once per unit.
 // Activations become fp16 (bf16 inputs are exact in fp16 within its range;
-// the grouped family needs |x| and |h| below 65504); the SwiGLU output h
+// the grouped family needs |x| and |h| to round below 65520, and the gate/up
+// kernel reports any value that does not in the call's status word); the SwiGLU output h
 // enters the down projection as an fp16 hi + lo pair (22 significant bits),
 // written operand-ready by the gate/up kernel together with the fp32 sums of
 // hi + lo over 16-column blocks for the down kernel's bias term.
@@ -91,11 +92,19 @@ __device__ __forceinline__ float f16_bits_f32(uint32_t b) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(b)));
 }
 
+// Nonzero when either fp16 half of w is an infinity or a NaN (exponent bits
+// all ones): the value did not fit the fp16 operand.
+__device__ __forceinline__ uint32_t f16x2_nonfinite(uint32_t w) {
+  const uint32_t e = w & 0x7C007C00u;
+  return static_cast<uint32_t>((e & 0xFFFFu) == 0x7C00u) | static_cast<uint32_t>((e >> 16) == 0x7C00u);
+}
+
 // A operand from 8 activations (16 bytes, value j at half j): fp16; int4:
 // values 2, 3, 6, 7 scaled by 1/16; int8: unscaled, in the order 0, 2, 1, 3,
-// 4, 6, 5, 7.  Adds the 8 activations to sum.
+// 4, 6, 5, 7.  Adds the 8 activations to sum; sets bad when one of them is
+// outside the fp16 range.
 template <int ACT, int BITS = 4>
-__device__ __forceinline__ uint4 act_operand(uint4 raw, float& sum) {
+__device__ __forceinline__ uint4 act_operand(uint4 raw, float& sum, uint32_t& bad) {
   const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
   uint32_t o[4];
   if constexpr (BITS == 8) {
@@ -120,6 +129,7 @@ __device__ __forceinline__ uint4 act_operand(uint4 raw, float& sum) {
       o[d] = f32_to_f16_bits(v0 * f) | (f32_to_f16_bits(v1 * f) << 16);
     }
   }
+  bad |= f16x2_nonfinite(o[0]) | f16x2_nonfinite(o[1]) | f16x2_nonfinite(o[2]) | f16x2_nonfinite(o[3]);
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
@@ -455,11 +465,12 @@ __global__ __launch_bounds__(512) void k_gateup_tiles(FfnArgs a) {
   // xr -> A operands and the column sums (32-column halves) for the C
   // layout rows
   auto take_x = [&]() {
+    uint32_t bad = 0;
 #pragma unroll
     for (int j = 0; j < kSlot; ++j) {
       float s0 = 0.0f, s1 = 0.0f;
-      xa[j][0] = act_operand<ACT, BITS>(xr[j][0], s0);
-      xa[j][1] = act_operand<ACT, BITS>(xr[j][1], s1);
+      xa[j][0] = act_operand<ACT, BITS>(xr[j][0], s0, bad);
+      xa[j][1] = act_operand<ACT, BITS>(xr[j][1], s1, bad);
       float hs[kHalves];
       if constexpr (G == 32) {
         hs[0] = s0;
@@ -485,6 +496,7 @@ __global__ __launch_bounds__(512) void k_gateup_tiles(FfnArgs a) {
         }
       }
     }
+    if (bad) atomicOr(a.status, kStatusF16Range);
     xu = pu;
     row0 = prow0;
     mc = pmc;
@@ -618,6 +630,7 @@ __global__ __launch_bounds__(512) void k_gateup_tiles(FfnArgs a) {
       // sum over the 16 columns of this row of the tile (one 16-lane DPP row)
       hs = __uint_as_float(dpp_row_sum(__float_as_uint(hs)));
       if (m < o.mc) {
+        if ((hi & 0x7C00u) == 0x7C00u) atomicOr(a.status, kStatusF16Range);   // h outside the fp16 range
         const int col = BITS == 8 ? h8_col(nn) : nn;
         const size_t off = static_cast<size_t>(o.row0 + m) * a.hstride + 16 * o.pt + col;
         h_hi[off] = static_cast<uint16_t>(hi);

@@ -33,7 +33,7 @@ struct FfnArgs {
   float* hsum;                // [rows][hstride/16] sums of h over 16-column blocks
   int T, H, K, I, Is, G, E;
   int hstride;                // max(I, Is)
-  int bits;                   // expert weight width, 4 or 8 (8: GEMV family only)
+  int bits;                   // expert weight width, 4 or 8
   // GEMV family with top-K fused into gate/up (route_part != nullptr): every
   // routed row's workgroups select the token's experts from the router's
   // logit slices themselves; one workgroup per token (rank 0, pair-tile 0,
@@ -44,7 +44,14 @@ struct FfnArgs {
   int32_t* sel_idx;
   float* sel_w;
   float* sel_gamma;
+  // status word of the call (workspace): with status_reset the GEMV gate/up
+  // kernel clears it (the grouped family clears it in the bucketing kernel);
+  // the grouped gate/up kernel sets kStatusF16Range when an activation or a
+  // SwiGLU output does not fit its fp16 matrix-core operand
+  uint32_t* status;
+  int status_reset;
 };
+constexpr uint32_t kStatusF16Range = 1u;
 
 // Units of the grouped family, written by the bucketing kernel.  A unit is up
 // to 16 rows of one expert: the shared expert's units come first (rows
@@ -57,6 +64,7 @@ struct UnitPlan {
   int32_t* n_units;
   int T, K;
   int shared;                 // 1 when the layer has a shared expert
+  uint32_t* status_reset;     // non-null: the call's status word, cleared here
 };
 // The grouped kernels run kGridTiles workgroups (one per CU, a multiple of 8).
 // Logical workgroup w takes the contiguous part [w L / W, (w+1) L / W) of the

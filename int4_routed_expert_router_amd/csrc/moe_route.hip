@@ -141,6 +141,7 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ to
     cnt[tid] = 0;
     run[tid] = 0;
   }
+  if (tid == 0 && plan.status_reset != nullptr) *plan.status_reset = 0u;
   __syncthreads();
   // rows whose expert index lies outside [0, E) are dropped: not counted,
   // not placed (inv = -1), so they contribute nothing
