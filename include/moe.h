@@ -233,6 +233,21 @@ moe_status moe_layer_forward(const moe_layer_desc* desc, const moe_layer_weights
                              float* topk_w_or_null, float* shared_gate_or_null,
                              void* ws, size_t ws_bytes, moe_stream stream);
 
+/* moe_layer_forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same call, bit for bit the same results, with its
+ * workspace in a static device array of MOE_STATIC_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on until the process ends.  It calls no
+ * allocating routine.  A batch whose workspace (moe_workspace_bytes) exceeds
+ * the array returns MOE_EWORKSPACE.  Every call on one GPU shares that GPU's
+ * array: calls that overlap in time on one GPU (other streams or threads)
+ * race on it; calls ordered on one stream do not.  The status word of the
+ * call (moe_workspace_status) sits in the array and is not readable here. */
+#define MOE_STATIC_SCRATCH_BYTES (32u << 20)
+moe_status moe_layer_forward_static(const moe_layer_desc* desc, const moe_layer_weights* w, const void* x,
+                                    int32_t n_tokens, float* y, int32_t* topk_idx_or_null,
+                                    float* topk_w_or_null, float* shared_gate_or_null, moe_stream stream);
+
 /* Chaining step between MoE layers of a stack (a pre-norm residual stand-in;
  * the pages do not describe the layers between MoE blocks):
  *   r[t] += y[t];  x_next[t] = round_rne(r[t] / sqrt(mean(r[t]^2) + 1e-6))

@@ -72,6 +72,7 @@ PROTOS = {
     "moe_permute": (i32, [vp, vp, i32, vp, vp, vp, vp, C.c_size_t, vp]),
     "moe_expert_ffn": (i32, [vp, vp, vp, i32, vp, vp, vp, vp, vp, C.c_size_t, vp]),
     "moe_layer_forward": (i32, [vp, vp, vp, i32, vp, vp, vp, vp, vp, C.c_size_t, vp]),
+    "moe_layer_forward_static": (i32, [vp, vp, vp, i32, vp, vp, vp, vp, vp]),
     "moe_stack_epilogue": (i32, [vp, i32, vp, vp, vp, vp]),
     "moe_stack_forward": (i32, [vp, vp, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, C.c_size_t, vp]),
     "moe_stack_graph_create": (i32, [vp, vp, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, C.c_size_t, vp,

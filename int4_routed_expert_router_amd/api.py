@@ -18,7 +18,7 @@ from ._lib import (GdnDesc, MOE_BF16, MOE_F16, MOE_PATH_AUTO, MOE_POOL_DMA_COPY,
 
 __all__ = ["Desc", "Layer", "blob_bytes", "pack_expert", "workspace_bytes", "workspace", "workspace_status",
            "route", "permute",
-           "expert_ffn", "layer_forward", "stack_epilogue", "stack_forward", "StackGraph", "synth_fill_experts",
+           "expert_ffn", "layer_forward", "layer_forward_static", "stack_epilogue", "stack_forward", "StackGraph", "synth_fill_experts",
            "synth_philox", "SlotPool", "pool_decode_step", "gdn_step"]
 
 
@@ -206,6 +206,17 @@ def layer_forward(desc, layer, x, y, topk_idx=None, topk_w=None, shared_gate=Non
     d, w = desc.c(), layer.c()
     ws = _scratch(desc, T, x.device, stream) if ws is None else ws
     check(lib().moe_layer_forward(C.byref(d), C.byref(w), *args, _ws(ws), ws.numel(), _stream(stream)))
+
+
+def layer_forward_static(desc, layer, x, y, topk_idx=None, topk_w=None, shared_gate=None, stream=None):
+    """moe_layer_forward_static: the layer call with the library's static
+    device scratch instead of a workspace (no allocation anywhere)."""
+    T = _tokens(x, desc)
+    K, H = desc.top_k, desc.hidden
+    args = (_ptr(x), T, _ptr(y, "y", _F32, T * H), _ptr(topk_idx, "topk_idx", _I32, T * K),
+            _ptr(topk_w, "topk_w", _F32, T * K), _ptr(shared_gate, "shared_gate", _F32, T))
+    d, w = desc.c(), layer.c()
+    check(lib().moe_layer_forward_static(C.byref(d), C.byref(w), *args, _stream(stream)))
 
 
 def stack_epilogue(desc, y, r, x_next, stream=None):
