@@ -112,7 +112,7 @@ Ws layout(const moe_layer_desc* d, int T) {
   s.inv = o; o += al(T * K * 4);
   s.units = o; o += al(4ull * moe::kUnitInts * moe::max_units(T, d->top_k, d->n_experts, d->shared_inter > 0));
   s.nunits = o; o += al(16);
-  // grouped: fp16 hi, lo planes (4 B per element); GEMV: splits of fp32 (gate, up)
+  // grouped: fp16 h (2 B per element); GEMV: splits of fp32 (gate, up)
   s.h = o; o += al(rows * hstride * 4 * 2 * moe::kGemvSplit);
   s.hsum = o; o += al(rows * (hstride / 16) * 4);
   s.yrow = o; o += al(rows * H * 4);

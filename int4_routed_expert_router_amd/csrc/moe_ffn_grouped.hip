@@ -33,10 +33,11 @@
 // with the column sums of the unit's activations computed once per unit.
 // Activations become fp16 (bf16 inputs are exact in fp16 within its range;
 // the grouped family needs |x| and |h| to round below 65520, and the gate/up
-// kernel reports any value that does not in the call's status word); the SwiGLU output h
-// enters the down projection as an fp16 hi + lo pair (22 significant bits),
-// written operand-ready by the gate/up kernel together with the fp32 sums of
-// hi + lo over 16-column blocks for the down kernel's bias term.
+// kernel reports any value that does not in the call's status word); the
+// SwiGLU output h enters the down projection as fp16 (11 significant bits,
+// one rounding of the fp32 h), written operand-ready by the gate/up kernel
+// together with the fp32 sums of those fp16 values over 16-column blocks for
+// the down kernel's bias term.
 //
 // int8 experts (BITS = 8) use the same stream with two 16-byte loads per lane
 // and chunk (the tile A and tile B planes of the blob).  A byte q becomes
@@ -372,9 +373,9 @@ __device__ __forceinline__ void staged_barrier() {
 // chunks c_j = w + 8 j (j < 4).  Each wave holds the A operands of its own
 // chunks for the current unit in registers (no LDS staging), and loads the
 // next unit's activations as soon as its weight stream reaches that unit.
-// Output: h as fp16 hi and lo planes, operand-ready for the down projection
-// (columns with (col & 2) != 0 scaled by 1/16), at rows row0.., columns
-// 16 pt.., and hsum[row][pt] = sum over the 16 columns of h (hi + lo).
+// Output: h as fp16, operand-ready for the down projection (columns with
+// (col & 2) != 0 scaled by 1/16), at rows row0.., columns 16 pt.., and
+// hsum[row][pt] = sum over the 16 columns of those fp16 values (unscaled).
 // FULL: H is the family's largest (2048, 32 chunks), so every chunk w + 8 j
 // a wave forms is in range and the product loop carries no range tests.
 // ---------------------------------------------------------------------------
@@ -400,9 +401,7 @@ __global__ __launch_bounds__(512) void k_gateup_tiles(FfnArgs a) {
   const int t0 = static_cast<int>((static_cast<long long>(lw) * L) >> kGridTilesLog2);
   const int t1 = static_cast<int>((static_cast<long long>(lw + 1) * L) >> kGridTilesLog2);
   if (t0 >= t1) return;
-  const int hplane = (a.T * a.K + (a.Is > 0 ? a.T : 0)) * a.hstride;
-  uint16_t* h_hi = reinterpret_cast<uint16_t*>(a.h);
-  uint16_t* h_lo = h_hi + hplane;
+  uint16_t* h16 = reinterpret_cast<uint16_t*>(a.h);
   const int hs_stride = a.hstride / 16;
   // tile cursor: (unit, pair-tile); units before n_su have nts tiles, the rest ntr
   struct Cursor {
@@ -618,14 +617,13 @@ __global__ __launch_bounds__(512) void k_gateup_tiles(FfnArgs a) {
       // silu(g) * u with the hardware exp2 and reciprocal (relative error a
       // few ulp, far inside the block's tolerance)
       const float hv = ga * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * ga)) * up;
-      // operand-ready fp16 hi + lo of h * f, f = 1/16 on the columns the down
+      // operand-ready fp16 of h * f, f = 1/16 on the columns the down
       // projection's B operand carries as q * 2^-20 (column 16 pt + nn); int8:
       // f = 1, stored at the permuted column h8_col
       const bool sc = BITS == 4 && (nn & 2) != 0;
       const float hf_v = sc ? hv * 0.0625f : hv;
       const uint32_t hi = f32_to_f16_bits(hf_v);
-      const uint32_t lo = f32_to_f16_bits(hf_v - f16_bits_f32(hi));
-      float hs = f16_bits_f32(hi) + f16_bits_f32(lo);
+      float hs = f16_bits_f32(hi);
       hs = sc ? hs * 16.0f : hs;
       // sum over the 16 columns of this row of the tile (one 16-lane DPP row)
       hs = __uint_as_float(dpp_row_sum(__float_as_uint(hs)));
@@ -633,8 +631,7 @@ __global__ __launch_bounds__(512) void k_gateup_tiles(FfnArgs a) {
         if ((hi & 0x7C00u) == 0x7C00u) atomicOr(a.status, kStatusF16Range);   // h outside the fp16 range
         const int col = BITS == 8 ? h8_col(nn) : nn;
         const size_t off = static_cast<size_t>(o.row0 + m) * a.hstride + 16 * o.pt + col;
-        h_hi[off] = static_cast<uint16_t>(hi);
-        h_lo[off] = static_cast<uint16_t>(lo);
+        h16[off] = static_cast<uint16_t>(hi);
         if (nn == 0) a.hsum[static_cast<size_t>(o.row0 + m) * hs_stride + o.pt] = hs;
       }
     }
@@ -659,8 +656,8 @@ __global__ __launch_bounds__(512) void k_gateup_tiles(FfnArgs a) {
 // ---------------------------------------------------------------------------
 // down projection.  Tiles are down pair-tiles (32 output rows); a step takes 4
 // consecutive tiles of one unit (quad), tile q4 = wave % 4, and the two waves
-// w, w + 4 split the reduction (chunks w / 4 + 2 j).  h (operand-ready fp16
-// hi, lo) of the unit's rows is staged in LDS, in one of two buffers: a
+// w, w + 4 split the reduction (chunks w / 4 + 2 j).  h (operand-ready fp16)
+// of the unit's rows is staged in LDS, in one of two buffers: a
 // workgroup's range spans at most two units at the batch shapes, and both
 // are staged before the first weight loads, so the switch to the second unit
 // waits for nothing (a third unit, possible at other shapes, is staged at its
@@ -679,7 +676,6 @@ __global__ __launch_bounds__(512) void k_down_tiles(FfnArgs a) {
   constexpr int kDepth = 2;
   constexpr int kHalves = G == 32 ? 2 : 1;
   __shared__ __attribute__((aligned(16))) uint16_t hsh[2][kSub * kGroupedMaxInter];
-  __shared__ __attribute__((aligned(16))) uint16_t hsl[2][kSub * kGroupedMaxInter];
   __shared__ float red[2][4][8][65];
   __shared__ __attribute__((aligned(16))) float cs[2][kGroupedMaxInter / 32][kSub];   // 32-column sums of h
   __shared__ int urow[2][kSub];
@@ -695,9 +691,7 @@ __global__ __launch_bounds__(512) void k_down_tiles(FfnArgs a) {
   const int s0 = static_cast<int>((static_cast<long long>(lw) * Q) >> kGridTilesLog2);
   const int s1 = static_cast<int>((static_cast<long long>(lw + 1) * Q) >> kGridTilesLog2);
   if (s0 >= s1) return;
-  const int hplane = (a.T * a.K + (a.Is > 0 ? a.T : 0)) * a.hstride;
-  const uint16_t* h_hi = reinterpret_cast<const uint16_t*>(a.h);
-  const uint16_t* h_lo = h_hi + hplane;
+  const uint16_t* h16 = reinterpret_cast<const uint16_t*>(a.h);
   const int hs_stride = a.hstride / 16;
   int xu = s0 / qpu;
   const UnitHdr hd0 = unit_hdr(a.units, xu);
@@ -720,15 +714,14 @@ __global__ __launch_bounds__(512) void k_down_tiles(FfnArgs a) {
     qb = reinterpret_cast<const uint4*>(sblob + blob_d_q(H, sI, BITS)) + static_cast<size_t>(pt) * ncq * 64 * NQ + lane;
     sb = sblob + blob_d_s(H, sI, G, BITS) + (static_cast<size_t>(pt) * (sI / G) * 16 + n) * 8;
   };
-  // stage h (hi, lo) of a unit's rows (direct-to-LDS) and fetch the sums of
+  // stage h of a unit's rows (direct-to-LDS) and fetch the sums of
   // h over 16-column blocks; the 32-column sums are stored afterwards, so
   // that loads issued in between stay in flight (kSub * inter / 32 <= 512:
   // one sum per thread)
   static_assert(kSub * (kGroupedMaxInter / 32) <= 512, "one column sum per thread");
   // urow[b] must hold the unit's rows (and be visible) before the call
   auto stage_issue = [&](int b, int r0, int mcu, int Iu, float& p0, float& p1) {
-    stage_rows(h_hi, urow[b], mcu, a.hstride, Iu, hsh[b], wave, lane);
-    stage_rows(h_lo, urow[b], mcu, a.hstride, Iu, hsl[b], wave, lane);
+    stage_rows(h16, urow[b], mcu, a.hstride, Iu, hsh[b], wave, lane);
     const int m = tid & (kSub - 1), j = tid >> 4;
     p0 = p1 = 0.0f;
     if (j < Iu / 32 && m < mcu) {
@@ -805,8 +798,6 @@ __global__ __launch_bounds__(512) void k_down_tiles(FfnArgs a) {
     tile_src(min(q + kDepth, s1 - 1), qnx, snx, ncn);
     const uint16_t* ha0 = &hsh[hb][(n * upr + (kb ^ (n & 7))) * 8];
     const uint16_t* ha1 = &hsh[hb][(n * upr + ((kb + 4) ^ (n & 7))) * 8];
-    const uint16_t* la0 = &hsl[hb][(n * upr + (kb ^ (n & 7))) * 8];
-    const uint16_t* la1 = &hsl[hb][(n * upr + ((kb + 4) ^ (n & 7))) * 8];
     const float(*csb)[kSub] = cs[hb];
     f32x4_t accA = {0, 0, 0, 0}, accB = {0, 0, 0, 0}, biasA = {0, 0, 0, 0}, biasB = {0, 0, 0, 0};
     // the scale of chunk j is applied after the products of chunk j + 1 are
@@ -825,8 +816,6 @@ __global__ __launch_bounds__(512) void k_down_tiles(FfnArgs a) {
       if (FULL || c < nc) {
         const uint4 h0 = *reinterpret_cast<const uint4*>(ha0 + 64 * c);
         const uint4 h1 = *reinterpret_cast<const uint4*>(ha1 + 64 * c);
-        const uint4 l0 = *reinterpret_cast<const uint4*>(la0 + 64 * c);
-        const uint4 l1 = *reinterpret_cast<const uint4*>(la1 + 64 * c);
         const float4 c0 = *reinterpret_cast<const float4*>(&csb[2 * c][4 * kb]);
         const float4 c1 = *reinterpret_cast<const float4*>(&csb[2 * c + 1][4 * kb]);
         if constexpr (G == 32) {
@@ -836,7 +825,7 @@ __global__ __launch_bounds__(512) void k_down_tiles(FfnArgs a) {
           cs0[0] = c0.x + c1.x; cs0[1] = c0.y + c1.y; cs0[2] = c0.z + c1.z; cs0[3] = c0.w + c1.w;
           cs1[0] = cs0[0]; cs1[1] = cs0[1]; cs1[2] = cs0[2]; cs1[3] = cs0[3];
         }
-        p = chunk_mfma<G, true>(d, h0, h1, l0, l1);
+        p = chunk_mfma<G, false>(d, h0, h1, h0, h1);
       }
       if (j > 0 && (FULL || c - 2 < nc)) chunk_scale<G>(pp, pk, pcs0, pcs1, accA, accB, biasA, biasB);
       pp = p;

@@ -24,7 +24,7 @@ struct FfnArgs {
   uint64_t stride;            // blob stride when offsets == nullptr
   const uint64_t* offsets;    // [E] byte offsets or nullptr
   const uint8_t* shared;      // shared blob or nullptr
-  float* h;                   // grouped: h as fp16 hi, lo planes [2][rows][hstride];
+  float* h;                   // grouped: h as fp16 [rows][hstride], operand-ready;
                               // GEMV: partial (gate, up) sums [kGemvSplit][rows][hstride][2] fp32
   float* yrow;                // [rows][H] per-row expert outputs (unweighted)
   // grouped family
