@@ -46,6 +46,9 @@ def parse():
                     help="pool80: copy misses with the copy kernel (mapped host reads) or the copy engine")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (scale reference for HBM byte counters)")
+    ap.add_argument("--read-ceiling", action="store_true",
+                    help="only measure plain streaming reads (read sizes x workgroup counts): the practical HBM "
+                         "read ceiling the FFN kernels are compared with")
     return ap.parse_args()
 
 
@@ -68,6 +71,43 @@ def copy_calibration():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_per_dispatch": COPY_BYTES, "dispatches": 3}))
+
+
+def read_ceiling():
+    """Plain streaming reads of windows of a 4 GiB buffer (so each read comes
+    from HBM, not the 256 MB Infinity Cache: consecutive launches read
+    different windows, as the 48 layers of a stack do), for read sizes of one
+    FFN launch (16 and 50 MB) and 1 GiB, and 256 to 2048 workgroups of 512
+    threads.  HIP events on the launch stream around every launch; one JSON
+    line per (size, workgroups) with the average rate."""
+    import ctypes as C
+    import torch
+    from int4_routed_expert_router_amd._lib import check, lib
+    buf_bytes = 4 << 30
+    buf = torch.empty(buf_bytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.zeros(65536, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.Stream()
+    base = buf.data_ptr()
+    for size in (16 << 20, 50 << 20, 1 << 30):
+        n_win = buf_bytes // size
+        for wgs in (256, 512, 1024, 2048):
+            reps = min(48, 4 * n_win)
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+            with torch.cuda.stream(stream):
+                for w in range(3):   # warm-up launches
+                    check(lib().moe_read_probe(C.c_void_p(base + (w % n_win) * size), size, wgs,
+                                               C.c_void_p(sink.data_ptr()), C.c_void_p(stream.cuda_stream)))
+                for i in range(reps):
+                    ev[i][0].record(stream)
+                    check(lib().moe_read_probe(C.c_void_p(base + ((i + 3) % n_win) * size), size, wgs,
+                                               C.c_void_p(sink.data_ptr()), C.c_void_p(stream.cuda_stream)))
+                    ev[i][1].record(stream)
+            torch.cuda.synchronize()
+            us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+            print(json.dumps({"read_bytes": size, "workgroups": wgs, "launches": reps, "avg_us": round(us, 2),
+                              "GBps": round(size / (us * 1e-6) / 1e9, 1),
+                              "frac_of_8TBps": round(size / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}), flush=True)
 
 
 def measured_traffic(path=TRAFFIC_FILE, src=GROUPED_SRC):
@@ -174,32 +214,47 @@ def clear_timer():
 
 def cpu_baseline(wl, budget_s):
     """fp64 oracle on a bounded sample: whole layers of the same workload
-    (all tokens), as many as fit the budget (at least one)."""
+    (all tokens), as many as fit the budget (at least one).  Each layer's
+    inputs (the quantised weights of the experts it selects, router weights
+    and bias) are generated before its timer starts; the timed part is the
+    oracle itself: routing, dequantisation of the selected experts, SwiGLU
+    FFNs and combine."""
     import synth
     from oracle import moe_oracle as mo
     cores = len(os.sched_getaffinity(0))
     x64 = mo.act_bits_to_f64(synth.tokens(wl), wl.act_dtype)
-    t0 = time.perf_counter()
+    timed, gen = 0.0, 0.0
     done = 0
     while True:
         l = done
-
-        def expert(e, shared=False, l=l):
-            r = synth.expert_raw(wl, l, e, shared=shared)
-            return mo.ExpertWeights.from_quant(r["gate"], r["up"], r["down"], wl.group, wl.bits)
-
+        g0 = time.perf_counter()
         wr = mo.f16_bits_to_f64(synth.router_weights(wl, l))
         b = synth.router_bias(wl, l)
-        mo.layer_forward(x64, wr, None if b is None else b.astype(np.float64), expert, expert(0, True), wl.top_k)
+        b64 = None if b is None else b.astype(np.float64)
+        # the experts the layer will select (routing is repeated, timed, below)
+        touched = sorted(set(mo.route(x64, wr, b64, wl.top_k)[0].ravel().tolist()))
+        raw = {e: synth.expert_raw(wl, l, e) for e in touched}
+        raw_shared = synth.expert_raw(wl, l, 0, shared=True)
+        gen += time.perf_counter() - g0
+
+        def expert(e, raw=raw):
+            r = raw[e]
+            return mo.ExpertWeights.from_quant(r["gate"], r["up"], r["down"], wl.group, wl.bits)
+
+        t0 = time.perf_counter()
+        shared = mo.ExpertWeights.from_quant(raw_shared["gate"], raw_shared["up"], raw_shared["down"], wl.group,
+                                             wl.bits)
+        mo.layer_forward(x64, wr, b64, expert, shared, wl.top_k)
+        timed += time.perf_counter() - t0
         done += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or done >= wl.layers:
+        if timed >= budget_s or done >= wl.layers:
             break
-    per_layer = el / done
+    per_layer = timed / done
     tok_s = wl.tokens / (per_layer * wl.layers)
     return dict(value=tok_s, unit="tokens/s", cores=cores, kind="oracle",
-                sample=f"{done} whole layer(s) x {wl.tokens} tokens of the same workload in {el:.1f} s, "
-                       f"scaled to the {wl.layers}-layer stack (weights generated and dequantised per layer)")
+                sample=f"{done} whole layer(s) x {wl.tokens} tokens of the same workload: {timed:.1f} s of oracle "
+                       f"time (routing, dequantisation of the selected experts, FFNs, combine), scaled to the "
+                       f"{wl.layers}-layer stack; input generation ({gen:.1f} s) outside the timer")
 
 
 def run_pool(args):
@@ -379,6 +434,9 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
+    if args.read_ceiling:
+        read_ceiling()
+        return
     if args.gpus != 1:
         print(json.dumps({"error": f"--gpus {args.gpus}: this benchmark runs on exactly one GPU; "
                                    "multi-GPU sharding is designed (DESIGN.md) but not built"}))
@@ -442,6 +500,7 @@ def main():
 
     roof = None
     kernel_us = {}
+    kernel_roof = None
     if not args.no_kernel_timing:
         # HIP events around each layer's kernel of one kind, recorded on the
         # stream that launches it, over eager (launch-by-launch) replays of the
@@ -474,6 +533,23 @@ def main():
                 "avg_us": round(avg_us, 2), "bytes_per_launch": int(per_launch),
                 "traffic_bytes_per_launch": None if tb is None else int(tb),
                 "events": "HIP events on the launch stream around each layer's gate/up kernel, eager replay"}
+        # the other timed kernels against the same peak: down (d values and
+        # their fp16 scale and bias per touched expert) and the router (the
+        # E+1 fp16 router rows, plus the tokens once)
+        d_bytes = (st.desc.inter * st.desc.hidden * wl.bits // 8
+                   + 4 * st.desc.inter * st.desc.hidden // st.desc.group_size)
+        d_launch = float(np.mean([(a + 1) * d_bytes for a in act]))
+        r_launch = (wl.n_experts + 1) * wl.hidden * 2 + wl.tokens * wl.hidden * 2
+        kernel_roof = {
+            "gateup": {"bytes_per_launch": int(per_launch), "avg_us": round(avg_us, 2),
+                       "GBps": round(achieved, 1), "frac": round(achieved / HBM_PEAK_GBS, 4)},
+            "down": {"bytes_per_launch": int(d_launch), "avg_us": round(kernel_us["down"], 2),
+                     "GBps": round(d_launch / (kernel_us["down"] * 1e-6) / 1e9, 1),
+                     "frac": round(d_launch / (kernel_us["down"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+            "router": {"bytes_per_launch": int(r_launch), "avg_us": round(kernel_us["router"], 2),
+                       "GBps": round(r_launch / (kernel_us["router"] * 1e-6) / 1e9, 1),
+                       "frac": round(r_launch / (kernel_us["router"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+        }
         print(f"[bench] kernel avg us: " + ", ".join(f"{k} {v:.2f}" for k, v in kernel_us.items())
               + f"; gate/up {achieved:.0f} GB/s", file=sys.stderr, flush=True)
 
@@ -512,6 +588,7 @@ def main():
                    "graph": not args.eager, "parallelism": "single GPU"},
         "roofline": roof,
         "kernel_avg_us": {k: round(v, 2) for k, v in kernel_us.items()},
+        "kernel_roofline": kernel_roof,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))

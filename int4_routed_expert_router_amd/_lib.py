@@ -91,6 +91,7 @@ PROTOS = {
     "slotpool_stats": (i32, [vp, C.POINTER(SlotPoolStats)]),
     "slotpool_destroy": (None, [vp]),
     "slotpool_get_config": (i32, [vp, C.POINTER(SlotPoolConfig)]),
+    "moe_read_probe": (i32, [vp, u64, i32, vp, vp]),
     "moe_pool_decode_step": (i32, [vp, vp, i32, vp, u64, vp, vp, vp, vp, vp, i32, vp, C.c_size_t, vp]),
 }
 

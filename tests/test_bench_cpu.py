@@ -18,3 +18,13 @@ def test_bench_refuses_several_gpus(capsys, monkeypatch):
     assert ex.value.code == 2
     line = capsys.readouterr().out.strip().splitlines()[-1]
     assert "one GPU" in json.loads(line)["error"]
+
+
+def test_cpu_baseline_times_the_oracle_not_the_generator():
+    if ROOT not in sys.path:
+        sys.path.insert(0, ROOT)
+    import bench
+    import synth
+    out = bench.cpu_baseline(synth.TINY, 0.05)
+    assert out["kind"] == "oracle" and out["value"] > 0 and out["cores"] >= 1
+    assert "outside the timer" in out["sample"]
