@@ -94,7 +94,7 @@ moe_status check_weights(const moe_layer_desc* d, const moe_layer_weights* w) {
 size_t al(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct Ws {
-  size_t logits, idx, w, gamma, off, perm, inv, units, nunits, h, hsum, yrow, pre, status, total;
+  size_t logits, idx, w, gamma, off, perm, inv, units, nunits, h, hsum, yrow, pre, status, rres, total;
 };
 
 Ws layout(const moe_layer_desc* d, int T) {
@@ -118,6 +118,7 @@ Ws layout(const moe_layer_desc* d, int T) {
   s.yrow = o; o += al(rows * H * 4);
   s.pre = o; o += al(T * K * 8 + T * 4);   // pre-gated selection: idx, w, gamma
   s.status = o; o += al(4);                 // status word of the last call (MOE_FLAG_*)
+  s.rres = o; o += al(static_cast<size_t>(T) * H * 4);   // second residual buffer of decode stacks
   s.total = o;
   return s;
 }
@@ -179,11 +180,47 @@ struct FusedTopk {
 
 bool fuse_topk(const moe_layer_desc* d, int T) { return !use_grouped(d, T) && d->n_experts <= 512; }
 
+// Decode-sized stacks (GEMV family, batches below the matrix-core router's
+// size): the combine, residual and normalisation of layer l run inside the
+// router of layer l + 1 (launch_router_combine), and one combine follows the
+// last layer, so a layer is three launches (router, gate/up with the top-K,
+// down).  The residual alternates between the caller's r and a workspace
+// buffer (layer l's input residual in buffer l & 1); the last combine
+// writes the caller's r.
+bool fold_combine(const moe_layer_desc* d, int T) {
+  return !use_grouped(d, T) && moe::router_combine_fits(T, d->hidden);
+}
+
+// The previous layer's outputs that the next router combines.
+struct PrevLayer {
+  const float* w;
+  const float* gamma;
+  const float* r_src;
+  float* r_dst;
+  float* y_out;
+};
+
+moe_status do_router_combine(const moe_layer_desc* d, const moe_layer_weights* w, int T, float* part,
+                             const float* yrow, const PrevLayer& pv, void* x_out, hipStream_t s, int layer,
+                             moe::RouterParts* rp) {
+  hipError_t e = timer_mark(true, MOE_TIME_ROUTER, layer, s);
+  if (e == hipSuccess)
+    e = moe::launch_router_combine(d->act_dtype, w->router_w, w->router_bias, part, T, d->hidden, d->n_experts,
+                                   d->top_k, d->shared_inter > 0, yrow, pv.w, pv.gamma, pv.r_src, pv.r_dst,
+                                   static_cast<uint16_t*>(x_out), pv.y_out, s, rp);
+  if (e == hipSuccess) e = timer_mark(false, MOE_TIME_ROUTER, layer, s);
+  if (e != hipSuccess) return hip_fail(e, "router + combine kernel launch");
+  return MOE_OK;
+}
+
 // reset_status: this FFN is the first of the call, so its first kernel clears
 // the call's status word (the grouped gate/up kernel may then set it)
+// skip_combine: leave the expert rows in the workspace for the next layer's
+// router (fold_combine).
 moe_status do_ffn(const moe_layer_desc* d, const moe_layer_weights* w, const void* x, int T, const int32_t* idx,
                   const float* tw, const float* gamma, float* y, float* r, void* x_next, void* ws, const Ws& L,
-                  hipStream_t s, bool reset_status, int layer = -1, const FusedTopk* fz = nullptr) {
+                  hipStream_t s, bool reset_status, int layer = -1, const FusedTopk* fz = nullptr,
+                  bool skip_combine = false) {
   moe::FfnArgs a{};
   a.status = at<uint32_t>(ws, L.status);
   a.x = static_cast<const uint16_t*>(x);
@@ -247,6 +284,7 @@ moe_status do_ffn(const moe_layer_desc* d, const moe_layer_weights* w, const voi
     if (e == hipSuccess) e = timer_mark(false, MOE_TIME_DOWN, layer, s);
     if (e != hipSuccess) return hip_fail(e, "down GEMV kernel launch");
   }
+  if (skip_combine) return MOE_OK;
   e = moe::launch_combine(d->act_dtype, a.yrow, inv, tw, gamma, T, d->top_k, d->hidden, d->shared_inter > 0, y, r,
                           static_cast<uint16_t*>(x_next), s);
   if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
@@ -500,16 +538,52 @@ static moe_status stack_enqueue(const moe_layer_desc* d, const moe_layer_weights
   Ws L;
   if ((st = check_ws(d, T, ws, ws_bytes, L))) return st;
   const size_t TH = static_cast<size_t>(T) * d->hidden, TK = static_cast<size_t>(T) * d->top_k;
+  const bool fold = fold_combine(d, T);
+  if (fold && !aligned(r, 16)) return fail(MOE_EINVAL, "r must be 16-byte aligned");
+  float* rbuf[2] = {r, at<float>(ws, L.rres)};
+  const float* prev_w = nullptr;
+  const float* prev_gamma = nullptr;
   for (int l = 0; l < L_; ++l) {
     const void* xl = (l == 0) ? x0 : x_buf;
-    if (x_all) {
-      hipError_t e = hipMemcpyAsync(static_cast<uint16_t*>(x_all) + l * TH, xl, TH * 2, hipMemcpyDeviceToDevice, s);
-      if (e != hipSuccess) return hip_fail(e, "x capture copy");
-    }
     int32_t* idx = idx_all ? idx_all + l * TK : at<int32_t>(ws, L.idx);
     float* tw = w_all ? w_all + l * TK : at<float>(ws, L.w);
     float* gamma = gamma_all ? gamma_all + static_cast<size_t>(l) * T : at<float>(ws, L.gamma);
     float* y = y_all ? y_all + l * TH : nullptr;
+    if (fold) {
+      // router (layers after the first also combine the previous layer into
+      // r and form this layer's x in x_buf), gate/up with the top-K, down
+      FusedTopk fz{at<float>(ws, L.logits), {}, idx, tw, gamma};
+      if (l == 0) {
+        if ((st = do_router(d, &layers[l], xl, T, at<float>(ws, L.logits), s, l, &fz.rp))) return st;
+      } else {
+        const PrevLayer pv{prev_w, prev_gamma, rbuf[(l - 1) & 1], rbuf[l & 1], y_all ? y_all + (l - 1) * TH : nullptr};
+        if ((st = do_router_combine(d, &layers[l], T, at<float>(ws, L.logits), at<float>(ws, L.yrow), pv, x_buf, s, l,
+                                    &fz.rp)))
+          return st;
+      }
+      if (x_all) {
+        hipError_t e = hipMemcpyAsync(static_cast<uint16_t*>(x_all) + l * TH, xl, TH * 2, hipMemcpyDeviceToDevice, s);
+        if (e != hipSuccess) return hip_fail(e, "x capture copy");
+      }
+      if (fuse_topk(d, T)) {
+        if ((st = do_ffn(d, &layers[l], xl, T, idx, tw, gamma, y, nullptr, nullptr, ws, L, s, l == 0, l, &fz, true)))
+          return st;
+      } else {
+        hipError_t e = moe::launch_topk(fz.part, fz.rp.n_part, fz.rp.biased ? nullptr : layers[l].router_bias, T,
+                                        d->n_experts, d->top_k, idx, tw, gamma, nullptr, s);
+        if (e != hipSuccess) return hip_fail(e, "top-k kernel launch");
+        if ((st = do_ffn(d, &layers[l], xl, T, idx, tw, gamma, y, nullptr, nullptr, ws, L, s, l == 0, l, nullptr,
+                         true)))
+          return st;
+      }
+      prev_w = tw;
+      prev_gamma = gamma;
+      continue;
+    }
+    if (x_all) {
+      hipError_t e = hipMemcpyAsync(static_cast<uint16_t*>(x_all) + l * TH, xl, TH * 2, hipMemcpyDeviceToDevice, s);
+      if (e != hipSuccess) return hip_fail(e, "x capture copy");
+    }
     if (fuse_topk(d, T)) {
       FusedTopk fz{at<float>(ws, L.logits), {}, idx, tw, gamma};
       if ((st = do_router(d, &layers[l], xl, T, at<float>(ws, L.logits), s, l, &fz.rp))) return st;
@@ -518,6 +592,12 @@ static moe_status stack_enqueue(const moe_layer_desc* d, const moe_layer_weights
     }
     if ((st = do_route(d, &layers[l], xl, T, idx, tw, gamma, at<float>(ws, L.logits), nullptr, s, l))) return st;
     if ((st = do_ffn(d, &layers[l], xl, T, idx, tw, gamma, y, r, x_buf, ws, L, s, l == 0, l))) return st;
+  }
+  if (fold) {   // the last layer's combine, residual and next input
+    hipError_t e = moe::launch_combine(d->act_dtype, at<float>(ws, L.yrow), nullptr, prev_w, prev_gamma, T, d->top_k,
+                                       d->hidden, d->shared_inter > 0, y_all ? y_all + (L_ - 1) * TH : nullptr, r,
+                                       static_cast<uint16_t*>(x_buf), s, rbuf[(L_ - 1) & 1]);
+    if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
   }
   return MOE_OK;
 }
@@ -611,11 +691,28 @@ moe_status moe_pool_decode_step(const moe_layer_desc* d, const moe_layer_weights
   float* pw = at<float>(ws, L.pre + static_cast<size_t>(K) * 4);
   float* pg = at<float>(ws, L.pre + static_cast<size_t>(K) * 8);
   const size_t xbytes = static_cast<size_t>(H) * 2;
+  // decode-sized: the router of layer l > 0 also combines layer l - 1 (see
+  // fold_combine), forming x of layer l in slot (l - 1) & 1 of x_buf
+  const bool fold = fold_combine(d, 1);
+  if (fold && !aligned(r, 16)) return fail(MOE_EINVAL, "r must be 16-byte aligned");
+  float* rbuf[2] = {r, at<float>(ws, L.rres)};
   for (int l = 0; l < L_; ++l) {
-    const void* xl = (l == 0) ? x0 : static_cast<const char*>(x_buf) + ((l - 1) & 1) * xbytes;
+    void* xslot = static_cast<char*>(x_buf) + ((l - 1) & 1) * xbytes;
+    const void* xl = (l == 0) ? x0 : xslot;
     void* xn = static_cast<char*>(x_buf) + (l & 1) * xbytes;
     const moe_layer_weights w = pooled(l);
-    if ((st = do_route(d, &w, xl, 1, idx, tw, gamma, at<float>(ws, L.logits), nullptr, s))) return st;
+    if (fold && l > 0) {
+      // tw and gamma still hold layer l - 1's values: the top-K below rewrites them
+      moe::RouterParts rp{};
+      const PrevLayer pv{tw, gamma, rbuf[(l - 1) & 1], rbuf[l & 1], nullptr};
+      if ((st = do_router_combine(d, &w, 1, at<float>(ws, L.logits), at<float>(ws, L.yrow), pv, xslot, s, -1, &rp)))
+        return st;
+      hipError_t e = moe::launch_topk(at<float>(ws, L.logits), rp.n_part, rp.biased ? nullptr : w.router_bias, 1,
+                                      d->n_experts, K, idx, tw, gamma, nullptr, s);
+      if (e != hipSuccess) return hip_fail(e, "top-k kernel launch");
+    } else if ((st = do_route(d, &w, xl, 1, idx, tw, gamma, at<float>(ws, L.logits), nullptr, s))) {
+      return st;
+    }
     hipError_t e = hipMemcpyAsync(idx_host, idx, K * 4, hipMemcpyDeviceToHost, s);
     const bool pre = pregate > 0 && l + 1 < L_;
     const int n_pre = pregate < K ? pregate : K;   // the highest-ranked predictions
@@ -636,8 +733,17 @@ moe_status moe_pool_decode_step(const moe_layer_desc* d, const moe_layer_weights
     if (pre && (st = slotpool_prefetch(pool, l + 1, idx_host + K, n_pre, step, compute, nullptr, nullptr, nullptr,
                                        nullptr)))
       return fail_layer(st, "prefetch, layer", l + 1);
-    if ((st = do_ffn(d, &w, xl, 1, idx, tw, gamma, nullptr, r, xn, ws, L, s, l == 0))) return st;
+    if ((st = do_ffn(d, &w, xl, 1, idx, tw, gamma, nullptr, fold ? nullptr : r, fold ? nullptr : xn, ws, L, s,
+                     l == 0, -1, nullptr, fold)))
+      return st;
     if ((st = slotpool_release(pool, l, compute))) return fail_layer(st, "release, layer", l);
+  }
+  if (fold) {
+    hipError_t e = moe::launch_combine(d->act_dtype, at<float>(ws, L.yrow), nullptr, tw, gamma, 1, K, H,
+                                       d->shared_inter > 0, nullptr, r,
+                                       reinterpret_cast<uint16_t*>(static_cast<char*>(x_buf) + ((L_ - 1) & 1) * xbytes),
+                                       s, rbuf[(L_ - 1) & 1]);
+    if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
   }
   return ok();
 }

@@ -488,7 +488,8 @@ template <int ACT, bool EPI>
 __global__ __launch_bounds__(512) void k_combine_direct(const float* __restrict__ yrow, const float* __restrict__ w,
                                                         const float* __restrict__ gamma, int T, int K, int H,
                                                         int has_shared, float* __restrict__ y,
-                                                        float* __restrict__ r, uint16_t* __restrict__ x_next) {
+                                                        float* r, uint16_t* __restrict__ x_next,
+                                                        const float* r_in) {
   __shared__ float lds16[16];
   const int t = blockIdx.x, tid = threadIdx.x;
   const int H4 = H / 4;
@@ -503,7 +504,7 @@ __global__ __launch_bounds__(512) void k_combine_direct(const float* __restrict_
   for (int u = 0; u < kPer; ++u) {
     const int c4 = tid + 512 * u;
     if (c4 < H4) {
-      if constexpr (EPI) rr[u] = reinterpret_cast<const float4*>(r + static_cast<size_t>(t) * H)[c4];
+      if constexpr (EPI) rr[u] = reinterpret_cast<const float4*>(r_in + static_cast<size_t>(t) * H)[c4];
       float4 acc = make_float4(0, 0, 0, 0);
       for (int k0 = 0; k0 < ns; k0 += kB) {
         float4 v[kB];
@@ -621,21 +622,24 @@ hipError_t launch_down_gemv(const FfnArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_combine(int act, const float* yrow, const int32_t* inv, const float* w, const float* gamma, int T,
-                          int K, int H, bool has_shared, float* y, float* r, uint16_t* x_next, hipStream_t s) {
+                          int K, int H, bool has_shared, float* y, float* r, uint16_t* x_next, hipStream_t s,
+                          const float* r_in) {
   const int hs = has_shared ? 1 : 0;
+  if (r_in == nullptr) r_in = r;
   if (inv == nullptr) {
     if (r == nullptr) {
       hipLaunchKernelGGL((k_combine_direct<2, false>), dim3(T), dim3(512), 0, s, yrow, w, gamma, T, K, H, hs, y, r,
-                         x_next);
+                         x_next, r_in);
     } else if (act == 2) {
       hipLaunchKernelGGL((k_combine_direct<2, true>), dim3(T), dim3(512), 0, s, yrow, w, gamma, T, K, H, hs, y, r,
-                         x_next);
+                         x_next, r_in);
     } else {
       hipLaunchKernelGGL((k_combine_direct<1, true>), dim3(T), dim3(512), 0, s, yrow, w, gamma, T, K, H, hs, y, r,
-                         x_next);
+                         x_next, r_in);
     }
     return hipGetLastError();
   }
+  if (r_in != r) return hipErrorInvalidValue;   // the bucketed combine updates r in place only
   if (r == nullptr) {
     hipLaunchKernelGGL((k_combine<2, false>), dim3(T), dim3(512), 0, s, yrow, inv, w, gamma, T, K, H, hs, y, r,
                        x_next);

@@ -93,6 +93,20 @@ struct RouterParts {
 };
 hipError_t launch_router_logits(int act, const uint16_t* x, const uint16_t* wr, const float* bias, float* part,
                                 int T, int H, int E, hipStream_t s, RouterParts* out);
+// Router of a layer after the first in a decode-sized stack with the
+// previous layer's combine, residual and normalisation folded in (the GEMV
+// family's rows yrow [T*K + T][H], weights w [T][K], gamma [T]):
+// r_dst = r_src + y, x_out = rne(r_dst / rms(r_dst)), y_out = y (optional),
+// logits of x_out as launch_router_logits writes them (one biased part).
+// r_dst must differ from r_src.  Fits for T * H <= 32768 (x of every token
+// in LDS) and T below the matrix-core router's size.
+inline bool router_combine_fits(int T, int H) {
+  return T >= 1 && T < kRouterMfmaMinTokens && static_cast<long long>(T) * H <= 32768;
+}
+hipError_t launch_router_combine(int act, const uint16_t* wr, const float* bias, float* logits, int T, int H, int E,
+                                 int K, bool has_shared, const float* yrow, const float* w, const float* gamma,
+                                 const float* r_src, float* r_dst, uint16_t* x_out, float* y_out, hipStream_t s,
+                                 RouterParts* out);
 // Top-K over z[t][e] = sum_p part[p][t][e] (p ascending) + bias[e] (bias may
 // be null); the shared-gate logit is column E, summed the same way.  Writes
 // the selection, the renormalised weights, the shared gate (when gamma is
@@ -108,10 +122,11 @@ hipError_t launch_gateup_grouped(int act, const FfnArgs& a, hipStream_t s);
 hipError_t launch_down_grouped(const FfnArgs& a, hipStream_t s);
 
 // y[t] = sum_k w[t,k] yrow[row(t,k)] + gamma[t] yrow[T*K+t]; row(t,k) = inv ? inv[t*K+k] : t*K+k.
-// With r != nullptr also the stack epilogue (r += y; x_next = rne(r / rms(r))).
+// With r != nullptr also the stack epilogue (r = r_in + y, r_in == nullptr
+// meaning r itself; x_next = rne(r / rms(r))).
 hipError_t launch_combine(int act, const float* yrow, const int32_t* inv, const float* w, const float* gamma,
                           int T, int K, int H, bool has_shared, float* y, float* r, uint16_t* x_next,
-                          hipStream_t s);
+                          hipStream_t s, const float* r_in = nullptr);
 hipError_t launch_epilogue(int act, const float* y, float* r, uint16_t* x_next, int T, int H, hipStream_t s);
 
 }  // namespace moe

@@ -57,6 +57,164 @@ __global__ __launch_bounds__(64) void k_router_logits(const uint16_t* __restrict
   }
 }
 
+// Router of a layer after the first in a decode-sized stack, with the
+// previous layer's combine and residual folded in:
+//   y_t  = sum_k w[t,k] yrow[tK+k] + gamma[t] yrow[TK+t]   (rank order, shared last)
+//   r'_t = r_src_t + y_t,   x_t = rne(r'_t / sqrt(mean(r'_t^2) + 1e-6))
+//   z[t][row] = sum_h x[t][h] Wr[row][h] (+ bias[row] for row < E)
+// Four router rows per 256-thread workgroup (one per wave).  Every workgroup
+// forms y, r' and x of every token itself, with the same code in the same
+// order, so all of them hold the same bits; workgroup 0 stores r' (r_dst,
+// a different buffer from r_src), x (x_out) and y (y_out, when non-null).
+// The router rows' loads are issued first (they do not depend on x); the
+// dot products follow k_router_logits' order exactly (lane-sequential over
+// the lane's columns, then the wave butterfly, then the bias).  Thread u
+// owns columns 2048 m + 8 u + i (i < 8) of the combine.  Dynamic LDS: x of
+// all tokens, T * H 16-bit values.
+template <int ACT>
+__global__ __launch_bounds__(256) void k_router_combine(const uint16_t* __restrict__ wr,
+                                                        const float* __restrict__ bias, float* __restrict__ logits,
+                                                        int T, int H, int E, int K, int has_shared,
+                                                        const float* __restrict__ yrow, const float* __restrict__ w,
+                                                        const float* __restrict__ gamma,
+                                                        const float* __restrict__ r_src, float* __restrict__ r_dst,
+                                                        uint16_t* __restrict__ x_out, float* __restrict__ y_out) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];   // [T][H]
+  __shared__ float red[4];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int row = 4 * blockIdx.x + wave;
+  const bool row_ok = row <= E;
+  const int nit = (H + 511) / 512;
+  uint4 wv[kMaxH / 512];
+#pragma unroll
+  for (int it = 0; it < kMaxH / 512; ++it) {
+    const int col = it * 512 + lane * 8;
+    wv[it] = (row_ok && it < nit && col < H)
+                 ? *reinterpret_cast<const uint4*>(wr + static_cast<size_t>(row) * H + col)
+                 : make_uint4(0, 0, 0, 0);
+  }
+  const float b = (row < E && bias != nullptr) ? bias[row] : 0.0f;
+  const int ns = K + has_shared;
+  constexpr int kCh = kMaxH / 2048;   // 8-column chunks per thread
+  for (int t = 0; t < T; ++t) {
+    float ss = 0.0f;
+    float rv[kCh][8];
+#pragma unroll
+    for (int m = 0; m < kCh; ++m) {
+      const int c = 2048 * m + 8 * tid;
+      if (c < H) {
+        // every source row's loads of the chunk are issued before the sums
+        constexpr int kB = 12;
+        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int k0 = 0; k0 < ns; k0 += kB) {
+          float4 v[kB][2];
+#pragma unroll
+          for (int q = 0; q < kB; ++q) {
+            const int k = min(k0 + q, ns - 1);
+            const float* src = yrow + static_cast<size_t>(k < K ? t * K + k : T * K + t) * H + c;
+            v[q][0] = *reinterpret_cast<const float4*>(src);
+            v[q][1] = *reinterpret_cast<const float4*>(src + 4);
+          }
+#pragma unroll
+          for (int q = 0; q < kB; ++q) {
+            if (k0 + q < ns) {   // uniform
+              const int k = k0 + q;
+              const float wk = k < K ? w[t * K + k] : gamma[t];
+              acc[0] = fmaf(wk, v[q][0].x, acc[0]);
+              acc[1] = fmaf(wk, v[q][0].y, acc[1]);
+              acc[2] = fmaf(wk, v[q][0].z, acc[2]);
+              acc[3] = fmaf(wk, v[q][0].w, acc[3]);
+              acc[4] = fmaf(wk, v[q][1].x, acc[4]);
+              acc[5] = fmaf(wk, v[q][1].y, acc[5]);
+              acc[6] = fmaf(wk, v[q][1].z, acc[6]);
+              acc[7] = fmaf(wk, v[q][1].w, acc[7]);
+            }
+          }
+        }
+        const float4 r0 = *reinterpret_cast<const float4*>(r_src + static_cast<size_t>(t) * H + c);
+        const float4 r1 = *reinterpret_cast<const float4*>(r_src + static_cast<size_t>(t) * H + c + 4);
+        const float rin[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          rv[m][i] = rin[i] + acc[i];
+          ss = fmaf(rv[m][i], rv[m][i], ss);
+        }
+        if (blockIdx.x == 0) {
+          float* rd = r_dst + static_cast<size_t>(t) * H + c;
+          *reinterpret_cast<float4*>(rd) = make_float4(rv[m][0], rv[m][1], rv[m][2], rv[m][3]);
+          *reinterpret_cast<float4*>(rd + 4) = make_float4(rv[m][4], rv[m][5], rv[m][6], rv[m][7]);
+          if (y_out != nullptr) {
+            float* yd = y_out + static_cast<size_t>(t) * H + c;
+            *reinterpret_cast<float4*>(yd) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            *reinterpret_cast<float4*>(yd + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+          }
+        }
+      }
+    }
+    // block sum of the squares: the wave butterfly, then the 4 waves in order
+    ss = wave_sum(ss);
+    if (lane == 0) red[wave] = ss;
+    __syncthreads();
+    const float tot = ((red[0] + red[1]) + red[2]) + red[3];
+    __syncthreads();
+    const float inv_rms = 1.0f / sqrtf(tot / static_cast<float>(H) + 1e-6f);
+#pragma unroll
+    for (int m = 0; m < kCh; ++m) {
+      const int c = 2048 * m + 8 * tid;
+      if (c < H) {
+        uint4 xv;
+        xv.x = f32_to_act<ACT>(rv[m][0] * inv_rms) | (static_cast<uint32_t>(f32_to_act<ACT>(rv[m][1] * inv_rms)) << 16);
+        xv.y = f32_to_act<ACT>(rv[m][2] * inv_rms) | (static_cast<uint32_t>(f32_to_act<ACT>(rv[m][3] * inv_rms)) << 16);
+        xv.z = f32_to_act<ACT>(rv[m][4] * inv_rms) | (static_cast<uint32_t>(f32_to_act<ACT>(rv[m][5] * inv_rms)) << 16);
+        xv.w = f32_to_act<ACT>(rv[m][6] * inv_rms) | (static_cast<uint32_t>(f32_to_act<ACT>(rv[m][7] * inv_rms)) << 16);
+        *reinterpret_cast<uint4*>(xs + static_cast<size_t>(t) * H + c) = xv;
+        if (blockIdx.x == 0) *reinterpret_cast<uint4*>(x_out + static_cast<size_t>(t) * H + c) = xv;
+      }
+    }
+  }
+  __syncthreads();
+  if (!row_ok) return;
+  for (int t = 0; t < T; ++t) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int it = 0; it < kMaxH / 512; ++it) {
+      const int col = it * 512 + lane * 8;
+      if (it < nit && col < H) {
+        const uint4 xv = *reinterpret_cast<const uint4*>(xs + static_cast<size_t>(t) * H + col);
+        const uint32_t xq[4] = {xv.x, xv.y, xv.z, xv.w};
+        const uint32_t wq[4] = {wv[it].x, wv[it].y, wv[it].z, wv[it].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc = fmaf(act_to_f32<ACT>(xq[i] & 0xFFFFu), f16_bits_to_f32(wq[i] & 0xFFFFu), acc);
+          acc = fmaf(act_to_f32<ACT>(xq[i] >> 16), f16_bits_to_f32(wq[i] >> 16), acc);
+        }
+      }
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) logits[static_cast<size_t>(t) * (E + 1) + row] = (row < E) ? acc + b : acc;
+  }
+}
+
+hipError_t launch_router_combine(int act, const uint16_t* wr, const float* bias, float* logits, int T, int H, int E,
+                                 int K, bool has_shared, const float* yrow, const float* w, const float* gamma,
+                                 const float* r_src, float* r_dst, uint16_t* x_out, float* y_out, hipStream_t s,
+                                 RouterParts* out) {
+  if (!router_combine_fits(T, H)) return hipErrorInvalidValue;
+  const dim3 grid((E + 1 + 3) / 4), block(256);
+  const size_t lds = static_cast<size_t>(T) * H * 2;
+  const int hs = has_shared ? 1 : 0;
+  if (act == 2)
+    hipLaunchKernelGGL(k_router_combine<2>, grid, block, lds, s, wr, bias, logits, T, H, E, K, hs, yrow, w, gamma,
+                       r_src, r_dst, x_out, y_out);
+  else
+    hipLaunchKernelGGL(k_router_combine<1>, grid, block, lds, s, wr, bias, logits, T, H, E, K, hs, yrow, w, gamma,
+                       r_src, r_dst, x_out, y_out);
+  out->n_part = 1;
+  out->biased = true;
+  return hipGetLastError();
+}
+
 // One token per 64-lane workgroup: spreads the loads over the compute units.
 template <int kJ>
 __global__ __launch_bounds__(64) void k_topk(const float* __restrict__ part, int n_part,
