@@ -109,6 +109,30 @@ def read_ceiling():
                               "GBps": round(size / (us * 1e-6) / 1e9, 1),
                               "frac_of_8TBps": round(size / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}), flush=True)
 
+    def events_avg(addrs, size, wgs):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in addrs]
+        with torch.cuda.stream(stream):
+            for i, a in enumerate(addrs):
+                ev[i][0].record(stream)
+                check(lib().moe_read_probe(C.c_void_p(a), size, wgs, C.c_void_p(sink.data_ptr()),
+                                           C.c_void_p(stream.cuda_stream)))
+                ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in ev[3:]])) * 1e3
+
+    # the fixed cost of event timing itself: 16 KiB read by one workgroup
+    print(json.dumps({"case": "16 KiB by one workgroup (event timing floor)",
+                      "avg_us": round(events_avg([base] * 40, 16384, 1), 2)}), flush=True)
+    # fresh pages or not: windows rotating over smaller spans, and one window re-read
+    for size in (16 << 20, 50 << 20):
+        for span in (1 << 30, 512 << 20):
+            n = span // size
+            print(json.dumps({"case": "rotating windows", "read_bytes": size, "span_bytes": span,
+                              "avg_us": round(events_avg([base + (i % n) * size for i in range(40)], size, 256), 2)}),
+                  flush=True)
+        print(json.dumps({"case": "one window re-read (Infinity Cache)", "read_bytes": size,
+                          "avg_us": round(events_avg([base] * 40, size, 256), 2)}), flush=True)
+
 
 def measured_traffic(path=TRAFFIC_FILE, src=GROUPED_SRC):
     """HBM bytes per launch of a kernel from its committed counter summary, or
