@@ -43,7 +43,10 @@ def parse():
     ap.add_argument("--pregate", type=int, default=0,
                     help="pool80: prefetch this many of the next layer's predicted experts per layer (0 = none)")
     ap.add_argument("--pool-copy", default="kernel", choices=["kernel", "engine"],
-                    help="pool80: copy misses with the copy kernel (mapped host reads) or the copy engine")
+                    help="pool80 host driver: copy misses with the copy kernel (mapped host reads) or the copy engine")
+    ap.add_argument("--pool-driver", default="device", choices=["device", "host"],
+                    help="pool80: the GPU-resident pool, one captured graph per token (device), or the host "
+                         "policy with a per-layer index read-back (host)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (scale reference for HBM byte counters)")
     ap.add_argument("--read-ceiling", action="store_true",
@@ -321,8 +324,12 @@ def run_pool(args):
     offsets = torch.zeros(L * E, dtype=torch.int64, device="cuda")
     copy_stream = torch.cuda.Stream()
     compute = torch.cuda.current_stream()
-    pool = api.SlotPool(L, E, S, wl.drift_period, stride, stride, host, slab, offsets, copy_stream,
-                        dma_copy=args.pool_copy == "engine")
+    device_pool = args.pool_driver == "device"
+    if device_pool:
+        pool = api.DevPool(L, E, S, wl.drift_period, stride, stride, host, slab, offsets)
+    else:
+        pool = api.SlotPool(L, E, S, wl.drift_period, stride, stride, host, slab, offsets, copy_stream,
+                            dma_copy=args.pool_copy == "engine")
     desc = api.Desc(H, E, K, wl.inter, wl.shared_inter, wl.group, wl.act_dtype, 0)
     ws = api.workspace(desc, 1)
     toks = torch.from_numpy(np.stack([synth.tokens(wl, step=s)[0] for s in range(steps)]).view(np.int16)).cuda()
@@ -332,15 +339,27 @@ def run_pool(args):
     pregate = args.pregate
     layers = [[api.Layer(routers[l], biases[l][ep], slab, stride, offsets, shared[l * sstride:]) for l in range(L)]
               for ep in range(epochs)]
+    graphs = []
+    x0 = torch.empty(1, H, dtype=torch.int16, device="cuda")
+    if device_pool:
+        # one captured token graph per drift epoch (the router bias differs),
+        # captured on and launched from a stream of its own
+        compute = torch.cuda.Stream()
+        graphs = [api.PoolGraph(desc, layers[ep], pool, x0, r, x_buf, ws, compute) for ep in range(epochs)]
     torch.cuda.synchronize()
     print(f"[bench] pool80 ready in {time.time() - t0:.1f} s; {steps} steps x {L} layers", file=sys.stderr,
           flush=True)
     t_start = time.perf_counter()
-    for s in range(steps):
-        x = toks[s:s + 1]
-        r.copy_(x.view(torch.bfloat16).float()[0])
-        api.pool_decode_step(desc, layers[s // wl.drift_period], pool, s, x, r, x_buf, idx_host, ws,
-                             pregate=pregate, stream=compute)
+    with torch.cuda.stream(compute):
+        for s in range(steps):
+            x = toks[s:s + 1]
+            r.copy_(x.view(torch.bfloat16).float()[0])
+            if device_pool:
+                x0.copy_(x)
+                graphs[s // wl.drift_period].launch(compute)
+            else:
+                api.pool_decode_step(desc, layers[s // wl.drift_period], pool, s, x, r, x_buf, idx_host, ws,
+                                     pregate=pregate, stream=compute)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     st = pool.stats()
@@ -354,9 +373,11 @@ def run_pool(args):
            "config": {"workload": f"pool80: {L} layers x {E} experts as pinned host blobs of {stride} B, "
                                   f"{S} HBM slots per layer, batch 1, {steps} steps, router bias re-drawn every "
                                   f"{wl.drift_period} steps, router weights x3, "
-                                  + (f"pre-gated prefetch of the top {pregate} predictions of the next layer"
-                                     if pregate else "no prefetch")
-                                  + f", copies by the copy {args.pool_copy}"},
+                                  + ("GPU-resident pool (policy kernel, miss copies by a kernel reading a "
+                                     "device miss list), one captured graph per token" if device_pool else
+                                     ("host policy, " + (f"pre-gated prefetch of the top {pregate} predictions of "
+                                      "the next layer" if pregate else "no prefetch")
+                                      + f", copies by the copy {args.pool_copy}"))},
            "data": "synthetic (seeded)"}
     pool.close()
     print(json.dumps(out))

@@ -143,6 +143,62 @@ moe_status moe_pool_decode_step(const moe_layer_desc* desc, const moe_layer_weig
 
 void slotpool_destroy(moe_slotpool* pool);
 
+/* GPU-resident slot pool.  The same policy as slotpool_acquire (residency,
+ * LFU counts with lazy aging, recency, lowest-id tie-break; the prefetch
+ * form is not offered), run by a one-wave kernel on the device on expert ids
+ * that are already on the device (the top-K output), with its misses copied
+ * by a kernel that reads the miss list from device memory and the blobs
+ * from mapped pinned host memory.  Nothing waits for the host, so a streamed
+ * decode token needs no host round trip per layer and can be captured in a
+ * graph.  Pins last for one acquire: the decode loop releases every layer
+ * before it is acquired again.  All work is ordered on the caller's stream
+ * (copies, then the FFN that reads the slots, then later copies into them),
+ * so there are no separate copy-stream events.
+ *   cfg:   as for slotpool_create; copy_stream is not used; flags must be 0;
+ *          host_blobs must be pinned host memory with a device mapping;
+ *          slots_per_layer <= min(n_experts, 1024)
+ *   state: caller-owned device memory of moe_devpool_state_bytes() bytes
+ *          (256-byte aligned) holding the residency tables, counts, the step
+ *          and the statistics; moe_devpool_reset gives the empty pool. */
+typedef struct moe_devpool moe_devpool;
+moe_status moe_devpool_state_bytes(const moe_slotpool_config* cfg, size_t* bytes);
+moe_status moe_devpool_create(const moe_slotpool_config* cfg, void* state, size_t state_bytes, moe_devpool** out);
+/* Enqueues the empty pool (no resident expert, step 0, statistics 0). */
+moe_status moe_devpool_reset(moe_devpool* pool, moe_stream stream);
+/* Enqueues one acquire of the n device expert ids at experts (distinct, in
+ * [0, n_experts); 1 <= n <= min(64, slots_per_layer)) at the pool's step and
+ * the copies of its misses; the device offsets of layer are updated for the
+ * loaded experts.  trace (device, [n][3] int32 or NULL): slot, evicted
+ * expert or -1, hit (0/1) per request.  bump_step != 0: the step advances by
+ * one afterwards.  Invalid ids change nothing and set the pool's error word
+ * (moe_devpool_stats). */
+moe_status moe_devpool_acquire(moe_devpool* pool, int32_t layer, const int32_t* experts, int32_t n,
+                               int32_t bump_step, int32_t* trace, moe_stream stream);
+/* Synchronous read of the statistics (prefetches = 0), the step and the
+ * error word (0 = none) after the work enqueued on stream. */
+moe_status moe_devpool_stats(const moe_devpool* pool, moe_slotpool_stats* out, uint64_t* step_out,
+                             int32_t* error_out, moe_stream stream);
+void moe_devpool_destroy(moe_devpool* pool);
+
+/* One batch-1 decode token through n_layers layers streamed through a
+ * GPU-resident pool, enqueued on stream with no host synchronisation:
+ * per layer, route (the router of layers after the first also combines the
+ * previous layer, as in moe_stack_forward), top-K, moe_devpool_acquire of
+ * the selection (the last layer's advances the step), the expert FFN from
+ * the pool's slots; then the last combine.  Arguments as for
+ * moe_pool_decode_step (layers' experts / stride / offsets come from the
+ * pool); trace (device, [n_layers][top_k][3] int32 or NULL) receives every
+ * layer's acquire trace.  The call can be captured (moe_pool_graph_create). */
+moe_status moe_pool_decode_step_dev(const moe_layer_desc* desc, const moe_layer_weights* layers, int32_t n_layers,
+                                    moe_devpool* pool, const void* x0, float* r, void* x_buf, int32_t* trace,
+                                    void* ws, size_t ws_bytes, moe_stream stream);
+/* moe_pool_decode_step_dev captured as a HIP graph (arguments fixed at
+ * capture; the pool's step lives on the device, so every launch is the next
+ * token).  capture_stream must not be the NULL stream. */
+moe_status moe_pool_graph_create(const moe_layer_desc* desc, const moe_layer_weights* layers, int32_t n_layers,
+                                 moe_devpool* pool, const void* x0, float* r, void* x_buf, int32_t* trace,
+                                 void* ws, size_t ws_bytes, moe_stream capture_stream, moe_graph** out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -92,6 +92,14 @@ PROTOS = {
     "slotpool_destroy": (None, [vp]),
     "slotpool_get_config": (i32, [vp, C.POINTER(SlotPoolConfig)]),
     "moe_read_probe": (i32, [vp, u64, i32, vp, vp]),
+    "moe_devpool_state_bytes": (i32, [C.POINTER(SlotPoolConfig), C.POINTER(C.c_size_t)]),
+    "moe_devpool_create": (i32, [C.POINTER(SlotPoolConfig), vp, C.c_size_t, C.POINTER(vp)]),
+    "moe_devpool_reset": (i32, [vp, vp]),
+    "moe_devpool_acquire": (i32, [vp, i32, vp, i32, i32, vp, vp]),
+    "moe_devpool_stats": (i32, [vp, C.POINTER(SlotPoolStats), C.POINTER(u64), C.POINTER(i32), vp]),
+    "moe_devpool_destroy": (None, [vp]),
+    "moe_pool_decode_step_dev": (i32, [vp, vp, i32, vp, vp, vp, vp, vp, vp, C.c_size_t, vp]),
+    "moe_pool_graph_create": (i32, [vp, vp, i32, vp, vp, vp, vp, vp, vp, C.c_size_t, vp, C.POINTER(vp)]),
     "moe_pool_decode_step": (i32, [vp, vp, i32, vp, u64, vp, vp, vp, vp, vp, i32, vp, C.c_size_t, vp]),
 }
 

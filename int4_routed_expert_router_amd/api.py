@@ -19,7 +19,7 @@ from ._lib import (GdnDesc, MOE_BF16, MOE_F16, MOE_PATH_AUTO, MOE_POOL_DMA_COPY,
 __all__ = ["Desc", "Layer", "blob_bytes", "pack_expert", "workspace_bytes", "workspace", "workspace_status",
            "route", "permute",
            "expert_ffn", "layer_forward", "layer_forward_static", "stack_epilogue", "stack_forward", "StackGraph", "synth_fill_experts",
-           "synth_philox", "SlotPool", "pool_decode_step", "gdn_step"]
+           "synth_philox", "SlotPool", "pool_decode_step", "DevPool", "pool_decode_step_dev", "PoolGraph", "gdn_step"]
 
 
 _ACT_DTYPES = (torch.int16, torch.float16, torch.bfloat16)
@@ -298,6 +298,102 @@ def pool_decode_step(desc, layers, pool, step, x0, r, x_buf, idx_host, ws, prega
     log = None if idx_log is None else idx_log.ctypes.data
     check(lib().moe_pool_decode_step(C.byref(d), arr, L, pool._h, step, *args, log, int(pregate), _ws(ws),
                                      ws.numel(), _stream(stream)))
+
+
+class DevPool:
+    """GPU-resident slot pool (moe_devpool_*): the policy runs on the device,
+    its state lives in a device tensor owned by this object."""
+
+    def __init__(self, n_layers, n_experts, slots, aging_period, blob_stride, blob_bytes_, host_blobs, device_slab,
+                 device_offsets, stream=None):
+        if not isinstance(host_blobs, torch.Tensor) or not host_blobs.is_pinned():
+            raise ValueError("host_blobs must be a pinned host tensor")
+        cfg = SlotPoolConfig(n_layers, n_experts, slots, aging_period, blob_stride, blob_bytes_,
+                             _ptr(host_blobs, "host_blobs", (torch.uint8,), host=True),
+                             _ptr(device_slab, "device_slab", (torch.uint8,)),
+                             _ptr(device_offsets, "device_offsets", (torch.int64,)), None, 0)
+        n = C.c_size_t(0)
+        check(lib().moe_devpool_state_bytes(C.byref(cfg), C.byref(n)))
+        self.state = torch.empty(int(n.value), dtype=torch.uint8, device=device_slab.device)
+        h = C.c_void_p()
+        check(lib().moe_devpool_create(C.byref(cfg), _ptr(self.state), self.state.numel(), C.byref(h)))
+        self._h = h
+        self._keep = (host_blobs, device_slab, device_offsets)
+        self.n_layers, self.n_experts, self.slots = n_layers, n_experts, slots
+        self.reset(stream)
+
+    def reset(self, stream=None):
+        check(lib().moe_devpool_reset(self._h, _stream(stream)))
+
+    def acquire(self, layer, experts, bump_step=False, trace=None, stream=None):
+        """experts: device int32 tensor of ids; trace: device int32 [n, 3] or None."""
+        n = experts.numel()
+        check(lib().moe_devpool_acquire(self._h, layer, _ptr(experts, "experts", _I32, n), n, int(bump_step),
+                                        _ptr(trace, "trace", _I32, 3 * n), _stream(stream)))
+
+    def stats(self, stream=None):
+        s = SlotPoolStats()
+        step = C.c_uint64(0)
+        err = C.c_int32(0)
+        check(lib().moe_devpool_stats(self._h, C.byref(s), C.byref(step), C.byref(err), _stream(stream)))
+        return dict(hits=s.hits, misses=s.misses, evictions=s.evictions, bytes_h2d=s.bytes_h2d,
+                    prefetches=s.prefetches, step=step.value, error=err.value)
+
+    def close(self):
+        if self._h:
+            lib().moe_devpool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _devpool_args(desc, layers, x0, r, x_buf, trace, ws):
+    H, K, L = desc.hidden, desc.top_k, len(layers)
+    return (_ptr(x0, "x0", _ACT_DTYPES, H), _ptr(r, "r", _F32, H), _ptr(x_buf, "x_buf", _ACT_DTYPES, 2 * H),
+            _ptr(trace, "trace", _I32, L * K * 3), _ws(ws), ws.numel())
+
+
+def pool_decode_step_dev(desc, layers, pool, x0, r, x_buf, ws, trace=None, stream=None):
+    """One batch-1 token streamed through a DevPool (moe_pool_decode_step_dev):
+    no host synchronisation; the pool's step advances on the device."""
+    args = _devpool_args(desc, layers, x0, r, x_buf, trace, ws)
+    d = desc.c()
+    arr = _layer_array(layers)
+    check(lib().moe_pool_decode_step_dev(C.byref(d), arr, len(layers), pool._h, *args, _stream(stream)))
+
+
+class PoolGraph:
+    """pool_decode_step_dev captured once (moe_pool_graph_create); every
+    launch() runs the next token."""
+
+    def __init__(self, desc, layers, pool, x0, r, x_buf, ws, capture_stream, trace=None):
+        self._h = None
+        args = _devpool_args(desc, layers, x0, r, x_buf, trace, ws)
+        d = desc.c()
+        arr = _layer_array(layers)
+        h = C.c_void_p()
+        self._keep = (layers, pool, x0, r, x_buf, ws, trace)
+        check(lib().moe_pool_graph_create(C.byref(d), arr, len(layers), pool._h, *args, _stream(capture_stream),
+                                          C.byref(h)))
+        self._h = h
+
+    def launch(self, stream=None):
+        check(lib().moe_graph_launch(self._h, _stream(stream)))
+
+    def close(self):
+        if self._h:
+            lib().moe_graph_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def gdn_step(q, k, v, g, beta, state, o, q_scale, act_dtype="bf16", stream=None):

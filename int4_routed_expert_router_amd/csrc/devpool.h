@@ -1,0 +1,30 @@
+// Internal interface of the GPU-resident slot pool (devpool.hip) for the
+// decode driver (moe_api.cpp).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe_slotpool.h"
+
+namespace moe {
+
+// Layout of the pool's device state (byte offsets): a header (step, hits,
+// misses, evictions, error word), per layer the aging epoch, per layer and
+// expert its slot (-1: not resident), per layer and slot the resident expert
+// (-1: free), its count and last use, and the miss list of the last acquire
+// ([0] = n, then n experts, then from [1 + 64] their slots).
+struct DevPoolGeom {
+  int L, E, S, P;
+  uint64_t stride;
+  size_t o_epoch, o_slot_of, o_expert_in, o_count, o_last_use, o_miss, bytes;
+};
+DevPoolGeom devpool_geom(int L, int E, int S, int P, uint64_t stride);
+
+// The acquire kernel for K device expert ids of `layer`, then the copy
+// kernel of its misses, on s.  bump_step: the pool's step advances after it.
+hipError_t devpool_enqueue_acquire(moe_devpool* p, int layer, const int32_t* idx, int K, bool bump_step,
+                                   int32_t* trace, hipStream_t s);
+const moe_slotpool_config& devpool_config(const moe_devpool* p);
+
+}  // namespace moe

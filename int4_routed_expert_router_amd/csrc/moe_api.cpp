@@ -6,6 +6,7 @@
 #include <cstring>
 #include <vector>
 
+#include "devpool.h"
 #include "moe.h"
 #include "moe_kernels.h"
 #include "moe_slotpool.h"
@@ -745,6 +746,122 @@ moe_status moe_pool_decode_step(const moe_layer_desc* d, const moe_layer_weights
                                        s, rbuf[(L_ - 1) & 1]);
     if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
   }
+  return ok();
+}
+
+static moe_status pool_dev_enqueue(const moe_layer_desc* d, const moe_layer_weights* layers, int32_t L_,
+                                   moe_devpool* pool, const void* x0, float* r, void* x_buf, int32_t* trace,
+                                   void* ws, size_t ws_bytes, hipStream_t s) {
+  moe_status st = check_desc(d);
+  if (st) return st;
+  if (!pool) return fail(MOE_EINVAL, "pool is NULL");
+  if (L_ < 0 || (L_ > 0 && !layers)) return fail(MOE_EINVAL, "bad layer array");
+  if (!x0 || !aligned(x0, 16) || !r || !aligned(r, 16) || !x_buf || !aligned(x_buf, 16))
+    return fail(MOE_EINVAL, "x0, r and x_buf are required (16-byte aligned)");
+  const moe_slotpool_config& pc = moe::devpool_config(pool);
+  if (pc.n_layers < L_ || pc.n_experts != d->n_experts)
+    return fail(MOE_ESHAPE, "pool of %d layers x %d experts does not fit %d layers x %d experts", pc.n_layers,
+                pc.n_experts, L_, d->n_experts);
+  if (d->top_k > pc.slots_per_layer || d->top_k > 64)
+    return fail(MOE_ESHAPE, "top_k=%d exceeds the pool's %d slots per layer (or 64)", d->top_k, pc.slots_per_layer);
+  if (pc.blob_bytes < blob_size(d->hidden, d->inter, d->group_size, wbits(d)))
+    return fail(MOE_ESHAPE, "pool blobs of %llu bytes are smaller than the layer's", (unsigned long long)pc.blob_bytes);
+  if (L_ == 0) return MOE_OK;
+  Ws L;
+  if ((st = check_ws(d, 1, ws, ws_bytes, L))) return st;
+  const int K = d->top_k, H = d->hidden;
+  const uint64_t S = static_cast<uint64_t>(pc.slots_per_layer), E = static_cast<uint64_t>(pc.n_experts);
+  auto pooled = [&](int l) {
+    moe_layer_weights w = layers[l];
+    w.experts = pc.device_slab + static_cast<uint64_t>(l) * S * pc.blob_stride;
+    w.expert_stride = pc.blob_stride;
+    w.expert_offset = pc.device_offsets + static_cast<uint64_t>(l) * E;
+    return w;
+  };
+  for (int l = 0; l < L_; ++l) {
+    moe_layer_weights w = pooled(l);
+    if ((st = check_weights(d, &w))) return fail_layer(st, "layer", l);
+  }
+  int32_t* idx = at<int32_t>(ws, L.idx);
+  float* tw = at<float>(ws, L.w);
+  float* gamma = at<float>(ws, L.gamma);
+  const size_t xbytes = static_cast<size_t>(H) * 2;
+  const bool fold = fold_combine(d, 1);
+  float* rbuf[2] = {r, at<float>(ws, L.rres)};
+  for (int l = 0; l < L_; ++l) {
+    void* xslot = static_cast<char*>(x_buf) + ((l - 1) & 1) * xbytes;
+    const void* xl = (l == 0) ? x0 : xslot;
+    void* xn = static_cast<char*>(x_buf) + (l & 1) * xbytes;
+    const moe_layer_weights w = pooled(l);
+    if (fold && l > 0) {
+      // tw and gamma still hold layer l - 1's values: the top-K below rewrites them
+      moe::RouterParts rp{};
+      const PrevLayer pv{tw, gamma, rbuf[(l - 1) & 1], rbuf[l & 1], nullptr};
+      if ((st = do_router_combine(d, &w, 1, at<float>(ws, L.logits), at<float>(ws, L.yrow), pv, xslot, s, -1, &rp)))
+        return st;
+      hipError_t e = moe::launch_topk(at<float>(ws, L.logits), rp.n_part, rp.biased ? nullptr : w.router_bias, 1,
+                                      d->n_experts, K, idx, tw, gamma, nullptr, s);
+      if (e != hipSuccess) return hip_fail(e, "top-k kernel launch");
+    } else if ((st = do_route(d, &w, xl, 1, idx, tw, gamma, at<float>(ws, L.logits), nullptr, s))) {
+      return st;
+    }
+    hipError_t e = moe::devpool_enqueue_acquire(pool, l, idx, K, l == L_ - 1,
+                                                trace ? trace + static_cast<size_t>(l) * K * 3 : nullptr, s);
+    if (e != hipSuccess) return hip_fail(e, "pool acquire launch");
+    if ((st = do_ffn(d, &w, xl, 1, idx, tw, gamma, nullptr, fold ? nullptr : r, fold ? nullptr : xn, ws, L, s,
+                     l == 0, -1, nullptr, fold)))
+      return st;
+  }
+  if (fold) {
+    hipError_t e = moe::launch_combine(d->act_dtype, at<float>(ws, L.yrow), nullptr, tw, gamma, 1, K, H,
+                                       d->shared_inter > 0, nullptr, r,
+                                       reinterpret_cast<uint16_t*>(static_cast<char*>(x_buf) + ((L_ - 1) & 1) * xbytes),
+                                       s, rbuf[(L_ - 1) & 1]);
+    if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
+  }
+  return MOE_OK;
+}
+
+moe_status moe_pool_decode_step_dev(const moe_layer_desc* d, const moe_layer_weights* layers, int32_t L_,
+                                    moe_devpool* pool, const void* x0, float* r, void* x_buf, int32_t* trace,
+                                    void* ws, size_t ws_bytes, moe_stream stream) {
+  moe_status st = pool_dev_enqueue(d, layers, L_, pool, x0, r, x_buf, trace, ws, ws_bytes,
+                                   reinterpret_cast<hipStream_t>(stream));
+  return st ? st : ok();
+}
+
+moe_status moe_pool_graph_create(const moe_layer_desc* d, const moe_layer_weights* layers, int32_t L_,
+                                 moe_devpool* pool, const void* x0, float* r, void* x_buf, int32_t* trace, void* ws,
+                                 size_t ws_bytes, moe_stream capture_stream, moe_graph** out) {
+  if (!out) return fail(MOE_EINVAL, "out is NULL");
+  if (!capture_stream) return fail(MOE_EINVAL, "graph capture needs a non-NULL stream");
+  *out = nullptr;
+  hipStream_t s = reinterpret_cast<hipStream_t>(capture_stream);
+  hipError_t e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamBeginCapture");
+  moe_status st = pool_dev_enqueue(d, layers, L_, pool, x0, r, x_buf, trace, ws, ws_bytes, s);
+  hipGraph_t g = nullptr;
+  e = hipStreamEndCapture(s, &g);
+  if (st) {
+    if (g) hipGraphDestroy(g);
+    return st;
+  }
+  if (e != hipSuccess) return hip_fail(e, "hipStreamEndCapture");
+  hipGraphExec_t ex = nullptr;
+  e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    hipGraphDestroy(g);
+    return hip_fail(e, "hipGraphInstantiate");
+  }
+  moe_graph* mg = new (std::nothrow) moe_graph;
+  if (!mg) {
+    hipGraphExecDestroy(ex);
+    hipGraphDestroy(g);
+    return fail(MOE_ENOMEM, "graph handle allocation");
+  }
+  mg->graph = g;
+  mg->exec = ex;
+  *out = mg;
   return ok();
 }
 
