@@ -255,3 +255,20 @@ def test_pool_decode_validation_before_any_gpu_work():
                                 None)
     assert st == -1 and b"pregate" in L.moe_last_error()
     pool.close()
+
+
+def test_device_pool_state_size_and_validation():
+    import ctypes as C
+    from int4_routed_expert_router_amd._lib import SlotPoolConfig, lib
+    L = lib()
+    n = C.c_size_t(0)
+    cfg = SlotPoolConfig(48, 512, 128, 32, 1769472, 1769472, None, None, None, None, 0)
+    assert L.moe_devpool_state_bytes(C.byref(cfg), C.byref(n)) == 0
+    # header, epochs, slot table, then per slot expert, count and last use, and the miss list
+    assert n.value >= 48 * 512 * 4 + 48 * 128 * (4 + 4 + 8)
+    bad = SlotPoolConfig(48, 512, 0, 32, 1769472, 1769472, None, None, None, None, 0)
+    assert L.moe_devpool_state_bytes(C.byref(bad), C.byref(n)) == -2
+    h = C.c_void_p()
+    assert L.moe_devpool_create(C.byref(cfg), None, 0, C.byref(h)) == -1      # no host blobs / state
+    big = SlotPoolConfig(1, 4096, 2048, 0, 256, 256, None, None, None, None, 0)
+    assert L.moe_devpool_create(C.byref(big), None, 0, C.byref(h)) == -2      # more than 1024 slots
