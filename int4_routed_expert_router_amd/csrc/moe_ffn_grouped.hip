@@ -604,7 +604,12 @@ __global__ __launch_bounds__(512) void k_gateup_tiles(FfnArgs a) {
   // after the barrier: thread (tile tt, row m, column n) sums the 8 wave
   // slices of gate and up in wave order and applies SwiGLU
   auto reduce = [&](const int pb, const TileOut& o0, const TileOut& o1, const int ntiles) {
-    const int tt = tid >> 8, m = (tid >> 4) & 15, nn = tid & 15;
+    // int8: the thread's indices are formed here; hoisted to the kernel's
+    // start they would stay live across the main loop and spill (int4 keeps
+    // the compiler's placement, which does not spill)
+    int tr = tid;
+    if constexpr (BITS == 8) asm volatile("" : "+v"(tr));
+    const int tt = tr >> 8, m = (tr >> 4) & 15, nn = tr & 15;
     if (tt < ntiles) {
       const TileOut& o = tt == 0 ? o0 : o1;
       const int src = nn + 16 * (m >> 2), e = m & 3;
