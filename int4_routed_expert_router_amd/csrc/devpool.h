@@ -21,10 +21,24 @@ struct DevPoolGeom {
 };
 DevPoolGeom devpool_geom(int L, int E, int S, int P, uint64_t stride);
 
+// The token's routing for an acquire that selects the experts itself: the
+// router's logit slices (n_part slices of [1][E+1], bias when the slices do
+// not hold it) and where the selection's weights and shared gate go.
+struct DevRoute {
+  const float* part;
+  int n_part;
+  const float* bias;
+  float* w;
+  float* gamma;
+};
+
 // The acquire kernel for K device expert ids of `layer`, then the copy
 // kernel of its misses, on s.  bump_step: the pool's step advances after it.
-hipError_t devpool_enqueue_acquire(moe_devpool* p, int layer, const int32_t* idx, int K, bool bump_step,
-                                   int32_t* trace, hipStream_t s);
+// With route, the acquire kernel first runs the top-K selection of the
+// token from route's logits and writes it to idx (and the weights and gate
+// to route's buffers); without it, idx holds the request.
+hipError_t devpool_enqueue_acquire(moe_devpool* p, int layer, int32_t* idx, int K, bool bump_step, int32_t* trace,
+                                   hipStream_t s, const DevRoute* route = nullptr);
 const moe_slotpool_config& devpool_config(const moe_devpool* p);
 
 }  // namespace moe

@@ -8,6 +8,7 @@
 
 #include "moe_common.h"
 #include "moe_slotpool.h"
+#include "moe_topk.h"
 #include "devpool.h"
 
 namespace moe {
@@ -17,8 +18,13 @@ moe_status set_error(moe_status code, const char* fmt, ...);
 namespace {
 
 using moe::DevPoolGeom;
+using moe::DevRoute;
+using moe::TopkIn;
+using moe::load_bias;
+using moe::topk_finish;
+using moe::topk_issue;
 
-constexpr int kMaxSlotsPerLane = 16;   // slots_per_layer <= 1024
+constexpr int kMaxSlotsPerLane = 16;   // slots_per_layer <= 1024 (the kernel is instantiated per slots per lane)
 constexpr int kMissCap = 64;           // top_k <= 64
 
 __device__ __forceinline__ uint64_t* hdr(uint8_t* st) { return reinterpret_cast<uint64_t*>(st); }
@@ -42,26 +48,61 @@ __global__ void k_devpool_reset(uint8_t* st, DevPoolGeom g) {
 // One acquire of `layer` for the K experts at idx (device), at the pool's
 // step: aging, hits, then each miss in request order into the lowest free
 // slot or in place of the unpinned resident expert with the smallest
-// (count, last_use, expert id).  Lane i owns slots i, i + 64, ...; every
-// choice is a wave reduction, so the result is the host policy's, exactly.
-// Writes the layer's device offsets of the loaded experts, the miss list for
-// the copy kernel, the statistics and, when trace is set, [K][3] = (slot,
-// victim or -1, hit).  Ids that are not distinct or not in [0, E) change
-// nothing and set the error word.  bump_step: advance the step afterwards.
+// (count, last_use, expert id).  Lane i owns slots i, i + 64, ... (SPL slots
+// per lane: S <= 64 SPL); every choice is a wave reduction, so the result is
+// the host policy's, exactly.  Writes the layer's device offsets of the
+// loaded experts, the miss list for the copy kernel, the statistics and,
+// when trace is set, [K][3] = (slot, victim or -1, hit).  Ids that are not
+// distinct or not in [0, E) change nothing and set the error word.
+// bump_step: advance the step afterwards.
+//
+// KJ > 0: the kernel first selects the token's experts itself from the
+// router's logit slices (the top-K kernel's code, KJ logits per lane) and
+// writes the selection, weights and shared gate to rt (rt.idx == idx).
+template <int SPL, int KJ>
 __global__ __launch_bounds__(64) void k_devpool_acquire(uint8_t* st, DevPoolGeom g, int layer,
-                                                        const int32_t* __restrict__ idx, int K, int bump_step,
-                                                        uint64_t* __restrict__ offsets, int32_t* __restrict__ trace) {
+                                                        int32_t* __restrict__ idx, int K, int bump_step,
+                                                        uint64_t* __restrict__ offsets, int32_t* __restrict__ trace,
+                                                        DevRoute rt) {
   const int lane = threadIdx.x;
   const int S = g.S, E = g.E;
   uint64_t* h = hdr(st);
-  const uint64_t step = h[0];
   int32_t* slot_of = reinterpret_cast<int32_t*>(st + g.o_slot_of) + static_cast<size_t>(layer) * E;
   int32_t* ein_g = reinterpret_cast<int32_t*>(st + g.o_expert_in) + static_cast<size_t>(layer) * S;
   uint32_t* cnt_g = reinterpret_cast<uint32_t*>(st + g.o_count) + static_cast<size_t>(layer) * S;
   uint64_t* lu_g = reinterpret_cast<uint64_t*>(st + g.o_last_use) + static_cast<size_t>(layer) * S;
   int32_t* miss = reinterpret_cast<int32_t*>(st + g.o_miss);
-  // the request: lane k < K holds expert k
-  const int e = lane < K ? idx[lane] : -1;
+  uint64_t* epoch = reinterpret_cast<uint64_t*>(st + g.o_epoch) + layer;
+  // this layer's slots in registers, and the step and aging epoch: loaded
+  // first, they do not depend on the request
+  const uint64_t step = h[0];
+  const uint64_t e0 = g.P > 0 ? *epoch : 0;
+  int ein[SPL];
+  uint32_t cnt[SPL];
+  uint64_t lu[SPL];
+  bool pin[SPL];
+#pragma unroll
+  for (int j = 0; j < SPL; ++j) {
+    const int s = lane + 64 * j;
+    ein[j] = s < S ? ein_g[s] : -2;   // -2: no slot
+    cnt[j] = s < S ? cnt_g[s] : 0;
+    lu[j] = s < S ? lu_g[s] : 0;
+    pin[j] = false;
+  }
+  int e;
+  if constexpr (KJ > 0) {
+    __shared__ int32_t ssel[kMissCap];
+    TopkIn<KJ> in;
+    topk_issue(rt.part, rt.n_part, 1, E, 0, lane, in);
+    float bj[KJ];
+    load_bias(rt.bias, E, lane, bj);
+    topk_finish(in, bj, rt.bias != nullptr, rt.n_part, E, K, 0, lane, idx, rt.w, rt.gamma, nullptr, ssel);
+    __syncthreads();
+    e = lane < K ? ssel[lane] : -1;
+  } else {
+    // the request: lane k < K holds expert k
+    e = lane < K ? idx[lane] : -1;
+  }
   bool bad = lane < K && (e < 0 || e >= E);
   for (int k = 0; k < K; ++k) {
     const int ek = __builtin_amdgcn_readlane(e, k);
@@ -71,38 +112,36 @@ __global__ __launch_bounds__(64) void k_devpool_acquire(uint8_t* st, DevPoolGeom
     if (lane == 0) h[4] = 1;   // error word
     return;
   }
-  // this layer's slots in registers
-  int ein[kMaxSlotsPerLane];
-  uint32_t cnt[kMaxSlotsPerLane];
-  uint64_t lu[kMaxSlotsPerLane];
-  bool pin[kMaxSlotsPerLane];
-#pragma unroll
-  for (int j = 0; j < kMaxSlotsPerLane; ++j) {
-    const int s = lane + 64 * j;
-    ein[j] = s < S ? ein_g[s] : -2;   // -2: no slot
-    cnt[j] = s < S ? cnt_g[s] : 0;
-    lu[j] = s < S ? lu_g[s] : 0;
-    pin[j] = false;
-  }
   // lazy aging: counts halved once per elapsed aging period
   if (g.P > 0) {
-    uint64_t* epoch = reinterpret_cast<uint64_t*>(st + g.o_epoch) + layer;
-    const uint64_t ep = step / static_cast<uint64_t>(g.P), e0 = *epoch;
+    const uint64_t ep = step / static_cast<uint64_t>(g.P);
     if (ep > e0) {
       const uint64_t d = ep - e0;
 #pragma unroll
-      for (int j = 0; j < kMaxSlotsPerLane; ++j) cnt[j] = d >= 32 ? 0u : (cnt[j] >> d);
+      for (int j = 0; j < SPL; ++j) cnt[j] = d >= 32 ? 0u : (cnt[j] >> d);
       if (lane == 0) *epoch = ep;
     }
   }
-  // hits: count + 1, last use, pinned
-  const int hs = lane < K ? slot_of[e] : -1;
+  // hits: the slot holding each requested expert, found in the slot
+  // registers (the same answer as the expert -> slot table, which the
+  // misses below keep up to date); count + 1, last use, pinned
+  int hs = -1;
+  for (int k = 0; k < K; ++k) {
+    const int ek = __builtin_amdgcn_readlane(e, k);
+    uint32_t found = 0xFFFFFFFFu;
+#pragma unroll
+    for (int j = 0; j < SPL; ++j)
+      if (ein[j] == ek) found = static_cast<uint32_t>(lane + 64 * j);
+    const unsigned long long at = __ballot(found != 0xFFFFFFFFu);
+    const int sk = at == 0ull ? -1 : __builtin_amdgcn_readlane(static_cast<int>(found), __ffsll(at) - 1);
+    if (lane == k) hs = sk;
+  }
   const bool hit = hs >= 0;
   for (int k = 0; k < K; ++k) {
     const int sk = __builtin_amdgcn_readlane(hs, k);
     if (sk < 0) continue;   // uniform
 #pragma unroll
-    for (int j = 0; j < kMaxSlotsPerLane; ++j)
+    for (int j = 0; j < SPL; ++j)
       if (lane + 64 * j == sk) {
         cnt[j] += 1;
         lu[j] = step;
@@ -118,7 +157,7 @@ __global__ __launch_bounds__(64) void k_devpool_acquire(uint8_t* st, DevPoolGeom
     // lowest free slot
     uint32_t free_s = 0xFFFFFFFFu;
 #pragma unroll
-    for (int j = 0; j < kMaxSlotsPerLane; ++j)
+    for (int j = 0; j < SPL; ++j)
       if (ein[j] == -1) free_s = min(free_s, static_cast<uint32_t>(lane + 64 * j));
     free_s = moe::wave_min_u32(free_s);
     int s = static_cast<int>(free_s), victim = -1;
@@ -126,24 +165,24 @@ __global__ __launch_bounds__(64) void k_devpool_acquire(uint8_t* st, DevPoolGeom
       // the unpinned resident expert with the smallest (count, last_use, id)
       uint32_t mc = 0xFFFFFFFFu;
 #pragma unroll
-      for (int j = 0; j < kMaxSlotsPerLane; ++j)
+      for (int j = 0; j < SPL; ++j)
         if (ein[j] >= 0 && !pin[j]) mc = min(mc, cnt[j]);
       mc = moe::wave_min_u32(mc);
       uint32_t mh = 0xFFFFFFFFu;
 #pragma unroll
-      for (int j = 0; j < kMaxSlotsPerLane; ++j)
+      for (int j = 0; j < SPL; ++j)
         if (ein[j] >= 0 && !pin[j] && cnt[j] == mc) mh = min(mh, static_cast<uint32_t>(lu[j] >> 32));
       mh = moe::wave_min_u32(mh);
       uint32_t ml = 0xFFFFFFFFu;
 #pragma unroll
-      for (int j = 0; j < kMaxSlotsPerLane; ++j)
+      for (int j = 0; j < SPL; ++j)
         if (ein[j] >= 0 && !pin[j] && cnt[j] == mc && static_cast<uint32_t>(lu[j] >> 32) == mh)
           ml = min(ml, static_cast<uint32_t>(lu[j]));
       ml = moe::wave_min_u32(ml);
       uint32_t me = 0xFFFFFFFFu;
       const uint64_t mlu = (static_cast<uint64_t>(mh) << 32) | ml;
 #pragma unroll
-      for (int j = 0; j < kMaxSlotsPerLane; ++j)
+      for (int j = 0; j < SPL; ++j)
         if (ein[j] >= 0 && !pin[j] && cnt[j] == mc && lu[j] == mlu) me = min(me, static_cast<uint32_t>(ein[j]));
       me = moe::wave_min_u32(me);   // K <= S, so an unpinned resident expert exists
       if (me == 0xFFFFFFFFu) {       // cannot happen: the launcher checks K <= S
@@ -153,14 +192,14 @@ __global__ __launch_bounds__(64) void k_devpool_acquire(uint8_t* st, DevPoolGeom
       victim = static_cast<int>(me);
       uint32_t vs = 0xFFFFFFFFu;
 #pragma unroll
-      for (int j = 0; j < kMaxSlotsPerLane; ++j)
+      for (int j = 0; j < SPL; ++j)
         if (ein[j] == victim) vs = static_cast<uint32_t>(lane + 64 * j);
       s = static_cast<int>(moe::wave_min_u32(vs));
       if (lane == 0) slot_of[victim] = -1;
       ++n_evict;
     }
 #pragma unroll
-    for (int j = 0; j < kMaxSlotsPerLane; ++j)
+    for (int j = 0; j < SPL; ++j)
       if (lane + 64 * j == s) {
         ein[j] = ek;
         cnt[j] = 1;
@@ -180,7 +219,7 @@ __global__ __launch_bounds__(64) void k_devpool_acquire(uint8_t* st, DevPoolGeom
     ++n_miss;
   }
 #pragma unroll
-  for (int j = 0; j < kMaxSlotsPerLane; ++j) {
+  for (int j = 0; j < SPL; ++j) {
     const int s = lane + 64 * j;
     if (s < S) {
       ein_g[s] = ein[j];
@@ -259,12 +298,37 @@ DevPoolGeom devpool_geom(int L, int E, int S, int P, uint64_t stride) {
   return g;
 }
 
-hipError_t devpool_enqueue_acquire(moe_devpool* p, int layer, const int32_t* idx, int K, bool bump_step,
-                                   int32_t* trace, hipStream_t s) {
+template <int SPL>
+static void launch_acquire(moe_devpool* p, int layer, int32_t* idx, int K, bool bump_step, int32_t* trace,
+                           const DevRoute& rt, hipStream_t s) {
+  const moe_slotpool_config& c = p->cfg;
+  const uint64_t E = static_cast<uint64_t>(c.n_experts);
+  uint64_t* off = c.device_offsets + layer * E;
+  const int b = bump_step ? 1 : 0;
+#define ACQ_LAUNCH(J) \
+  hipLaunchKernelGGL((k_devpool_acquire<SPL, J>), dim3(1), dim3(64), 0, s, p->state, p->g, layer, idx, K, b, off, trace, rt)
+  if (rt.part == nullptr) ACQ_LAUNCH(0);
+  else if (E <= 64) ACQ_LAUNCH(1);
+  else if (E <= 128) ACQ_LAUNCH(2);
+  else if (E <= 256) ACQ_LAUNCH(4);
+  else if (E <= 512) ACQ_LAUNCH(8);
+  else ACQ_LAUNCH(16);
+#undef ACQ_LAUNCH
+}
+
+hipError_t devpool_enqueue_acquire(moe_devpool* p, int layer, int32_t* idx, int K, bool bump_step, int32_t* trace,
+                                   hipStream_t s, const DevRoute* route) {
   const moe_slotpool_config& c = p->cfg;
   const uint64_t S = static_cast<uint64_t>(c.slots_per_layer), E = static_cast<uint64_t>(c.n_experts);
-  hipLaunchKernelGGL(k_devpool_acquire, dim3(1), dim3(64), 0, s, p->state, p->g, layer, idx, K, bump_step ? 1 : 0,
-                     c.device_offsets + layer * E, trace);
+  const DevRoute rt = route != nullptr ? *route : DevRoute{};
+  if (rt.part != nullptr && (c.n_experts > moe::kMaxExperts || rt.w == nullptr || rt.gamma == nullptr))
+    return hipErrorInvalidValue;
+  const int spl = static_cast<int>((S + 63) / 64);
+  if (spl <= 1) launch_acquire<1>(p, layer, idx, K, bump_step, trace, rt, s);
+  else if (spl <= 2) launch_acquire<2>(p, layer, idx, K, bump_step, trace, rt, s);
+  else if (spl <= 4) launch_acquire<4>(p, layer, idx, K, bump_step, trace, rt, s);
+  else if (spl <= 8) launch_acquire<8>(p, layer, idx, K, bump_step, trace, rt, s);
+  else launch_acquire<kMaxSlotsPerLane>(p, layer, idx, K, bump_step, trace, rt, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_copy_listed, dim3(kCopySlices, K), dim3(256), 0, s, p->host_dev + layer * E * c.blob_stride,
@@ -336,7 +400,7 @@ moe_status moe_devpool_acquire(moe_devpool* p, int32_t layer, const int32_t* exp
   if (layer < 0 || layer >= p->cfg.n_layers) return set_error(MOE_EINVAL, "layer %d out of range", layer);
   if (n < 1 || n > kMissCap || n > p->cfg.slots_per_layer || !experts)
     return set_error(MOE_EINVAL, "need 1 <= n <= min(64, slots_per_layer) device expert ids");
-  const hipError_t e = moe::devpool_enqueue_acquire(p, layer, experts, n, bump_step != 0, trace,
+  const hipError_t e = moe::devpool_enqueue_acquire(p, layer, const_cast<int32_t*>(experts), n, bump_step != 0, trace,
                                                    reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return set_error(MOE_EHIP, "pool acquire launch: %s", hipGetErrorString(e));
   return set_error(MOE_OK, "");

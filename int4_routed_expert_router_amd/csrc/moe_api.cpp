@@ -793,20 +793,20 @@ static moe_status pool_dev_enqueue(const moe_layer_desc* d, const moe_layer_weig
     const void* xl = (l == 0) ? x0 : xslot;
     void* xn = static_cast<char*>(x_buf) + (l & 1) * xbytes;
     const moe_layer_weights w = pooled(l);
+    moe::RouterParts rp{};
     if (fold && l > 0) {
-      // tw and gamma still hold layer l - 1's values: the top-K below rewrites them
-      moe::RouterParts rp{};
+      // tw and gamma still hold layer l - 1's values: the selection below rewrites them
       const PrevLayer pv{tw, gamma, rbuf[(l - 1) & 1], rbuf[l & 1], nullptr};
       if ((st = do_router_combine(d, &w, 1, at<float>(ws, L.logits), at<float>(ws, L.yrow), pv, xslot, s, -1, &rp)))
         return st;
-      hipError_t e = moe::launch_topk(at<float>(ws, L.logits), rp.n_part, rp.biased ? nullptr : w.router_bias, 1,
-                                      d->n_experts, K, idx, tw, gamma, nullptr, s);
-      if (e != hipSuccess) return hip_fail(e, "top-k kernel launch");
-    } else if ((st = do_route(d, &w, xl, 1, idx, tw, gamma, at<float>(ws, L.logits), nullptr, s))) {
+    } else if ((st = do_router(d, &w, xl, 1, at<float>(ws, L.logits), s, -1, &rp))) {
       return st;
     }
+    // the pool's policy kernel selects the token's experts itself (the top-K
+    // kernel's code) and then acquires them
+    const moe::DevRoute rt{at<float>(ws, L.logits), rp.n_part, rp.biased ? nullptr : w.router_bias, tw, gamma};
     hipError_t e = moe::devpool_enqueue_acquire(pool, l, idx, K, l == L_ - 1,
-                                                trace ? trace + static_cast<size_t>(l) * K * 3 : nullptr, s);
+                                                trace ? trace + static_cast<size_t>(l) * K * 3 : nullptr, s, &rt);
     if (e != hipSuccess) return hip_fail(e, "pool acquire launch");
     if ((st = do_ffn(d, &w, xl, 1, idx, tw, gamma, nullptr, fold ? nullptr : r, fold ? nullptr : xn, ws, L, s,
                      l == 0, -1, nullptr, fold)))
