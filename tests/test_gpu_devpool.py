@@ -98,6 +98,41 @@ def test_device_pool_trace_and_placement(slots, period):
     pool.close()
 
 
+@pytest.mark.parametrize("n_experts,top_k,slots,period", [(300, 16, 200, 4), (350, 32, 300, 0), (700, 64, 600, 3)],
+                         ids=["4_slots_per_lane", "8_slots_per_lane", "16_slots_per_lane_E700_K64"])
+def test_device_pool_larger_pools(n_experts, top_k, slots, period):
+    """The policy kernel is instantiated per slots per lane (1, 2, 4, 8, 16)
+    and selects the token's experts itself (8 or 16 logits per lane): pools
+    of 200 to 600 slots per layer, up to 64 experts per token, trace equal to
+    the pool simulator's and the streamed stack equal to the resident one."""
+    import torch
+    from int4_routed_expert_router_amd import api
+    wl = dataclasses.replace(synth.TINY, name="pooled_big", hidden=64, inter=64, shared_inter=64, group=32,
+                             n_experts=n_experts, top_k=top_k, tokens=1, layers=2, weight_seed=43, token_seed=143,
+                             router_sigma=0.5, zipf_s=0.0)   # diverse selections, so the pools fill and evict
+    rig = DevPoolRig(wl, slots, period)
+    pool = rig.pool()
+    sim = PoolSim(wl.layers, wl.n_experts, slots, period, blob_bytes=rig.blob)
+    L, K, H = wl.layers, wl.top_k, wl.hidden
+    ws = api.workspace(rig.desc, 1)
+    x_buf = torch.empty(2, H, dtype=torch.int16, device="cuda")
+    trace = torch.full((L, K, 3), -9, dtype=torch.int32, device="cuda")
+    steps = 24
+    for step in range(steps):
+        x0 = torch.from_numpy(synth.tokens(wl, step=step).view(np.int16).copy()).cuda()
+        r = x0.view(torch.float16).float().reshape(-1)
+        api.pool_decode_step_dev(rig.desc, rig.layers, pool, x0, r, x_buf, ws, trace=trace)
+        torch.cuda.synchronize()
+        r_ref, x_ref, sel = rig.resident(x0)
+        assert np.array_equal(r.cpu().numpy(), r_ref), f"step {step}: residual differs from the resident stack"
+        check_trace(sim, step, sel, trace.cpu().numpy())
+    st = pool.stats()
+    want = sim.stats()
+    assert (st["hits"], st["misses"], st["evictions"]) == (want["hits"], want["misses"], want["evictions"])
+    assert st["evictions"] > 0 and st["error"] == 0, st
+    pool.close()
+
+
 def test_device_pool_graph_replays_token_after_token():
     """One captured token graph launched once per token (the input copied into
     the captured x0 buffer between launches): the same residuals, next inputs
