@@ -379,8 +379,13 @@ __device__ __forceinline__ void staged_barrier() {
 // FULL: H is the family's largest (2048, 32 chunks), so every chunk w + 8 j
 // a wave forms is in range and the product loop carries no range tests.
 // ---------------------------------------------------------------------------
-template <int ACT, int G, int BITS, bool FULL>
-__global__ __launch_bounds__(512) void k_gateup_tiles(FfnArgs a) {
+template <int ACT, int G, int BITS, bool FULL, int NW>
+__global__ __launch_bounds__(64 * NW) void k_gateup_tiles(FfnArgs a) {
+  // NW waves split each tile's chunks: NW = 8 takes 4 chunks per wave and
+  // tile (two waves per SIMD), NW = 16 takes 2 (four waves per SIMD, half the
+  // registers per wave)
+  constexpr int kWaves = NW;
+  constexpr int kSlot = 32 / NW;
   constexpr int NQ = BITS / 4;   // 16-byte weight loads per lane and chunk
   // tiles are processed in pairs (one barrier per pair); the two tiles of a
   // pair use the two slot groups, so kDepth = 2 tiles are in flight per wave
@@ -389,8 +394,9 @@ __global__ __launch_bounds__(512) void k_gateup_tiles(FfnArgs a) {
   // partial tiles of a pair: buffer, tile, wave, gate / up, row e, lane.  The
   // row stride of 80 floats puts rows e and e + 1 on opposite bank halves, so
   // the reduction reads (64 lanes: 4 rows x 16 consecutive lanes) take the
-  // minimum two LDS cycles.
-  constexpr int kRowStride = 80;
+  // minimum two LDS cycles; with 16 waves the stride is 72 (two-way
+  // conflicts) so that the partials fit the 160 KB of LDS.
+  constexpr int kRowStride = NW == 8 ? 80 : 72;
   __shared__ float red[2][2][kWaves][2][4][kRowStride];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, kb = lane >> 4;
@@ -601,7 +607,7 @@ __global__ __launch_bounds__(512) void k_gateup_tiles(FfnArgs a) {
     advance(cc);
     return out;
   };
-  // after the barrier: thread (tile tt, row m, column n) sums the 8 wave
+  // after the barrier: thread (tile tt, row m, column n) sums the wave
   // slices of gate and up in wave order and applies SwiGLU
   auto reduce = [&](const int pb, const TileOut& o0, const TileOut& o1, const int ntiles) {
     // int8: the thread's indices are formed here; hoisted to the kernel's
@@ -878,18 +884,31 @@ static bool full_shape(const FfnArgs& a) {
   return a.H == kGroupedMaxH && a.I == kGroupedMaxInter && (a.Is == kGroupedMaxInter || a.Is == 0);
 }
 
-hipError_t launch_gateup_grouped(int act, const FfnArgs& a, hipStream_t s) {
+// 16 waves where that form needs no more than its 128 registers per lane
+// (bf16 activations, int4, group 64 or 128, the full shape); 8 elsewhere.
+template <int A, int G, int B>
+static void launch_gateup_t(const FfnArgs& a, hipStream_t s) {
   const bool full = a.H == kGroupedMaxH;
-#define GU_LAUNCH(A_, G_, B_)                                                                              \
-  do {                                                                                                     \
-    if (full) hipLaunchKernelGGL((k_gateup_tiles<A_, G_, B_, true>), dim3(kGridTiles), dim3(512), 0, s, a); \
-    else hipLaunchKernelGGL((k_gateup_tiles<A_, G_, B_, false>), dim3(kGridTiles), dim3(512), 0, s, a);     \
-  } while (0)
-#define GU_G(A_, B_)                      \
-  do {                                    \
-    if (a.G == 32) GU_LAUNCH(A_, 32, B_); \
-    else if (a.G == 64) GU_LAUNCH(A_, 64, B_); \
-    else GU_LAUNCH(A_, 128, B_);          \
+  if constexpr (A == 2 && B == 4 && G >= 64) {
+    if (full) {
+      hipLaunchKernelGGL((k_gateup_tiles<A, G, B, true, 16>), dim3(kGridTiles), dim3(1024), 0, s, a);
+      return;
+    }
+  } else {
+    if (full) {
+      hipLaunchKernelGGL((k_gateup_tiles<A, G, B, true, 8>), dim3(kGridTiles), dim3(512), 0, s, a);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((k_gateup_tiles<A, G, B, false, 8>), dim3(kGridTiles), dim3(512), 0, s, a);
+}
+
+hipError_t launch_gateup_grouped(int act, const FfnArgs& a, hipStream_t s) {
+#define GU_G(A_, B_)                                   \
+  do {                                                 \
+    if (a.G == 32) launch_gateup_t<A_, 32, B_>(a, s);  \
+    else if (a.G == 64) launch_gateup_t<A_, 64, B_>(a, s); \
+    else launch_gateup_t<A_, 128, B_>(a, s);           \
   } while (0)
   if (a.bits == 8) {
     if (act == 2) GU_G(2, 8);
@@ -899,7 +918,6 @@ hipError_t launch_gateup_grouped(int act, const FfnArgs& a, hipStream_t s) {
     else GU_G(1, 4);
   }
 #undef GU_G
-#undef GU_LAUNCH
   return hipGetLastError();
 }
 
