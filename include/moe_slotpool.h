@@ -182,10 +182,13 @@ void moe_devpool_destroy(moe_devpool* pool);
 
 /* One batch-1 decode token through n_layers layers streamed through a
  * GPU-resident pool, enqueued on stream with no host synchronisation:
- * per layer, route (the router of layers after the first also combines the
- * previous layer, as in moe_stack_forward), top-K, moe_devpool_acquire of
- * the selection (the last layer's advances the step), the expert FFN from
- * the pool's slots; then the last combine.  Arguments as for
+ * per layer, the router (that of layers after the first also combines the
+ * previous layer, as in moe_stack_forward); the pool's acquire, whose kernel
+ * first selects the token's top-K experts from the router's logits (the
+ * same selection as moe_route) and then applies the policy of
+ * moe_devpool_acquire to them (the last layer's advances the step); the
+ * copies of the misses; the expert FFN from the pool's slots; then the last
+ * combine.  Arguments as for
  * moe_pool_decode_step (layers' experts / stride / offsets come from the
  * pool); trace (device, [n_layers][top_k][3] int32 or NULL) receives every
  * layer's acquire trace.  The call can be captured (moe_pool_graph_create). */
