@@ -175,18 +175,23 @@ moe_status moe_pack_expert(int32_t hidden, int32_t inter, int32_t group_size,
 moe_status moe_workspace_bytes(const moe_layer_desc* desc, int32_t n_tokens, size_t* bytes);
 
 /* Status word of a call.  moe_expert_ffn, moe_layer_forward,
- * moe_stack_forward (and its graphs) and moe_pool_decode_step clear a
- * uint32 status word inside the workspace at their start (in their first
- * FFN kernel) and their kernels set flags in it:
- *   MOE_FLAG_F16_RANGE  a grouped-family operand (an activation or a SwiGLU
- *                       output) fell outside the fp16 range: the outputs of
- *                       the call are not valid (run such inputs with
- *                       MOE_PATH_GEMV).
+ * moe_stack_forward (and its graphs), moe_pool_decode_step and
+ * moe_pool_decode_step_dev (and its graphs) clear a uint32 status word
+ * inside the workspace at their start (in their first FFN kernel) and their
+ * kernels set flags in it:
+ *   MOE_FLAG_F16_RANGE    a grouped-family operand (an activation or a
+ *                         SwiGLU output) fell outside the fp16 range: the
+ *                         outputs of the call are not valid (run such inputs
+ *                         with MOE_PATH_GEMV).
+ *   MOE_FLAG_STREAM_WAIT  a streamed decode's gate/up product gave up
+ *                         waiting (about 0.1 s) for its expert's copy: the
+ *                         outputs of the call are not valid.
  * moe_workspace_status returns the byte offset of the word in a workspace
  * laid out for (desc, n_tokens); read it (device memory) after the call's
  * stream has been synchronised.  Calls that overlap on one workspace race on
  * it, as they do on the rest of the workspace. */
 #define MOE_FLAG_F16_RANGE 1u
+#define MOE_FLAG_STREAM_WAIT 2u
 moe_status moe_workspace_status(const moe_layer_desc* desc, int32_t n_tokens, size_t* offset);
 
 /* Router GEMV (shared-gate row fused), top-K with lower-index tie-break,

@@ -156,7 +156,8 @@ void slotpool_destroy(moe_slotpool* pool);
  * so there are no separate copy-stream events.
  *   cfg:   as for slotpool_create; copy_stream is not used; flags must be 0;
  *          host_blobs must be pinned host memory with a device mapping;
- *          slots_per_layer <= min(n_experts, 1024)
+ *          blob_bytes a multiple of 16; slots_per_layer <= min(n_experts,
+ *          1024)
  *   state: caller-owned device memory of moe_devpool_state_bytes() bytes
  *          (256-byte aligned) holding the residency tables, counts, the step
  *          and the statistics; moe_devpool_reset gives the empty pool. */
@@ -187,8 +188,14 @@ void moe_devpool_destroy(moe_devpool* pool);
  * first selects the token's top-K experts from the router's logits (the
  * same selection as moe_route) and then applies the policy of
  * moe_devpool_acquire to them (the last layer's advances the step); the
- * copies of the misses; the expert FFN from the pool's slots; then the last
- * combine.  Arguments as for
+ * expert FFN from the pool's slots, whose gate/up kernel also copies the
+ * misses (the gate/up sections of every missed blob first: a missed
+ * expert's products wait for its sections, the others do not; then the
+ * down sections, complete before down runs; a desc that forces the grouped
+ * family copies with the copy kernel after the acquire); then the last
+ * combine.  A
+ * wait that gives up sets MOE_FLAG_STREAM_WAIT in the call's status word
+ * (moe.h).  Arguments as for
  * moe_pool_decode_step (layers' experts / stride / offsets come from the
  * pool); trace (device, [n_layers][top_k][3] int32 or NULL) receives every
  * layer's acquire trace.  The call can be captured (moe_pool_graph_create). */

@@ -17,6 +17,7 @@ MOE_POOL_HOST_ONLY = 1
 MOE_POOL_DMA_COPY = 2
 MOE_TIME_GATEUP, MOE_TIME_DOWN, MOE_TIME_ROUTER = 0, 1, 2
 MOE_FLAG_F16_RANGE = 1
+MOE_FLAG_STREAM_WAIT = 2
 
 STATUS_NAMES = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_ESHAPE", -3: "MOE_EWORKSPACE", -4: "MOE_EHIP",
                 -5: "MOE_EPOOLFULL", -6: "MOE_EBUSY", -7: "MOE_ENOMEM"}

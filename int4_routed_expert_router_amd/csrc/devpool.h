@@ -5,6 +5,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "blob_copy.h"
 #include "moe_slotpool.h"
 
 namespace moe {
@@ -13,7 +14,9 @@ namespace moe {
 // misses, evictions, error word), per layer the aging epoch, per layer and
 // expert its slot (-1: not resident), per layer and slot the resident expert
 // (-1: free), its count and last use, and the miss list of the last acquire
-// ([0] = n, then n experts, then from [1 + 64] their slots).
+// ([0] = n, then n experts, from [1 + 64] their slots, from [1 + 128] each
+// request's list entry (-1: a hit), from [1 + 192] the copy counters of a
+// streamed FFN, cleared by the acquire).
 struct DevPoolGeom {
   int L, E, S, P;
   uint64_t stride;
@@ -32,13 +35,21 @@ struct DevRoute {
   float* gamma;
 };
 
-// The acquire kernel for K device expert ids of `layer`, then the copy
-// kernel of its misses, on s.  bump_step: the pool's step advances after it.
-// With route, the acquire kernel first runs the top-K selection of the
-// token from route's logits and writes it to idx (and the weights and gate
-// to route's buffers); without it, idx holds the request.
+// The miss copy of `layer`'s last acquire (list, source and destination
+// set; no byte ranges).
+BlobCopy devpool_miss_copy(const moe_devpool* p, int layer);
+// The same as a streamed FFN's copy (both parts without ranges), with the
+// acquire's per-request list entries and the copy counters it cleared.
+StreamCopy devpool_stream_copy(const moe_devpool* p, int layer);
+// The acquire kernel for K device expert ids of `layer`, then (copy) the
+// copy kernel of its misses, on s.  bump_step: the pool's step advances
+// after it.  With route, the acquire kernel first runs the top-K selection
+// of the token from route's logits and writes it to idx (and the weights
+// and gate to route's buffers); without it, idx holds the request.  Without
+// copy the caller copies the misses (devpool_stream_copy) before they are
+// read.
 hipError_t devpool_enqueue_acquire(moe_devpool* p, int layer, int32_t* idx, int K, bool bump_step, int32_t* trace,
-                                   hipStream_t s, const DevRoute* route = nullptr);
+                                   hipStream_t s, const DevRoute* route = nullptr, bool copy = true);
 const moe_slotpool_config& devpool_config(const moe_devpool* p);
 
 }  // namespace moe

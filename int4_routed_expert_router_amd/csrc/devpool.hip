@@ -6,6 +6,7 @@
 
 #include <new>
 
+#include "blob_copy.h"
 #include "moe_common.h"
 #include "moe_slotpool.h"
 #include "moe_topk.h"
@@ -42,7 +43,8 @@ __global__ void k_devpool_reset(uint8_t* st, DevPoolGeom g) {
     reinterpret_cast<uint32_t*>(st + g.o_count)[i] = 0;
     reinterpret_cast<uint64_t*>(st + g.o_last_use)[i] = 0;
   }
-  for (size_t i = tid; i < 1 + 2 * kMissCap; i += nth) reinterpret_cast<int32_t*>(st + g.o_miss)[i] = 0;
+  for (size_t i = tid; i < 1 + 4 * kMissCap; i += nth)
+    reinterpret_cast<int32_t*>(st + g.o_miss)[i] = (i >= 1 + 2 * kMissCap && i < 1 + 3 * kMissCap) ? -1 : 0;
 }
 
 // One acquire of `layer` for the K experts at idx (device), at the pool's
@@ -72,7 +74,14 @@ __global__ __launch_bounds__(64) void k_devpool_acquire(uint8_t* st, DevPoolGeom
   uint32_t* cnt_g = reinterpret_cast<uint32_t*>(st + g.o_count) + static_cast<size_t>(layer) * S;
   uint64_t* lu_g = reinterpret_cast<uint64_t*>(st + g.o_last_use) + static_cast<size_t>(layer) * S;
   int32_t* miss = reinterpret_cast<int32_t*>(st + g.o_miss);
+  int32_t* entry_of = miss + 1 + 2 * kMissCap;
+  uint32_t* ready = reinterpret_cast<uint32_t*>(miss + 1 + 3 * kMissCap);
   uint64_t* epoch = reinterpret_cast<uint64_t*>(st + g.o_epoch) + layer;
+  // an empty miss list until this acquire has placed its misses (so an
+  // error return copies nothing), no request waiting, no copy counted
+  if (lane == 0) miss[0] = 0;
+  entry_of[lane] = -1;
+  ready[lane] = 0u;
   // this layer's slots in registers, and the step and aging epoch: loaded
   // first, they do not depend on the request
   const uint64_t step = h[0];
@@ -149,7 +158,7 @@ __global__ __launch_bounds__(64) void k_devpool_acquire(uint8_t* st, DevPoolGeom
       }
   }
   // misses in request order
-  int my_slot = hs, my_victim = -1;
+  int my_slot = hs, my_victim = -1, my_entry = -1;
   int n_miss = 0, n_evict = 0;
   for (int k = 0; k < K; ++k) {
     if (__builtin_amdgcn_readlane(hs, k) >= 0) continue;   // a hit (uniform)
@@ -215,6 +224,7 @@ __global__ __launch_bounds__(64) void k_devpool_acquire(uint8_t* st, DevPoolGeom
     if (lane == k) {
       my_slot = s;
       my_victim = victim;
+      my_entry = n_miss;
     }
     ++n_miss;
   }
@@ -227,6 +237,7 @@ __global__ __launch_bounds__(64) void k_devpool_acquire(uint8_t* st, DevPoolGeom
       lu_g[s] = lu[j];
     }
   }
+  if (lane < K) entry_of[lane] = my_entry;
   if (trace != nullptr && lane < K) {
     trace[3 * lane] = my_slot;
     trace[3 * lane + 1] = my_victim;
@@ -241,31 +252,12 @@ __global__ __launch_bounds__(64) void k_devpool_acquire(uint8_t* st, DevPoolGeom
   }
 }
 
-// Copies of the blobs on the miss list (expert e of the layer -> slot s):
-// blockIdx.y = entry of the list (entries past its length return at once),
-// blockIdx.x = contiguous slice of the blob; every thread keeps kCopyDepth
-// 16-byte host reads in flight.
-constexpr int kCopySlices = 64;
-constexpr int kCopyDepth = 4;
-__global__ __launch_bounds__(256) void k_copy_listed(const uint8_t* __restrict__ host, uint8_t* __restrict__ dev,
-                                                     uint64_t stride, uint64_t bytes, const int32_t* __restrict__ miss) {
-  const int i = blockIdx.y;
-  if (i >= miss[0]) return;
-  const uint4* src = reinterpret_cast<const uint4*>(host + static_cast<uint64_t>(miss[1 + i]) * stride);
-  uint4* dst = reinterpret_cast<uint4*>(dev + static_cast<uint64_t>(miss[1 + kMissCap + i]) * stride);
-  const uint64_t n16 = bytes / 16;
-  const uint64_t per = (n16 + kCopySlices - 1) / kCopySlices;
-  const uint64_t k0 = blockIdx.x * per;
-  const uint64_t k1 = k0 + per < n16 ? k0 + per : n16;
-  for (uint64_t k = k0 + threadIdx.x; k < k1; k += kCopyDepth * 256) {
-    uint4 v[kCopyDepth];
-#pragma unroll
-    for (int d = 0; d < kCopyDepth; ++d)
-      if (k + d * 256 < k1) v[d] = src[k + d * 256];
-#pragma unroll
-    for (int d = 0; d < kCopyDepth; ++d)
-      if (k + d * 256 < k1) dst[k + d * 256] = v[d];
-  }
+// The miss copies: the listed blobs' byte ranges, cut into equal pieces over
+// the grid (entries past the list's length take no piece).
+constexpr int kCopyWgs = 256;
+__global__ __launch_bounds__(256) void k_copy_listed(moe::BlobCopy c) {
+  uint64_t k0, k1;
+  moe::blob_copy_part<256>(c, blockIdx.x, gridDim.x, k0, k1);
 }
 
 }  // namespace
@@ -293,7 +285,7 @@ DevPoolGeom devpool_geom(int L, int E, int S, int P, uint64_t stride) {
   g.o_expert_in = o; o += al(static_cast<size_t>(L) * S * 4);
   g.o_count = o; o += al(static_cast<size_t>(L) * S * 4);
   g.o_last_use = o; o += al(static_cast<size_t>(L) * S * 8);
-  g.o_miss = o; o += al((1 + 2 * kMissCap) * 4);
+  g.o_miss = o; o += al((1 + 4 * kMissCap) * 4);
   g.bytes = o;
   return g;
 }
@@ -316,10 +308,31 @@ static void launch_acquire(moe_devpool* p, int layer, int32_t* idx, int K, bool 
 #undef ACQ_LAUNCH
 }
 
-hipError_t devpool_enqueue_acquire(moe_devpool* p, int layer, int32_t* idx, int K, bool bump_step, int32_t* trace,
-                                   hipStream_t s, const DevRoute* route) {
+BlobCopy devpool_miss_copy(const moe_devpool* p, int layer) {
   const moe_slotpool_config& c = p->cfg;
   const uint64_t S = static_cast<uint64_t>(c.slots_per_layer), E = static_cast<uint64_t>(c.n_experts);
+  BlobCopy b{};
+  b.host = p->host_dev + layer * E * c.blob_stride;
+  b.dev = c.device_slab + layer * S * c.blob_stride;
+  b.stride = c.blob_stride;
+  b.list = reinterpret_cast<const int32_t*>(p->state + p->g.o_miss);
+  b.cap = kMissCap;
+  return b;
+}
+
+StreamCopy devpool_stream_copy(const moe_devpool* p, int layer) {
+  StreamCopy c{};
+  c.first = c.second = devpool_miss_copy(p, layer);
+  int32_t* miss = reinterpret_cast<int32_t*>(p->state + p->g.o_miss);
+  c.entry_of = miss + 1 + 2 * kMissCap;
+  c.ready = reinterpret_cast<uint32_t*>(miss + 1 + 3 * kMissCap);
+  return c;
+}
+
+hipError_t devpool_enqueue_acquire(moe_devpool* p, int layer, int32_t* idx, int K, bool bump_step, int32_t* trace,
+                                   hipStream_t s, const DevRoute* route, bool copy) {
+  const moe_slotpool_config& c = p->cfg;
+  const uint64_t S = static_cast<uint64_t>(c.slots_per_layer);
   const DevRoute rt = route != nullptr ? *route : DevRoute{};
   if (rt.part != nullptr && (c.n_experts > moe::kMaxExperts || rt.w == nullptr || rt.gamma == nullptr))
     return hipErrorInvalidValue;
@@ -330,10 +343,10 @@ hipError_t devpool_enqueue_acquire(moe_devpool* p, int layer, int32_t* idx, int 
   else if (spl <= 8) launch_acquire<8>(p, layer, idx, K, bump_step, trace, rt, s);
   else launch_acquire<kMaxSlotsPerLane>(p, layer, idx, K, bump_step, trace, rt, s);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_copy_listed, dim3(kCopySlices, K), dim3(256), 0, s, p->host_dev + layer * E * c.blob_stride,
-                     c.device_slab + layer * S * c.blob_stride, c.blob_stride, c.blob_bytes,
-                     reinterpret_cast<const int32_t*>(p->state + p->g.o_miss));
+  if (e != hipSuccess || !copy) return e;
+  BlobCopy b = devpool_miss_copy(p, layer);
+  b.len[0] = c.blob_bytes;   // a multiple of 16 (checked at creation)
+  hipLaunchKernelGGL(k_copy_listed, dim3(kCopyWgs), dim3(256), 0, s, b);
   return hipGetLastError();
 }
 
@@ -364,8 +377,9 @@ moe_status moe_devpool_create(const moe_slotpool_config* c, void* state, size_t 
     return set_error(MOE_ESHAPE, "slots_per_layer=%d must be <= n_experts=%d and <= %d", c->slots_per_layer,
                      c->n_experts, 64 * kMaxSlotsPerLane);
   if (c->flags != 0) return set_error(MOE_EINVAL, "flags must be 0 (the device pool copies with its copy kernel)");
-  if (c->blob_stride == 0 || c->blob_stride % 256 || c->blob_bytes == 0 || c->blob_bytes > c->blob_stride)
-    return set_error(MOE_EINVAL, "blob_stride must be a positive multiple of 256 and >= blob_bytes");
+  if (c->blob_stride == 0 || c->blob_stride % 256 || c->blob_bytes == 0 || c->blob_bytes % 16 ||
+      c->blob_bytes > c->blob_stride)
+    return set_error(MOE_EINVAL, "blob_stride must be a positive multiple of 256 and >= blob_bytes, a multiple of 16");
   if (!c->host_blobs || !c->device_slab || !c->device_offsets)
     return set_error(MOE_EINVAL, "host_blobs, device_slab and device_offsets are required");
   if (reinterpret_cast<uintptr_t>(c->device_slab) % 256) return set_error(MOE_EINVAL, "device_slab must be 256-byte aligned");

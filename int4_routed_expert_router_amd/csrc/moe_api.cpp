@@ -7,6 +7,7 @@
 #include <vector>
 
 #include "devpool.h"
+#include "moe_common.h"
 #include "moe.h"
 #include "moe_kernels.h"
 #include "moe_slotpool.h"
@@ -52,7 +53,7 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 // weight_bits 0 means 4 (a zero-initialised descriptor describes int4 experts)
 int wbits(const moe_layer_desc* d) { return d->weight_bits == 8 ? 8 : 4; }
-uint64_t blob_size(int H, int I, int G, int bits) { return 3ull * I * H * bits / 8 + 12ull * I * H / G; }
+using moe::blob_size;
 
 bool grouped_fits(const moe_layer_desc* d);
 
@@ -221,8 +222,12 @@ moe_status do_router_combine(const moe_layer_desc* d, const moe_layer_weights* w
 moe_status do_ffn(const moe_layer_desc* d, const moe_layer_weights* w, const void* x, int T, const int32_t* idx,
                   const float* tw, const float* gamma, float* y, float* r, void* x_next, void* ws, const Ws& L,
                   hipStream_t s, bool reset_status, int layer = -1, const FusedTopk* fz = nullptr,
-                  bool skip_combine = false) {
+                  bool skip_combine = false, const moe::StreamCopy* streamed = nullptr) {
   moe::FfnArgs a{};
+  // a streamed FFN's copies run in the GEMV gate/up kernel
+  if (streamed != nullptr && (use_grouped(d, T) || fz != nullptr))
+    return fail(MOE_EINVAL, "a streamed FFN needs the GEMV family without the fused top-K");
+  if (streamed != nullptr) a.stream = *streamed;
   a.status = at<uint32_t>(ws, L.status);
   a.x = static_cast<const uint16_t*>(x);
   a.topk_idx = idx;
@@ -805,11 +810,30 @@ static moe_status pool_dev_enqueue(const moe_layer_desc* d, const moe_layer_weig
     // the pool's policy kernel selects the token's experts itself (the top-K
     // kernel's code) and then acquires them
     const moe::DevRoute rt{at<float>(ws, L.logits), rp.n_part, rp.biased ? nullptr : w.router_bias, tw, gamma};
+    // GEMV family: the misses are copied by the gate/up kernel's first
+    // workgroups, the gate/up sections first (a missed row's products wait
+    // for its expert's), then the down sections, so the products overlap the
+    // copies and no separate copy launch is paid.  The grouped family (a
+    // forced path) copies with the copy kernel after the acquire.
+    const bool streamed = !use_grouped(d, 1);
+    moe::StreamCopy sc = moe::devpool_stream_copy(pool, l);
+    {
+      const int I = d->inter, G = d->group_size, bits = wbits(d);
+      sc.first.off[0] = 0;
+      sc.first.len[0] = moe::blob_d_q(H, I, bits);
+      sc.first.off[1] = moe::blob_gu_s(H, I, bits);
+      sc.first.len[1] = moe::blob_d_s(H, I, G, bits) - moe::blob_gu_s(H, I, bits);
+      sc.second.off[0] = moe::blob_d_q(H, I, bits);
+      sc.second.len[0] = moe::blob_gu_s(H, I, bits) - moe::blob_d_q(H, I, bits);
+      sc.second.off[1] = moe::blob_d_s(H, I, G, bits);
+      sc.second.len[1] = pc.blob_bytes - moe::blob_d_s(H, I, G, bits);
+    }
     hipError_t e = moe::devpool_enqueue_acquire(pool, l, idx, K, l == L_ - 1,
-                                                trace ? trace + static_cast<size_t>(l) * K * 3 : nullptr, s, &rt);
+                                                trace ? trace + static_cast<size_t>(l) * K * 3 : nullptr, s, &rt,
+                                                !streamed);
     if (e != hipSuccess) return hip_fail(e, "pool acquire launch");
     if ((st = do_ffn(d, &w, xl, 1, idx, tw, gamma, nullptr, fold ? nullptr : r, fold ? nullptr : xn, ws, L, s,
-                     l == 0, -1, nullptr, fold)))
+                     l == 0, -1, nullptr, fold, streamed ? &sc : nullptr)))
       return st;
   }
   if (fold) {

@@ -75,7 +75,13 @@ constexpr int kGemvGateUpWaves = 8;
 // router's logit slices (KJ logits per lane, the top-K kernel's code) and
 // passes its rank's expert through LDS; the other rows skip it.  The weight
 // loads then follow as usual.
-template <int ACT, int BITS, int KJ>
+//
+// STREAMED (a streamed decode through the GPU-resident slot pool): a 1-D
+// grid whose first kStreamCopyWgs workgroups copy the layer's missed blobs
+// from host memory (stream_copy), followed by the (j, p, z) workgroups in
+// the order above.  A row whose expert is being copied waits for its gate/up
+// sections before its first weight load; resident rows do not wait.
+template <int ACT, int BITS, int KJ, bool STREAMED = false>
 __global__ __launch_bounds__(64 * kGemvGateUpWaves) void k_gateup_gemv(FfnArgs a) {
   constexpr int NW = kGemvGateUpWaves;
   constexpr int NQ = BITS / 4;   // 16-byte loads per lane and chunk
@@ -86,10 +92,33 @@ __global__ __launch_bounds__(64 * kGemvGateUpWaves) void k_gateup_gemv(FfnArgs a
   __shared__ float red[NW][2][16];
   const uint8_t* blob;
   int t, inter;
-  const int j = blockIdx.x;
-  const int p = blockIdx.y, z = blockIdx.z;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rows = a.T * a.K + (a.Is > 0 ? a.T : 0);
+  // a streamed FFN runs a 1-D grid: the copy workgroups, then (j, p, z)
+  constexpr bool streamed = STREAMED;
+  static_assert(!STREAMED || KJ == 0, "a streamed FFN has its selection before gate/up");
+  if (streamed && static_cast<int>(blockIdx.x) < kStreamCopyWgs) {
+    stream_copy<64 * NW>(a.stream, blockIdx.x);
+    return;
+  }
+  int j = blockIdx.x, p = blockIdx.y, z = blockIdx.z;
+  if constexpr (streamed) {
+    const int lin = static_cast<int>(blockIdx.x) - kStreamCopyWgs;
+    const int np = (a.hstride + 15) / 16;
+    j = lin % rows;
+    p = (lin / rows) % np;
+    z = lin / (rows * np);
+  }
+  // a streamed row's copy entry (-1: resident, nothing to wait for), loaded
+  // first as a vector load (a scalar one would be waited for before the
+  // expert lookup), so that its latency overlaps the lookup's
+  int ent_v = -1;
+  if (streamed && j < a.T * a.K) {
+    int jv = j;
+    asm volatile("" : "+v"(jv));
+    ent_v = a.stream.entry_of[jv];
+  }
   if (a.status_reset && j == 0 && p == 0 && z == 0 && threadIdx.x == 0) *a.status = 0u;
   if constexpr (KJ > 0) {
     __shared__ int32_t ssel[kMaxTopK];
@@ -117,7 +146,6 @@ __global__ __launch_bounds__(64 * kGemvGateUpWaves) void k_gateup_gemv(FfnArgs a
     row_source(a, j, blob, t, inter);
   }
   if (p * 16 >= inter) return;
-  const int rows = gridDim.x;
   float* part = a.h + ((static_cast<size_t>(z) * rows + j) * a.hstride + 16 * p) * 2;
   if (blob == nullptr) {
     if (threadIdx.x < 32) part[threadIdx.x] = 0.0f;
@@ -131,6 +159,9 @@ __global__ __launch_bounds__(64 * kGemvGateUpWaves) void k_gateup_gemv(FfnArgs a
   const uint8_t* ssec = blob + blob_gu_s(H, inter, BITS);
   uint4 q[kGemvBatch][NQ];
   uint2 sv[kGemvBatch][2];
+  // a streamed row whose expert is being copied waits for its gate/up sections
+  const int ent = __builtin_amdgcn_readfirstlane(ent_v);
+  if (ent >= 0 && !stream_wait(a.stream, ent) && threadIdx.x == 0) atomicOr(a.status, kStatusStreamWait);
   // chunk of the wave's i-th step: z + S (wave + NW i)
   auto chunk = [&](int i) { return z + kGemvSplit * (wave + NW * i); };
   auto issue = [&](int i0) {
@@ -583,14 +614,28 @@ __global__ __launch_bounds__(256) void k_epilogue(const float* __restrict__ y, f
 
 hipError_t launch_gateup_gemv(int act, const FfnArgs& a, hipStream_t s) {
   const int rows = a.T * a.K + (a.Is > 0 ? a.T : 0);
-  dim3 grid(rows, (a.hstride + 15) / 16, kGemvSplit);
+  const int np = (a.hstride + 15) / 16;
+  const bool streamed = a.stream.first.list != nullptr;
+  if (streamed && (a.route_part != nullptr || a.stream.entry_of == nullptr || a.stream.ready == nullptr ||
+                   a.stream.first.len[0] + a.stream.first.len[1] == 0))
+    return hipErrorInvalidValue;
+  const dim3 grid = streamed ? dim3(kStreamCopyWgs + rows * np * kGemvSplit) : dim3(rows, np, kGemvSplit);
   const dim3 block(64 * kGemvGateUpWaves);
   int kj = 0;   // logits per lane of the fused top-K (0: not fused)
   if (a.route_part != nullptr) {
     if (a.E > 512) return hipErrorInvalidValue;
     kj = a.E <= 64 ? 1 : a.E <= 128 ? 2 : a.E <= 256 ? 4 : 8;
   }
-#define GATEUP_LAUNCH(ACT_, BITS_, KJ_) hipLaunchKernelGGL((k_gateup_gemv<ACT_, BITS_, KJ_>), grid, block, 0, s, a)
+#define GATEUP_LAUNCH(ACT_, BITS_, KJ_)                                                               \
+  do {                                                                                                \
+    if constexpr (KJ_ == 0) {                                                                         \
+      if (streamed) {                                                                                 \
+        hipLaunchKernelGGL((k_gateup_gemv<ACT_, BITS_, 0, true>), grid, block, 0, s, a);              \
+        break;                                                                                        \
+      }                                                                                               \
+    }                                                                                                 \
+    hipLaunchKernelGGL((k_gateup_gemv<ACT_, BITS_, KJ_>), grid, block, 0, s, a);                      \
+  } while (0)
 #define GATEUP_KJ(ACT_, BITS_)               \
   do {                                       \
     switch (kj) {                            \

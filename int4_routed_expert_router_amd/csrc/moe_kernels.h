@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "blob_copy.h"
+
 namespace moe {
 
 constexpr int kMaxH = 8192;        // hidden size limit (router keeps a row in registers)
@@ -50,8 +52,12 @@ struct FfnArgs {
   // SwiGLU output does not fit its fp16 matrix-core operand
   uint32_t* status;
   int status_reset;
+  // GEMV gate/up of a streamed FFN (the slot pool's misses copied by the
+  // kernel's first workgroups; stream.first.list == nullptr: none)
+  StreamCopy stream;
 };
 constexpr uint32_t kStatusF16Range = 1u;
+constexpr uint32_t kStatusStreamWait = 2u;   // a streamed gate/up row gave up waiting for its copy
 
 // Units of the grouped family, written by the bucketing kernel.  A unit is up
 // to 16 rows of one expert: the shared expert's units come first (rows
