@@ -100,8 +100,12 @@ struct StreamCopy {
   BlobCopy first;            // list == nullptr: no streamed copy
   BlobCopy second;           // same list, source and destination; other ranges
   const int32_t* entry_of;   // [T*K]: list entry of routed row j, -1: resident (no wait)
-  uint32_t* ready;           // [cap]: 16-byte words of each entry's first ranges copied (zero at launch)
+  uint32_t* ready;           // entry i's counter at ready[i * kReadyStride]: 16-byte words of its first
+                             // ranges copied (zero at launch)
 };
+// each counter on a 256-byte line of its own: polls of one line serialise
+// (and load the memory channel that holds it)
+constexpr int kReadyStride = 64;
 // the copy workgroups come first in the grid, so in-order dispatch puts them
 // on the chip before any workgroup that waits for them
 constexpr int kStreamCopyWgs = 64;
@@ -121,7 +125,8 @@ __device__ __forceinline__ void stream_copy(const StreamCopy& c, int wg) {
     for (uint64_t i = k0 / per; i <= (k1 - 1) / per; ++i) {
       const uint64_t lo = k0 > per * i ? k0 : per * i;
       const uint64_t hi = k1 < per * (i + 1) ? k1 : per * (i + 1);
-      __hip_atomic_fetch_add(c.ready + i, static_cast<uint32_t>(hi - lo), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(c.ready + i * kReadyStride, static_cast<uint32_t>(hi - lo), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   blob_copy_part<NT>(c.second, wg, kStreamCopyWgs, k0, k1);
@@ -134,9 +139,10 @@ __device__ __forceinline__ bool stream_wait(const StreamCopy& c, int ent) {
   if (threadIdx.x == 0) {
     const uint32_t target = static_cast<uint32_t>((c.first.len[0] + c.first.len[1]) / 16);
     int it = 0;
-    while (__hip_atomic_load(c.ready + ent, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target &&
+    while (__hip_atomic_load(c.ready + static_cast<size_t>(ent) * kReadyStride, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT) < target &&
            it < kStreamSpinLimit) {
-      __builtin_amdgcn_s_sleep(2);
+      __builtin_amdgcn_s_sleep(8);
       ++it;
     }
     ok = it < kStreamSpinLimit;

@@ -15,12 +15,12 @@ namespace moe {
 // expert its slot (-1: not resident), per layer and slot the resident expert
 // (-1: free), its count and last use, and the miss list of the last acquire
 // ([0] = n, then n experts, from [1 + 64] their slots, from [1 + 128] each
-// request's list entry (-1: a hit), from [1 + 192] the copy counters of a
-// streamed FFN, cleared by the acquire).
+// request's list entry (-1: a hit)), and the copy counters of a streamed FFN
+// (one per list entry, kReadyStride words apart, cleared by the acquire).
 struct DevPoolGeom {
   int L, E, S, P;
   uint64_t stride;
-  size_t o_epoch, o_slot_of, o_expert_in, o_count, o_last_use, o_miss, bytes;
+  size_t o_epoch, o_slot_of, o_expert_in, o_count, o_last_use, o_miss, o_ready, bytes;
 };
 DevPoolGeom devpool_geom(int L, int E, int S, int P, uint64_t stride);
 

@@ -43,8 +43,10 @@ __global__ void k_devpool_reset(uint8_t* st, DevPoolGeom g) {
     reinterpret_cast<uint32_t*>(st + g.o_count)[i] = 0;
     reinterpret_cast<uint64_t*>(st + g.o_last_use)[i] = 0;
   }
-  for (size_t i = tid; i < 1 + 4 * kMissCap; i += nth)
+  for (size_t i = tid; i < 1 + 3 * kMissCap; i += nth)
     reinterpret_cast<int32_t*>(st + g.o_miss)[i] = (i >= 1 + 2 * kMissCap && i < 1 + 3 * kMissCap) ? -1 : 0;
+  for (size_t i = tid; i < static_cast<size_t>(kMissCap) * moe::kReadyStride; i += nth)
+    reinterpret_cast<uint32_t*>(st + g.o_ready)[i] = 0u;
 }
 
 // One acquire of `layer` for the K experts at idx (device), at the pool's
@@ -75,13 +77,13 @@ __global__ __launch_bounds__(64) void k_devpool_acquire(uint8_t* st, DevPoolGeom
   uint64_t* lu_g = reinterpret_cast<uint64_t*>(st + g.o_last_use) + static_cast<size_t>(layer) * S;
   int32_t* miss = reinterpret_cast<int32_t*>(st + g.o_miss);
   int32_t* entry_of = miss + 1 + 2 * kMissCap;
-  uint32_t* ready = reinterpret_cast<uint32_t*>(miss + 1 + 3 * kMissCap);
+  uint32_t* ready = reinterpret_cast<uint32_t*>(st + g.o_ready);
   uint64_t* epoch = reinterpret_cast<uint64_t*>(st + g.o_epoch) + layer;
   // an empty miss list until this acquire has placed its misses (so an
   // error return copies nothing), no request waiting, no copy counted
   if (lane == 0) miss[0] = 0;
   entry_of[lane] = -1;
-  ready[lane] = 0u;
+  ready[lane * moe::kReadyStride] = 0u;
   // this layer's slots in registers, and the step and aging epoch: loaded
   // first, they do not depend on the request
   const uint64_t step = h[0];
@@ -285,7 +287,8 @@ DevPoolGeom devpool_geom(int L, int E, int S, int P, uint64_t stride) {
   g.o_expert_in = o; o += al(static_cast<size_t>(L) * S * 4);
   g.o_count = o; o += al(static_cast<size_t>(L) * S * 4);
   g.o_last_use = o; o += al(static_cast<size_t>(L) * S * 8);
-  g.o_miss = o; o += al((1 + 4 * kMissCap) * 4);
+  g.o_miss = o; o += al((1 + 3 * kMissCap) * 4);
+  g.o_ready = o; o += al(static_cast<size_t>(kMissCap) * moe::kReadyStride * 4);
   g.bytes = o;
   return g;
 }
@@ -325,7 +328,7 @@ StreamCopy devpool_stream_copy(const moe_devpool* p, int layer) {
   c.first = c.second = devpool_miss_copy(p, layer);
   int32_t* miss = reinterpret_cast<int32_t*>(p->state + p->g.o_miss);
   c.entry_of = miss + 1 + 2 * kMissCap;
-  c.ready = reinterpret_cast<uint32_t*>(miss + 1 + 3 * kMissCap);
+  c.ready = reinterpret_cast<uint32_t*>(p->state + p->g.o_ready);
   return c;
 }
 
