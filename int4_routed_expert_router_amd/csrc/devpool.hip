@@ -170,7 +170,7 @@ __global__ __launch_bounds__(64) void k_devpool_acquire(uint8_t* st, DevPoolGeom
 #pragma unroll
     for (int j = 0; j < SPL; ++j)
       if (ein[j] == -1) free_s = min(free_s, static_cast<uint32_t>(lane + 64 * j));
-    free_s = moe::wave_min_u32(free_s);
+    free_s = moe::wave_min_u32_s(free_s);
     int s = static_cast<int>(free_s), victim = -1;
     if (free_s == 0xFFFFFFFFu) {
       // the unpinned resident expert with the smallest (count, last_use, id)
@@ -178,24 +178,24 @@ __global__ __launch_bounds__(64) void k_devpool_acquire(uint8_t* st, DevPoolGeom
 #pragma unroll
       for (int j = 0; j < SPL; ++j)
         if (ein[j] >= 0 && !pin[j]) mc = min(mc, cnt[j]);
-      mc = moe::wave_min_u32(mc);
+      mc = moe::wave_min_u32_s(mc);
       uint32_t mh = 0xFFFFFFFFu;
 #pragma unroll
       for (int j = 0; j < SPL; ++j)
         if (ein[j] >= 0 && !pin[j] && cnt[j] == mc) mh = min(mh, static_cast<uint32_t>(lu[j] >> 32));
-      mh = moe::wave_min_u32(mh);
+      mh = moe::wave_min_u32_s(mh);
       uint32_t ml = 0xFFFFFFFFu;
 #pragma unroll
       for (int j = 0; j < SPL; ++j)
         if (ein[j] >= 0 && !pin[j] && cnt[j] == mc && static_cast<uint32_t>(lu[j] >> 32) == mh)
           ml = min(ml, static_cast<uint32_t>(lu[j]));
-      ml = moe::wave_min_u32(ml);
+      ml = moe::wave_min_u32_s(ml);
       uint32_t me = 0xFFFFFFFFu;
       const uint64_t mlu = (static_cast<uint64_t>(mh) << 32) | ml;
 #pragma unroll
       for (int j = 0; j < SPL; ++j)
         if (ein[j] >= 0 && !pin[j] && cnt[j] == mc && lu[j] == mlu) me = min(me, static_cast<uint32_t>(ein[j]));
-      me = moe::wave_min_u32(me);   // K <= S, so an unpinned resident expert exists
+      me = moe::wave_min_u32_s(me);   // K <= S, so an unpinned resident expert exists
       if (me == 0xFFFFFFFFu) {       // cannot happen: the launcher checks K <= S
         if (lane == 0) h[4] = 2;
         return;
@@ -205,7 +205,7 @@ __global__ __launch_bounds__(64) void k_devpool_acquire(uint8_t* st, DevPoolGeom
 #pragma unroll
       for (int j = 0; j < SPL; ++j)
         if (ein[j] == victim) vs = static_cast<uint32_t>(lane + 64 * j);
-      s = static_cast<int>(moe::wave_min_u32(vs));
+      s = static_cast<int>(moe::wave_min_u32_s(vs));
       if (lane == 0) slot_of[victim] = -1;
       ++n_evict;
     }

@@ -80,6 +80,36 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
   return wave_allreduce_u32(v, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
 }
 
+// Wave reduction into a scalar (uniform) result: DPP within rows of 16, then
+// the row broadcasts (lane 15 of each row into the next row, lane 31 into
+// rows 2 and 3), after which lane 63 holds the reduction of all 64 lanes.
+// Disabled rows keep their value (old = the operand).  Six DPP steps and a
+// lane read, against eight steps for the all-lane form; for max and min the
+// result does not depend on the order.
+// (the moved value of a disabled row is the operation's identity, so the
+// move folds into the operation as one DPP instruction)
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ uint32_t dpp_upd_u32(uint32_t v, uint32_t identity) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(static_cast<int>(identity), static_cast<int>(v), kCtrl, kRowMask, 0xF, false));
+}
+template <class Op>
+__device__ __forceinline__ uint32_t wave_reduce_scalar_u32(uint32_t v, Op op, uint32_t id) {
+  v = op(v, dpp_upd_u32<0xB1, 0xF>(v, id));    // quad_perm [1,0,3,2]
+  v = op(v, dpp_upd_u32<0x4E, 0xF>(v, id));    // quad_perm [2,3,0,1]
+  v = op(v, dpp_upd_u32<0x141, 0xF>(v, id));   // row_half_mirror
+  v = op(v, dpp_upd_u32<0x140, 0xF>(v, id));   // row_mirror
+  v = op(v, dpp_upd_u32<0x142, 0xA>(v, id));   // row_bcast:15 into rows 1 and 3
+  v = op(v, dpp_upd_u32<0x143, 0xC>(v, id));   // row_bcast:31 into rows 2 and 3
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
+}
+__device__ __forceinline__ uint32_t wave_max_u32_s(uint32_t v) {
+  return wave_reduce_scalar_u32(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; }, 0u);
+}
+__device__ __forceinline__ uint32_t wave_min_u32_s(uint32_t v) {
+  return wave_reduce_scalar_u32(v, [](uint32_t a, uint32_t b) { return a < b ? a : b; }, 0xFFFFFFFFu);
+}
+
 // ---- int4 nibble words -------------------------------------------------------
 // A 32-bit word holds 8 values; value j sits in nibble (j>>1) + 4*(j&1).
 //

@@ -144,7 +144,7 @@ __device__ __forceinline__ void topk_finish(TopkIn<kJ>& in, const float (&bj)[kJ
   int my_i = 0;
   for (int k = 0; k < K; ++k) {
     // K <= E, so some lane still holds an entry and m > 0
-    const uint32_t m = wave_max_u32(hi[0]);
+    const uint32_t m = wave_max_u32_s(hi[0]);
     const unsigned long long cand = __ballot(hi[0] == m);
     const uint32_t head_lo = lo_packed & 0xFu;
     int wl;
@@ -152,7 +152,7 @@ __device__ __forceinline__ void topk_finish(TopkIn<kJ>& in, const float (&bj)[kJ
       wl = __ffsll(cand) - 1;
     } else {
       const uint32_t idx = (hi[0] == m) ? (kJ - 1 - head_lo) * 64u + static_cast<uint32_t>(lane) : 0xFFFFFFFFu;
-      wl = __builtin_amdgcn_readfirstlane(static_cast<int>(wave_min_u32(idx) & 63u));
+      wl = static_cast<int>(wave_min_u32_s(idx) & 63u);
     }
     const int e = (kJ - 1 - __builtin_amdgcn_readlane(static_cast<int>(head_lo), wl)) * 64 + wl;
     if (k == 0) key0 = m;
