@@ -1,9 +1,11 @@
 """GPU-resident slot pool: the policy kernel's trace equals the pool simulator's
 (own Python code) request by request, the streamed decode (no host round
-trip per layer) equals the resident stack bit for bit, and the captured
-token graph replays token after token with the step advancing on the device.
-The pages' placement check: an expert answers identically from cache or
-disk (Show HN page, validation paragraph)."""
+trip per layer; on the GEMV family the gate/up kernel copies the misses
+beside its products, a missed expert's rows waiting for its sections)
+equals the resident stack bit for bit with no wait given up, and the
+captured token graph replays token after token with the step advancing on
+the device.  The pages' placement check: an expert answers identically from
+cache or disk (Show HN page, validation paragraph)."""
 import dataclasses
 
 import numpy as np
@@ -20,7 +22,7 @@ POOLED4 = dataclasses.replace(synth.TINY, name="pooled4", n_experts=16, top_k=3,
 
 
 class DevPoolRig:
-    def __init__(self, wl, slots, period):
+    def __init__(self, wl, slots, period, path=0):
         import torch
         from int4_routed_expert_router_amd import api
         self.wl = wl
@@ -32,7 +34,7 @@ class DevPoolRig:
         for l in range(L):
             self.host[l * E * self.stride:(l + 1) * E * self.stride].copy_(self.dls[l].experts.cpu())
         self.slots, self.period = slots, period
-        self.desc = desc_for(wl, path=0)
+        self.desc = desc_for(wl, path=path)
         self.layers = [dl.api_layer() for dl in self.dls]
 
     def pool(self):
@@ -66,12 +68,17 @@ def check_trace(sim, step, sel, trace):
         assert got == want, f"step {step} layer {l}: device pool {got} != simulator {want}"
 
 
-@pytest.mark.parametrize("slots,period", [(5, 4), (3, 0), (16, 2)])
-def test_device_pool_trace_and_placement(slots, period):
+@pytest.mark.parametrize("slots,period,path", [(5, 4, 0), (3, 0, 0), (16, 2, 0), (5, 4, 2)],
+                         ids=["5_slots", "3_slots_no_aging", "all_resident", "5_slots_grouped_copy_kernel"])
+def test_device_pool_trace_and_placement(slots, period, path):
+    """path 0: the GEMV family, misses copied inside the gate/up kernel; path
+    2 (the grouped family forced): misses copied by the copy kernel after the
+    acquire."""
     import torch
     from int4_routed_expert_router_amd import api
+    from int4_routed_expert_router_amd._lib import MOE_FLAG_STREAM_WAIT
     wl = POOLED4
-    rig = DevPoolRig(wl, slots, period)
+    rig = DevPoolRig(wl, slots, period, path)
     pool = rig.pool()
     sim = PoolSim(wl.layers, wl.n_experts, slots, period, blob_bytes=rig.blob)
     L, K, H = wl.layers, wl.top_k, wl.hidden
@@ -84,6 +91,7 @@ def test_device_pool_trace_and_placement(slots, period):
         r = (x0.view(torch.float16).float() if wl.act_dtype == "f16" else x0.view(torch.bfloat16).float()).reshape(-1)
         api.pool_decode_step_dev(rig.desc, rig.layers, pool, x0, r, x_buf, ws, trace=trace)
         torch.cuda.synchronize()
+        assert api.workspace_status(rig.desc, 1, ws) & MOE_FLAG_STREAM_WAIT == 0, f"step {step}: a wait gave up"
         r_ref, x_ref, sel = rig.resident(x0)
         assert np.array_equal(r.cpu().numpy(), r_ref), f"step {step}: residual differs from the resident stack"
         assert np.array_equal(x_buf[(L - 1) % 2].cpu().numpy(), x_ref), f"step {step}: next input differs"
@@ -179,6 +187,7 @@ def test_device_pool_at_the_80b_shape():
     simulator's, with misses and evictions."""
     import torch
     from int4_routed_expert_router_amd import api
+    from int4_routed_expert_router_amd._lib import MOE_FLAG_STREAM_WAIT
     wl = dataclasses.replace(synth.POOL80, layers=3)
     rig = DevPoolRig(wl, wl.slots_per_layer, 8)
     pool = rig.pool()
@@ -192,6 +201,7 @@ def test_device_pool_at_the_80b_shape():
         r = x0.view(torch.bfloat16).float().reshape(-1)
         api.pool_decode_step_dev(rig.desc, rig.layers, pool, x0, r, x_buf, ws, trace=trace)
         torch.cuda.synchronize()
+        assert api.workspace_status(rig.desc, 1, ws) & MOE_FLAG_STREAM_WAIT == 0, f"step {step}: a wait gave up"
         r_ref, x_ref, sel = rig.resident(x0)
         assert np.array_equal(r.cpu().numpy(), r_ref), f"step {step}: residual differs"
         check_trace(sim, step, sel, trace.cpu().numpy())
@@ -207,7 +217,18 @@ def test_device_pool_rejects_bad_ids_without_changes():
     from int4_routed_expert_router_amd import api
     wl = POOLED4
     rig = DevPoolRig(wl, 5, 4)
-    pool = rig.pool()
+    slab = torch.zeros(wl.layers * 5 * rig.stride, dtype=torch.uint8, device="cuda")
+    offsets = torch.zeros(wl.layers * wl.n_experts, dtype=torch.int64, device="cuda")
+    pool = api.DevPool(wl.layers, wl.n_experts, 5, 4, rig.stride, rig.blob, rig.host, slab, offsets)
+    # a good acquire on layer 0 leaves a miss list; a rejected one on layer 1
+    # must copy nothing (its copy kernel sees an empty list, not layer 0's)
+    pool.acquire(0, torch.tensor([3, 4, 2], dtype=torch.int32, device="cuda"))
+    pool.acquire(1, torch.tensor([5, 5, 6], dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert pool.stats()["error"] == 1
+    assert int(slab[5 * rig.stride:10 * rig.stride].count_nonzero()) == 0, "a rejected acquire copied blobs"
+    assert int(slab[:5 * rig.stride].count_nonzero()) > 0
+    pool.reset()
     pool.acquire(0, torch.tensor([1, 1, 2], dtype=torch.int32, device="cuda"))   # repeated id
     st = pool.stats()
     assert st["error"] == 1 and st["hits"] == 0 and st["misses"] == 0
