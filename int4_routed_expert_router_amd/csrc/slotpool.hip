@@ -50,14 +50,20 @@ __global__ __launch_bounds__(256) void k_copy_blobs(const uint8_t* __restrict__ 
   const uint64_t per = (n16 + kCopySlices - 1) / kCopySlices;
   const uint64_t k0 = blockIdx.x * per;
   const uint64_t k1 = k0 + per < n16 ? k0 + per : n16;
+  // kCopyDepth = 4 reads in flight, in named registers (an array here is
+  // placed in LDS by the compiler)
+  static_assert(kCopyDepth == 4, "four named registers");
   for (uint64_t k = k0 + threadIdx.x; k < k1; k += kCopyDepth * 256) {
-    uint4 v[kCopyDepth];
-#pragma unroll
-    for (int d = 0; d < kCopyDepth; ++d)
-      if (k + d * 256 < k1) v[d] = src[k + d * 256];
-#pragma unroll
-    for (int d = 0; d < kCopyDepth; ++d)
-      if (k + d * 256 < k1) dst[k + d * 256] = v[d];
+    const bool m0 = k < k1, m1 = k + 256 < k1, m2 = k + 512 < k1, m3 = k + 768 < k1;
+    uint4 v0, v1, v2, v3;
+    if (m0) v0 = src[k];
+    if (m1) v1 = src[k + 256];
+    if (m2) v2 = src[k + 512];
+    if (m3) v3 = src[k + 768];
+    if (m0) dst[k] = v0;
+    if (m1) dst[k + 256] = v1;
+    if (m2) dst[k + 512] = v2;
+    if (m3) dst[k + 768] = v3;
   }
   // a tail of fewer than 16 bytes, by one thread
   if (blockIdx.x == 0 && threadIdx.x == 0)
