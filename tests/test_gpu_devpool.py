@@ -29,7 +29,7 @@ class DevPoolRig:
         L, E, H = wl.layers, wl.n_experts, wl.hidden
         self.dls = [DeviceLayer(wl, l, use_gpu_fill=wl.hidden > 256) for l in range(L)]
         self.stride = self.dls[0].stride
-        self.blob = api.blob_bytes(H, wl.inter, wl.group)
+        self.blob = api.blob_bytes(H, wl.inter, wl.group, wl.bits)
         self.host = torch.empty(L * E * self.stride, dtype=torch.uint8, pin_memory=True)
         for l in range(L):
             self.host[l * E * self.stride:(l + 1) * E * self.stride].copy_(self.dls[l].experts.cpu())
@@ -68,16 +68,20 @@ def check_trace(sim, step, sel, trace):
         assert got == want, f"step {step} layer {l}: device pool {got} != simulator {want}"
 
 
-@pytest.mark.parametrize("slots,period,path", [(5, 4, 0), (3, 0, 0), (16, 2, 0), (5, 4, 2)],
-                         ids=["5_slots", "3_slots_no_aging", "all_resident", "5_slots_grouped_copy_kernel"])
-def test_device_pool_trace_and_placement(slots, period, path):
-    """path 0: the GEMV family, misses copied inside the gate/up kernel; path
-    2 (the grouped family forced): misses copied by the copy kernel after the
+@pytest.mark.parametrize("slots,period,path,bits", [(5, 4, 0, 4), (3, 0, 0, 4), (16, 2, 0, 4), (5, 4, 2, 4),
+                                                     (5, 4, 0, 8)],
+                         ids=["5_slots", "3_slots_no_aging", "all_resident", "5_slots_grouped_copy_kernel",
+                              "5_slots_int8"])
+def test_device_pool_trace_and_placement(slots, period, path, bits):
+    """path 0: the GEMV family, misses copied inside the gate/up kernel (its
+    gate/up and down byte ranges of the blob, int4 or int8); path 2 (the
+    grouped family forced): misses copied by the copy kernel after the
     acquire."""
     import torch
     from int4_routed_expert_router_amd import api
     from int4_routed_expert_router_amd._lib import MOE_FLAG_STREAM_WAIT
-    wl = POOLED4
+    wl = POOLED4 if bits == 4 else dataclasses.replace(POOLED4, name="pooled4_int8", bits=8, scale_lo=1e-4,
+                                                       scale_hi=1e-3)
     rig = DevPoolRig(wl, slots, period, path)
     pool = rig.pool()
     sim = PoolSim(wl.layers, wl.n_experts, slots, period, blob_bytes=rig.blob)
