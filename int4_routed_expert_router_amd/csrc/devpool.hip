@@ -107,7 +107,7 @@ __global__ __launch_bounds__(64) void k_devpool_acquire(uint8_t* st, DevPoolGeom
     topk_issue(rt.part, rt.n_part, 1, E, 0, lane, in);
     float bj[KJ];
     load_bias(rt.bias, E, lane, bj);
-    topk_finish(in, bj, rt.bias != nullptr, rt.n_part, E, K, 0, lane, idx, rt.w, rt.gamma, nullptr, ssel);
+    topk_finish(in, bj, rt.bias != nullptr, rt.n_part, E, K, 0, lane, idx, rt.w, rt.gamma, nullptr, ssel, K);
     __syncthreads();
     e = lane < K ? ssel[lane] : -1;
   } else {

@@ -71,10 +71,11 @@ constexpr int kGemvGateUpWaves = 8;
 // int8 bytes multiply activations staged as fp32.
 //
 // KJ > 0 (batch-1 decode): top-K runs here instead of in its own kernel.
-// Wave 0 of a routed row's workgroup selects the token's K experts from the
-// router's logit slices (KJ logits per lane, the top-K kernel's code) and
-// passes its rank's expert through LDS; the other rows skip it.  The weight
-// loads then follow as usual.
+// Wave 0 of a routed row's workgroup selects from the router's logit slices
+// (KJ logits per lane, the top-K kernel's code) and passes its rank's expert
+// through LDS; the other rows skip it.  A workgroup of rank k runs only the
+// first k + 1 selection rounds, so the early ranks start their weight loads
+// while the later ranks still select.  The weight loads then follow as usual.
 //
 // STREAMED (a streamed decode through the GPU-resident slot pool): a 1-D
 // grid whose first kStreamCopyWgs workgroups copy the layer's missed blobs
@@ -131,9 +132,12 @@ __global__ __launch_bounds__(64 * kGemvGateUpWaves) void k_gateup_gemv(FfnArgs a
         topk_issue(a.route_part, a.route_nparts, a.T, a.E, t, lane, in);
         float bj[KJ];
         load_bias(a.route_bias, a.E, lane, bj);
-        const bool writer = p == 0 && z == 0 && k == 0;
+        // one workgroup per token (of the last rank: it runs every round
+        // anyway) writes the selection for the down and combine kernels; the
+        // others stop at their own rank
+        const bool writer = p == 0 && z == 0 && k == a.K - 1;
         topk_finish(in, bj, a.route_bias != nullptr, a.route_nparts, a.E, a.K, t, lane, writer ? a.sel_idx : nullptr,
-                    writer ? a.sel_w : nullptr, writer ? a.sel_gamma : nullptr, nullptr, ssel);
+                    writer ? a.sel_w : nullptr, writer ? a.sel_gamma : nullptr, nullptr, ssel, writer ? a.K : k + 1);
       }
       __syncthreads();
       const int e = ssel[k];

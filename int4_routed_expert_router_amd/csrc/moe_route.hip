@@ -228,7 +228,7 @@ __global__ __launch_bounds__(64) void k_topk(const float* __restrict__ part, int
   topk_issue(part, n_part, T, E, t, lane, in);
   float bj[kJ];
   load_bias(bias, E, lane, bj);
-  topk_finish(in, bj, bias != nullptr, n_part, E, K, t, lane, topk_idx, topk_w, gamma, logits, nullptr);
+  topk_finish(in, bj, bias != nullptr, n_part, E, K, t, lane, topk_idx, topk_w, gamma, logits, nullptr, K);
 }
 
 // Inclusive prefix sums of two values at once over a 1024-thread block.

@@ -54,11 +54,10 @@ __device__ __forceinline__ void shift_up(uint32_t (&a)[N], bool take, std::integ
 
 // Top-K of one token on one wave.  Lane l holds experts l, l+64, ... (kJ of
 // them).  Each lane first sorts its own entries by (logit desc, expert index
-// asc), as a 64-bit key (order_key(logit), kJ-1-j).  Then K rounds: the wave
-// maximum of the lanes' head keys picks the logit; among the lanes whose head
-// holds it (one, unless logits tie across lanes) the lowest expert index
-// wins, and the winning lane pops its head.  So ties resolve to the lower
-// expert index.  The shared-gate logit is column E of the slices.
+// asc), as a 64-bit key (order_key(logit), kJ-1-j).  Then K rounds, each of
+// which takes the largest remaining entry of the wave (ties to the lower
+// expert index) from the head of its lane's list.  The shared-gate logit is
+// column E of the slices.
 //
 // topk_issue issues every load of a token (all slices of the lane's kJ
 // logits and of the gate column; indices clamped to valid memory) without
@@ -82,15 +81,22 @@ __device__ __forceinline__ void topk_issue(const float* __restrict__ part, int n
   }
 }
 
-// z = slice 0 + slice 1 + ... (in order) + bias; selection; softmax weights
-// of the selected set; sigmoid gate.  Writes idx/w when topk_idx is non-null,
-// the token's K indices in rank order to sidx[0..K) when sidx is non-null,
-// gamma when non-null, logits when non-null.
+// A lane's entries after the sort, by (logit desc, expert index asc): the
+// keys, and the matching fields kJ-1-j packed 4 bits each (list positions
+// 0..7 in lo, 8..15 in lo_hi8), so that a pop is one shift; head is the
+// expert index of the lane's first entry.
 template <int kJ>
-__device__ __forceinline__ void topk_finish(TopkIn<kJ>& in, const float (&bj)[kJ], bool has_bias, int n_part, int E,
-                                            int K, int t, int lane, int32_t* __restrict__ topk_idx,
-                                            float* __restrict__ topk_w, float* __restrict__ gamma,
-                                            float* __restrict__ logits, int32_t* sidx) {
+struct TopkList {
+  uint32_t hi[kJ];
+  uint32_t lo, lo_hi8;
+  int head;
+};
+
+// z = slice 0 + slice 1 + ... (in order) + bias, written to logits when
+// non-null; returns the gate logit in zg and the lane's sorted list.
+template <int kJ>
+__device__ __forceinline__ TopkList<kJ> topk_sorted(TopkIn<kJ>& in, const float (&bj)[kJ], bool has_bias, int n_part,
+                                                    int E, int t, int lane, float* __restrict__ logits, float& zg) {
   // opaque to the optimiser, so no load is sunk into a branch
 #pragma unroll
   for (int p = 0; p < kRouterMaxParts; ++p) {
@@ -98,7 +104,7 @@ __device__ __forceinline__ void topk_finish(TopkIn<kJ>& in, const float (&bj)[kJ
     for (int j = 0; j < kJ; ++j) asm volatile("" : "+v"(in.raw[p][j]));
     asm volatile("" : "+v"(in.zg[p]));
   }
-  float zg = in.zg[0];
+  zg = in.zg[0];
 #pragma unroll
   for (int p = 1; p < kRouterMaxParts; ++p) {
     if (p < n_part) {   // uniform
@@ -118,6 +124,8 @@ __device__ __forceinline__ void topk_finish(TopkIn<kJ>& in, const float (&bj)[kJ
       if (lane + 64 * j < E) lo_out[lane + 64 * j] = in.raw[0][j];
     if (lane == 0) lo_out[E] = zg;
   }
+  // sorted as plain local arrays (a member array of the result, captured by
+  // the compare-and-swap, would be lowered to branches and moves)
   uint32_t hi[kJ], lo[kJ];
 #pragma unroll
   for (int j = 0; j < kJ; ++j) {
@@ -132,53 +140,78 @@ __device__ __forceinline__ void topk_finish(TopkIn<kJ>& in, const float (&bj)[kJ
     hi[b] = swap ? ha : hi[b];
     lo[b] = swap ? la : lo[b];
   });
-  // after the sort the lane's indices travel as one word of 4-bit fields
-  // (field i = kJ-1-j of list position i), so a pop is one shift
-  uint32_t lo_packed = 0;
+  TopkList<kJ> L;
 #pragma unroll
-  for (int i = 0; i < kJ && i < 8; ++i) lo_packed |= lo[i] << (4 * i);
-  uint32_t lo_hi8 = 0;   // positions 8..15 (kJ = 16 only)
+  for (int j = 0; j < kJ; ++j) L.hi[j] = hi[j];
+  L.lo = 0;
 #pragma unroll
-  for (int i = 8; i < kJ; ++i) lo_hi8 |= lo[i] << (4 * (i - 8));
+  for (int i = 0; i < kJ && i < 8; ++i) L.lo |= lo[i] << (4 * i);
+  L.lo_hi8 = 0;
+#pragma unroll
+  for (int i = 8; i < kJ; ++i) L.lo_hi8 |= lo[i] << (4 * (i - 8));
+  L.head = (kJ - 1 - static_cast<int>(L.lo & 0xFu)) * 64 + lane;
+  return L;
+}
+
+// One round: the wave maximum of the lanes' head keys picks the logit key m;
+// among the lanes whose head holds it (one, unless logits tie across lanes)
+// the lowest expert index wins, and the winning lane pops its head.  Returns
+// the winner's expert index (uniform).  Some lane must still hold an entry.
+template <int kJ>
+__device__ __forceinline__ int topk_round(TopkList<kJ>& L, int lane, uint32_t& m) {
+  m = wave_max_u32_s(L.hi[0]);
+  const unsigned long long cand = __ballot(L.hi[0] == m);
+  int wl = __ffsll(cand) - 1;
+  if (__builtin_expect(__popcll(cand) != 1, 0)) {
+    const uint32_t idx = (L.hi[0] == m) ? static_cast<uint32_t>(L.head) : 0xFFFFFFFFu;
+    wl = static_cast<int>(wave_min_u32_s(idx) & 63u);
+  }
+  const int e = __builtin_amdgcn_readlane(L.head, wl);
+  // the winning lane drops its head: its list moves up one position
+  const bool pop = lane == wl;
+  shift_up(L.hi, pop, std::make_integer_sequence<int, kJ - 1>{});
+  L.hi[kJ - 1] = pop ? 0u : L.hi[kJ - 1];
+  if constexpr (kJ > 8) {
+    L.lo = pop ? (L.lo >> 4) | (L.lo_hi8 << 28) : L.lo;
+    L.lo_hi8 = pop ? L.lo_hi8 >> 4 : L.lo_hi8;
+  } else {
+    L.lo = pop ? L.lo >> 4 : L.lo;
+  }
+  L.head = (kJ - 1 - static_cast<int>(L.lo & 0xFu)) * 64 + lane;
+  return e;
+}
+
+// The selection: K rounds (K <= E), softmax weights of the selected set,
+// sigmoid gate.  Writes idx/w when topk_idx is non-null, the token's K
+// indices in rank order to sidx[0..K) when sidx is non-null, gamma when
+// non-null, logits when non-null.  With rounds < K (uniform) only the first
+// `rounds` ranks are selected, into sidx[0..rounds) (the same experts those
+// ranks get from the whole selection), and nothing else is written.
+template <int kJ>
+__device__ __forceinline__ void topk_finish(TopkIn<kJ>& in, const float (&bj)[kJ], bool has_bias, int n_part, int E,
+                                            int K, int t, int lane, int32_t* __restrict__ topk_idx,
+                                            float* __restrict__ topk_w, float* __restrict__ gamma,
+                                            float* __restrict__ logits, int32_t* sidx, int rounds) {
+  float zg;
+  TopkList<kJ> L = topk_sorted(in, bj, has_bias, n_part, E, t, lane, logits, zg);
   uint32_t my_key = 0, key0 = 0;
   int my_i = 0;
-  for (int k = 0; k < K; ++k) {
-    // K <= E, so some lane still holds an entry and m > 0
-    const uint32_t m = wave_max_u32_s(hi[0]);
-    const unsigned long long cand = __ballot(hi[0] == m);
-    const uint32_t head_lo = lo_packed & 0xFu;
-    int wl;
-    if (__popcll(cand) == 1) {
-      wl = __ffsll(cand) - 1;
-    } else {
-      const uint32_t idx = (hi[0] == m) ? (kJ - 1 - head_lo) * 64u + static_cast<uint32_t>(lane) : 0xFFFFFFFFu;
-      wl = static_cast<int>(wave_min_u32_s(idx) & 63u);
-    }
-    const int e = (kJ - 1 - __builtin_amdgcn_readlane(static_cast<int>(head_lo), wl)) * 64 + wl;
+  for (int k = 0; k < rounds; ++k) {
+    uint32_t m;
+    const int e = topk_round(L, lane, m);
     if (k == 0) key0 = m;
     if (lane == k) {
       my_key = m;
       my_i = e;
     }
-    // the winning lane drops its head: its list moves up one position
-    const bool pop = lane == wl;
-    shift_up(hi, pop, std::make_integer_sequence<int, kJ - 1>{});
-    hi[kJ - 1] = pop ? 0u : hi[kJ - 1];
-    if constexpr (kJ > 8) {
-      lo_packed = pop ? (lo_packed >> 4) | (lo_hi8 << 28) : lo_packed;
-      lo_hi8 = pop ? lo_hi8 >> 4 : lo_hi8;
-    } else {
-      lo_packed = pop ? lo_packed >> 4 : lo_packed;
-    }
   }
+  if (sidx != nullptr && lane < rounds) sidx[lane] = my_i;
+  if (rounds < K) return;
   const float ex = (lane < K) ? expf(key_value(my_key) - key_value(key0)) : 0.0f;
   const float s = wave_sum(ex);
-  if (lane < K) {
-    if (topk_idx != nullptr) {
-      topk_idx[static_cast<size_t>(t) * K + lane] = my_i;
-      topk_w[static_cast<size_t>(t) * K + lane] = ex / s;
-    }
-    if (sidx != nullptr) sidx[lane] = my_i;
+  if (lane < K && topk_idx != nullptr) {
+    topk_idx[static_cast<size_t>(t) * K + lane] = my_i;
+    topk_w[static_cast<size_t>(t) * K + lane] = ex / s;
   }
   if (lane == 0 && gamma != nullptr) gamma[t] = 1.0f / (1.0f + expf(-zg));
 }

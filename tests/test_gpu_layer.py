@@ -215,22 +215,19 @@ def test_deterministic_repeat():
         assert np.array_equal(a["y"], b["y"])
 
 
-@pytest.mark.parametrize("wl,n_tokens", [(synth.TINY, 4), (RAGGED, 7), (synth.DEC80, 1), (synth.DEC80, 3)],
-                         ids=["tiny_E16", "ragged_E24", "dec80_T1", "dec80_T3"])
-def test_fused_topk_gemv_matches_separate_kernels(wl, n_tokens):
-    """On the GEMV family a layer call selects the experts inside the gate/up
-    kernel (no top-K launch); moe_route + moe_expert_ffn run the top-K
-    kernel.  Same code, same order: bit-identical selection, weights, gate
-    and output."""
+def fused_and_separate(wl, dl, x_bits):
+    """One layer call with the selection inside the gate/up kernel, then
+    moe_route + moe_expert_ffn (the top-K kernel); returns both results as
+    [y, idx, w, gamma] and the router logits of the separate call."""
     import torch
     from int4_routed_expert_router_amd import api
-    dl = DeviceLayer(wl, 2)
     desc = desc_for(wl, path=1)
-    x = torch.from_numpy(synth.tokens(wl, n_tokens=n_tokens).view(np.int16).copy()).cuda()
-    T, K, H = n_tokens, wl.top_k, wl.hidden
+    x = torch.from_numpy(x_bits.view(np.int16).copy()).cuda()
+    T, K, H = x_bits.shape[0], wl.top_k, wl.hidden
     layer = dl.api_layer()
     ws = api.workspace(desc, T)
     outs = []
+    logits = torch.full((T, wl.n_experts + 1), float("nan"), dtype=torch.float32, device="cuda")
     for fused in (True, False):
         y = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
         idx = torch.full((T, K), -7, dtype=torch.int32, device="cuda")
@@ -239,10 +236,49 @@ def test_fused_topk_gemv_matches_separate_kernels(wl, n_tokens):
         if fused:
             api.layer_forward(desc, layer, x, y, idx, w, g, ws=ws)
         else:
-            api.route(desc, layer, x, idx, w, g, ws=ws)
+            api.route(desc, layer, x, idx, w, g, logits, ws=ws)
             api.expert_ffn(desc, layer, x, idx, w, g, y, ws=ws)
         torch.cuda.synchronize()
         outs.append([t.cpu().numpy() for t in (y, idx, w, g)])
+    return outs, logits.cpu().numpy()
+
+
+@pytest.mark.parametrize("wl,n_tokens", [(synth.TINY, 4), (RAGGED, 7), (synth.DEC80, 1), (synth.DEC80, 3)],
+                         ids=["tiny_E16", "ragged_E24", "dec80_T1", "dec80_T3"])
+def test_fused_topk_gemv_matches_separate_kernels(wl, n_tokens):
+    """On the GEMV family a layer call selects the experts inside the gate/up
+    kernel (no top-K launch); moe_route + moe_expert_ffn run the top-K
+    kernel.  Same code, same order: bit-identical selection, weights, gate
+    and output."""
+    dl = DeviceLayer(wl, 2)
+    outs, _ = fused_and_separate(wl, dl, synth.tokens(wl, n_tokens=n_tokens))
     for name, a, b in zip(("y", "idx", "w", "gamma"), outs[0], outs[1]):
         assert np.array_equal(a, b), f"{wl.name} T={n_tokens}: {name} differs between fused and separate top-K"
+    assert np.isfinite(outs[0][0]).all()
+
+
+def test_fused_topk_gemv_exact_ties_dec80():
+    """Nine experts with the same router row (no bias) tie for the top of the
+    token's selection, across lanes and within a lane's list of the wave
+    selection.  Inside the gate/up kernel a workgroup of rank k runs only the
+    first k + 1 selection rounds; every rank must still get the expert of the
+    whole selection (ties to the lower expert index), bit for bit as the
+    top-K kernel gives it."""
+    import torch
+    wl = dataclasses.replace(synth.DEC80, name="dec80_ties", zipf_s=0.0)
+    tied = [5, 6, 69, 70, 133, 197, 300, 301, 511]   # lanes 5, 6, 5, 6, 5, 5, 44, 45, 63 of the selecting wave
+    x_bits = synth.tokens(wl, 1)
+    xf = (x_bits.astype(np.uint32) << 16).view(np.float32)[0]
+    row = synth.f32_to_f16_bits(np.where(xf >= 0, 0.02, -0.02).astype(np.float32))
+    dl = DeviceLayer(wl, 0)
+    for e in tied:
+        dl.router_bits[e] = row
+    dl.router_w.copy_(torch.from_numpy(dl.router_bits.view(np.int16).copy()))
+    outs, z = fused_and_separate(wl, dl, x_bits)
+    for name, a, b in zip(("y", "idx", "w", "gamma"), outs[0], outs[1]):
+        assert np.array_equal(a, b), f"{name} differs between fused and separate top-K"
+    assert len(set(z[0, tied].tolist())) == 1 and z[0, tied[0]] > np.delete(z[0, :-1], tied).max()
+    idx = outs[0][1][0]
+    assert idx[:len(tied)].tolist() == tied
+    assert idx.tolist() == mo.topk_order(z[0, :-1].astype(np.float64), wl.top_k).tolist()
     assert np.isfinite(outs[0][0]).all()
