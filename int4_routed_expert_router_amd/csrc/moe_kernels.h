@@ -38,8 +38,9 @@ struct FfnArgs {
   int bits;                   // expert weight width, 4 or 8
   // GEMV family with top-K fused into gate/up (route_part != nullptr): every
   // routed row's workgroups select the token's experts from the router's
-  // logit slices themselves; one workgroup per token (rank 0, pair-tile 0,
-  // split 0) writes the selection to sel_idx (== topk_idx), sel_w, sel_gamma
+  // logit slices themselves; one workgroup per token (the last rank's,
+  // pair-tile 0, split 0) writes the selection to sel_idx (== topk_idx),
+  // sel_w, sel_gamma
   const float* route_part;    // [route_nparts][T][E+1]
   const float* route_bias;    // [E] or nullptr (also nullptr when the slices hold it)
   int route_nparts;
