@@ -257,16 +257,20 @@ def test_fused_topk_gemv_matches_separate_kernels(wl, n_tokens):
     assert np.isfinite(outs[0][0]).all()
 
 
-def test_fused_topk_gemv_exact_ties_dec80():
-    """Nine experts with the same router row (no bias) tie for the top of the
+@pytest.mark.parametrize("base,tied", [
+    (synth.DEC80, [5, 6, 69, 70, 133, 197, 300, 301, 511]),   # lanes 5, 6, 5, 6, 5, 5, 44, 45, 63
+    (synth.DEC35, [5, 6, 69, 70, 133, 197, 255]),             # lanes 5, 6, 5, 6, 5, 5, 63
+], ids=["dec80", "dec35"])
+def test_fused_topk_gemv_exact_ties(base, tied):
+    """Experts with the same router row (no bias) tie for the top of the
     token's selection, across lanes and within a lane's list of the wave
-    selection.  Inside the gate/up kernel a workgroup of rank k runs only the
-    first k + 1 selection rounds; every rank must still get the expert of the
-    whole selection (ties to the lower expert index), bit for bit as the
-    top-K kernel gives it."""
+    selection (expert e sits in lane e % 64).  Inside the gate/up kernel a
+    workgroup of rank k runs only the first k + 1 selection rounds; every
+    rank must still get the expert of the whole selection (ties to the lower
+    expert index), bit for bit as the top-K kernel gives it."""
     import torch
-    wl = dataclasses.replace(synth.DEC80, name="dec80_ties", zipf_s=0.0)
-    tied = [5, 6, 69, 70, 133, 197, 300, 301, 511]   # lanes 5, 6, 5, 6, 5, 5, 44, 45, 63 of the selecting wave
+    wl = dataclasses.replace(base, name=base.name + "_ties", zipf_s=0.0)
+    assert len(tied) < wl.top_k
     x_bits = synth.tokens(wl, 1)
     xf = (x_bits.astype(np.uint32) << 16).view(np.float32)[0]
     row = synth.f32_to_f16_bits(np.where(xf >= 0, 0.02, -0.02).astype(np.float32))
