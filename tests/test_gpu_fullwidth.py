@@ -112,11 +112,12 @@ def teacher_forced(st, got):
     return flagged
 
 
-@pytest.mark.parametrize("wl_name,n_tokens", [("bat80", 64), ("dec80", 1)])
+@pytest.mark.parametrize("wl_name,n_tokens", [("bat80", 64), ("dec80", 1), ("dec35", 1), ("dec80i8", 1)])
 def test_chained_stack_graph_replay_parity(wl_name, n_tokens):
-    """Three chained layers at the benchmark's shape (batched: grouped family
+    """Three chained layers at the benchmarks' shapes (batched: grouped family
     with the fused combine + epilogue at hidden 2048; batch 1: GEMV family
-    with top-K inside gate/up), replayed from one captured graph twice:
+    with top-K inside gate/up, at the 80B and 35B shapes and with int8
+    experts), replayed from one captured graph twice:
     every replay equals the eager run bit for bit, and each layer matches the
     oracle (teacher forced)."""
     wl = synth.WORKLOADS[wl_name]
