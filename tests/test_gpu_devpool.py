@@ -4,8 +4,9 @@ trip per layer; on the GEMV family the gate/up kernel copies the misses
 beside its products, a missed expert's rows waiting for its sections)
 equals the resident stack bit for bit with no wait given up, and the
 captured token graph replays token after token with the step advancing on
-the device.  The pages' placement check: an expert answers identically from
-cache or disk (Show HN page, validation paragraph)."""
+the device.  The pages' placement check: an expert gives the same result whether it
+was already resident or had to be loaded (Show HN page, validation
+paragraph)."""
 import dataclasses
 
 import numpy as np

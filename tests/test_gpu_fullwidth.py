@@ -6,9 +6,9 @@ without a shared expert and with down ranges over three units, and the fp16
 range status of the grouped family.
 
 The pages' validation paragraph (Show HN page) names the checks adapted
-here: incremental decoding against whole-sequence processing (batch
-invariance), and an expert answering identically from cache or disk
-(placement invariance of the pooled decode)."""
+here: decoding token by token agrees with running the batch at once (batch
+invariance), and an expert gives the same result wherever it was loaded
+from (placement invariance of the pooled decode)."""
 import dataclasses
 
 import numpy as np
