@@ -243,8 +243,13 @@ def fused_and_separate(wl, dl, x_bits):
     return outs, logits.cpu().numpy()
 
 
-@pytest.mark.parametrize("wl,n_tokens", [(synth.TINY, 4), (RAGGED, 7), (synth.DEC80, 1), (synth.DEC80, 3)],
-                         ids=["tiny_E16", "ragged_E24", "dec80_T1", "dec80_T3"])
+WIDE_K32 = dataclasses.replace(synth.DEC80, name="wide_k32", hidden=256, inter=128, shared_inter=128, top_k=32,
+                               weight_seed=14, token_seed=114)
+
+
+@pytest.mark.parametrize("wl,n_tokens", [(synth.TINY, 4), (RAGGED, 7), (synth.DEC80, 1), (synth.DEC80, 3),
+                                         (WIDE_K32, 1)],
+                         ids=["tiny_E16", "ragged_E24", "dec80_T1", "dec80_T3", "E512_K32_T1"])
 def test_fused_topk_gemv_matches_separate_kernels(wl, n_tokens):
     """On the GEMV family a layer call selects the experts inside the gate/up
     kernel (no top-K launch); moe_route + moe_expert_ffn run the top-K
